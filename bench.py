@@ -1,0 +1,252 @@
+"""Paged-attention decode benchmark on one MI355X.
+
+A step is one pass of the decode hot path over one batch: append each
+sequence's new token K/V into its tail block, then paged-attention decode
+(block-table resolve, K/V stream, scaled QK^T, online softmax, PV, split
+merge, output write) for one layer.  The batched paged-KV gather is timed
+separately and reported beside the step.
+
+    python bench.py [--workload llama8b_decode_bf16] [--steps K] [--warmup W]
+
+Prints one JSON line.  `value` is effective HBM GB/s of the step (algorithmic
+bytes / step time, inputs resident in HBM).  Inputs are rotated among
+replicas so that consecutive steps do not hit in the 256 MB Infinity Cache.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+WORKLOADS = {
+    "tiny_fp32_mha": 0,
+    "churned_pool_bf16_gqa7": 1,
+    "llama8b_decode_bf16": 2,
+    "long_context_bf16": 3,
+    "high_concurrency_bf16": 4,
+}
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic bytes of one decode: every cached K/V row once, q in, out
+    out, the used block-table entries and the context lengths."""
+    e = 4 if w.dtype == "f32" else 2
+    T = w.context_lens.astype(np.int64)
+    kv = int((2 * T * w.Hkv * w.D * e).sum())
+    qo = w.S * w.Hq * w.D * 2 * e
+    tables = 4 * int(((T + w.BS - 1) // w.BS).sum())
+    return kv + qo + tables + 4 * w.S
+
+
+def append_bytes(w) -> int:
+    e = 4 if w.dtype == "f32" else 2
+    return 2 * (2 * w.S * w.Hkv * w.D * e) + 4 * w.S + 4 * w.S
+
+
+def gather_bytes(w, max_len: int) -> int:
+    e = 4 if w.dtype == "f32" else 2
+    T = w.context_lens.astype(np.int64)
+    read = int((2 * T * w.Hkv * w.D * e).sum()) + 4 * int(((T + w.BS - 1) // w.BS).sum()) + 4 * w.S
+    write = 2 * w.S * max_len * w.Hkv * w.D * e + w.S * max_len
+    return read + write
+
+
+def cpu_baseline(w, budget_tokens: int):
+    """The oracle, as it stands, on a bounded sample of the same batch."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        blas_threads = 1
+    order = np.random.default_rng(7).permutation(w.S)
+    seqs, toks = [], 0
+    for b in order:
+        seqs.append(int(b))
+        toks += int(w.context_lens[b])
+        if toks >= budget_tokens:
+            break
+    t0 = time.perf_counter()
+    oracle.paged_attention_decode(w.pool, w.dtype, w.layer, w.block_tables, w.context_lens, w.q,
+                                  w.scale, seqs=seqs)
+    dt = time.perf_counter() - t0
+    e = 4 if w.dtype == "f32" else 2
+    sample_bytes = sum(2 * int(w.context_lens[b]) * w.Hkv * w.D * e for b in seqs) + \
+        len(seqs) * w.Hq * w.D * 2 * e
+    return {
+        "value": sample_bytes / dt / 1e9,
+        "unit": "GB/s",
+        "cores": int(blas_threads),
+        "kind": "oracle",
+        "sample": f"{len(seqs)} of {w.S} sequences ({toks} cached tokens), fp64 numpy, "
+                  f"{dt:.1f} s wall; tokens/s {len(seqs) / dt:.3g}",
+        "tokens_per_s": len(seqs) / dt,
+        "seconds": dt,
+    }
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama8b_decode_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=0, help="input replicas (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-gather", action="store_true")
+    ap.add_argument("--cpu-budget-tokens", type=int, default=0)
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py: this path runs on one GPU only; --gpus {args.gpus} is not supported",
+              file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr, flush=True)
+        return 2
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import paged_kv_cache_resolve_amd as pk
+    from workloads import make_workload
+
+    idx = WORKLOADS[args.workload]
+    w0 = make_workload(idx)
+    kvb = decode_bytes(w0)
+    reps = args.rotate or max(1, min(4, math.ceil(4 * MALL_BYTES / max(kvb, 1))))
+    ws = [w0] + [make_workload(idx, seed_offset=r) for r in range(1, reps)]
+    print(f"[bench] workload {args.workload}: S={w0.S} Hq={w0.Hq} Hkv={w0.Hkv} D={w0.D} "
+          f"BS={w0.BS} sum(T)={int(w0.context_lens.sum())} replicas={reps}", file=sys.stderr,
+          flush=True)
+
+    tdt = torch.float32 if w0.dtype == "f32" else torch.bfloat16
+
+    def dev(x):
+        if w0.dtype == "f32":
+            return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+    reps_dev = []
+    for w in ws:
+        pool = pk.KVPool(w.NB, w.BS, w.L, w.Hkv, w.D, tdt, data=dev(w.pool))
+        reps_dev.append(dict(
+            w=w, pool=pool, tables=torch.from_numpy(w.block_tables).cuda(),
+            lens=torch.from_numpy(w.context_lens).cuda(),
+            pos=torch.from_numpy(w.positions).cuda(), q=dev(w.q), k=dev(w.k_new), v=dev(w.v_new),
+            out=torch.empty(w.S, w.Hq, w.D, dtype=tdt, device="cuda")))
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+
+    def step(i, events=None):
+        r = reps_dev[i % len(reps_dev)]
+        w = r["w"]
+        pk.kv_append(r["pool"], w.layer, r["k"], r["v"], r["tables"], r["pos"])
+        if events is not None:
+            events[0].record(stream)
+        pk.paged_attention_decode(r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"],
+                                  w.scale)
+        if events is not None:
+            events[1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, ev[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    dec_ms = [a.elapsed_time(b) for a, b in ev]
+    dec_avg_ms = float(np.mean(dec_ms))
+
+    step_bytes = np.mean([decode_bytes(r["w"]) + append_bytes(r["w"]) for r in reps_dev])
+    dec_bytes = np.mean([decode_bytes(r["w"]) for r in reps_dev])
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = dec_bytes / (dec_avg_ms * 1e-3) / 1e9
+    tokens_per_s = w0.S / (ms_per_step * 1e-3)
+
+    result = {
+        "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s at batch x context",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w0.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) K/V/q, seeded context lengths and block tables)",
+        "config": {
+            "workload": args.workload,
+            "batch": w0.S, "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.D,
+            "block_size": w0.BS, "layers_in_pool": w0.L, "layer": w0.layer,
+            "sum_context_tokens": int(w0.context_lens.sum()),
+            "max_context": int(w0.context_lens.max()),
+            "input_replicas": reps,
+            "parallelism": "single GPU",
+        },
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(tokens_per_s, 1),
+        "decode_ms": round(dec_avg_ms, 5),
+        "decode_ms_p10_p90": [round(float(np.percentile(dec_ms, 10)), 5),
+                              round(float(np.percentile(dec_ms, 90)), 5)],
+        "roofline": {
+            "kernel": "paged_attention_decode (pass 1 + split merge)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": int(dec_bytes),
+        },
+    }
+
+    if not args.no_gather:
+        r = reps_dev[0]
+        w = r["w"]
+        max_len = w.max_len
+        try:
+            outs = (torch.empty(w.S, max_len, w.Hkv, w.D, dtype=tdt, device="cuda"),
+                    torch.empty(w.S, max_len, w.Hkv, w.D, dtype=tdt, device="cuda"),
+                    torch.empty(w.S, max_len, dtype=torch.uint8, device="cuda"))
+            gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(5)]
+            pk.paged_kv_gather(r["pool"], w.layer, r["tables"], r["lens"], max_len, out=outs)
+            for a, b in gev:
+                a.record(stream)
+                pk.paged_kv_gather(r["pool"], w.layer, r["tables"], r["lens"], max_len, out=outs)
+                b.record(stream)
+            torch.cuda.synchronize()
+            gms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
+            gb = gather_bytes(w, max_len)
+            result["gather"] = {"ms": round(gms, 4), "bytes": gb,
+                                "GB_per_s": round(gb / (gms * 1e-3) / 1e9, 1)}
+            del outs
+        except torch.cuda.OutOfMemoryError:
+            result["gather"] = None
+
+    if not args.no_cpu_baseline:
+        budget = args.cpu_budget_tokens or 60000
+        result["cpu_baseline"] = cpu_baseline(w0, budget)
+
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,184 @@
+/*
+ * pagedkv.h -- paged KV-cache attention decode for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpagedkv.so.  Plain pointers and sizes only.
+ *
+ * Sources (three web pages on paged KV caches):
+ *   [vllmini]    "vllmini: Building a Minimalist PagedAttention and KV Cache
+ *                Engine", sections "PagedAttention Metaphor" and "The CUDA
+ *                Block Kernel".
+ *   [kv-cache]   "KV Cache and Attention Mechanisms: PagedAttention and vLLM",
+ *                section 2 "PagedAttention Architecture".
+ *   [mini-infer] "Paged KV-Cache Memory Management", sections "The Solution",
+ *                "Python Implementation: Physical Block Pool & Batched
+ *                Paging" and "Zero-Copy Batched Attention Gather".
+ *
+ * Conventions shared by every call
+ *   - Device memory is owned by the caller (PyTorch in the Python binding).
+ *     The library never allocates or frees device memory and never
+ *     synchronises; GPU work is enqueued on the given stream (a hipStream_t
+ *     passed as void*; NULL = the default stream) and is asynchronous.
+ *   - Every call returns an int status: PAGEDKV_OK (0) or a negative code.
+ *     No exception crosses the ABI.
+ *   - Pool layout ([mini-infer] "Python Implementation: Physical Block
+ *     Pool"): one contiguous array
+ *         [num_blocks][2 (0 = K, 1 = V)][layers][kv_heads][block_size][head_dim]
+ *     of the pool dtype, row-major.  One physical block holds block_size
+ *     tokens of K and V for every layer and KV head.
+ *   - Block tables ([vllmini] "PagedAttention Metaphor"; [mini-infer] "The
+ *     Solution"): int32, row-major [batch][max_blocks_per_seq]; entry j of
+ *     row b is the physical block holding tokens j*block_size ..
+ *     j*block_size + block_size - 1 of sequence b.  One row serves all heads
+ *     and layers.  Entries at j >= ceil(T_b / block_size) are never read.
+ *   - context_lens: int32 [batch], T_b = number of cached tokens of sequence
+ *     b, counting the token appended in the same step.
+ *   - Values that live in device memory (block ids, context lengths,
+ *     positions) are not validated: checking them would need a
+ *     synchronisation.  Block ids outside [0, num_blocks) or lengths beyond
+ *     max_blocks_per_seq * block_size are undefined behaviour.  Every
+ *     host-visible argument is validated before anything is enqueued.
+ *   - Calls that share a workspace or write the same output must not run
+ *     concurrently on different streams.
+ */
+#ifndef PAGEDKV_H
+#define PAGEDKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define PAGEDKV_OK 0
+#define PAGEDKV_ERR_INVALID_ARG (-1)   /* null pointer, out-of-range size or index */
+#define PAGEDKV_ERR_OUT_OF_BLOCKS (-2) /* free-block stack empty */
+#define PAGEDKV_ERR_UNSUPPORTED (-3)   /* shape/dtype combination with no kernel */
+#define PAGEDKV_ERR_WORKSPACE (-4)     /* workspace missing or too small */
+#define PAGEDKV_ERR_HIP (-5)           /* a HIP runtime call or launch failed */
+
+/* Element types of the pool (and of q / out / new tokens / gather output). */
+typedef enum {
+  PAGEDKV_F32 = 0,
+  PAGEDKV_BF16 = 1
+} pagedkv_dtype_t;
+
+/* Opaque host handle describing a pool.  It records the geometry and the
+ * device address of the pool storage and keeps the host free-block stack.
+ * It does not own the device memory. */
+typedef struct kv_pool kv_pool_t;
+
+/* Bytes of device storage a pool of this geometry needs:
+ * num_blocks * 2 * layers * kv_heads * block_size * head_dim * sizeof(dtype).
+ * Returns 0 for invalid arguments. */
+size_t kv_pool_bytes(int num_blocks, int block_size, int layers, int kv_heads,
+                     int head_dim, pagedkv_dtype_t dtype);
+
+/* Describe a pool over caller-owned device memory of at least
+ * kv_pool_bytes(...) bytes at device_base (any 16-byte-aligned device
+ * allocation; its contents are left untouched).  All num_blocks ids start on
+ * the free-block stack in ascending order, so the first allocation returns
+ * num_blocks - 1 ([mini-infer] "Python Implementation: Physical Block Pool":
+ * the free list is a stack popped from its end).
+ * Requirements: all sizes >= 1, head_dim a multiple of 8 (bf16) or 4 (fp32).
+ * On success *out receives a handle to release with kv_pool_destroy. */
+int kv_pool_create(kv_pool_t** out, int num_blocks, int block_size, int layers,
+                   int kv_heads, int head_dim, pagedkv_dtype_t dtype,
+                   void* device_base, size_t device_bytes);
+
+/* Release the handle (not the device memory).  NULL is accepted. */
+int kv_pool_destroy(kv_pool_t* pool);
+
+/* Geometry query; any output pointer may be NULL. */
+int kv_pool_geometry(const kv_pool_t* pool, int* num_blocks, int* block_size,
+                     int* layers, int* kv_heads, int* head_dim,
+                     pagedkv_dtype_t* dtype, void** device_base);
+
+/* Pop a free physical block id from the top of the host stack
+ * ([mini-infer] "Python Implementation": allocation fails once no block is
+ * free).  Returns PAGEDKV_ERR_OUT_OF_BLOCKS when the stack is empty. */
+int kv_pool_alloc_block(kv_pool_t* pool, int32_t* block_id);
+
+/* Push block_id back onto the stack.  Unlike the page's list, ids outside
+ * [0, num_blocks) and ids that are already free are rejected with
+ * PAGEDKV_ERR_INVALID_ARG. */
+int kv_pool_free_block(kv_pool_t* pool, int32_t block_id);
+
+/* Number of free blocks, or a negative status. */
+int kv_pool_num_free(const kv_pool_t* pool);
+
+/* Append one token per sequence into its tail block
+ * ([kv-cache] section 2: blocks are filled per block as generation
+ * proceeds; [mini-infer] "The Solution": a block stores K and V of B
+ * tokens for every layer).
+ *   k_new, v_new : device, [batch][kv_heads][head_dim], pool dtype.
+ *   block_tables : device, [batch][max_blocks_per_seq] int32.
+ *   positions    : device, [batch] int32; token index written for sequence b
+ *                  (normally T_b - 1).  A negative position skips b.
+ * Writes pool[table[b][pos/B]][0|1][layer][g][pos%B][:] for every g.  The
+ * copy is bit-exact.  The caller must have placed the tail block in the
+ * table (allocate when pos % block_size == 0). */
+int kv_append(kv_pool_t* pool, int layer, const void* k_new, const void* v_new,
+              const int32_t* block_tables, int max_blocks_per_seq,
+              const int32_t* positions, int batch, void* stream);
+
+/* Batched gather of paged K/V into contiguous tensors
+ * ([mini-infer] "Zero-Copy Batched Attention Gather").
+ *   k_out, v_out : device, [batch][max_len][kv_heads][head_dim], pool dtype.
+ *   mask         : device, [batch][max_len] uint8: 1 for t < T_b, else 0.
+ *   context_lens : device, [batch] int32, each <= max_len.
+ * Positions t >= T_b are written as zero bits.  Bit-exact copy. */
+int paged_kv_gather(void* k_out, void* v_out, uint8_t* mask,
+                    const kv_pool_t* pool, int layer,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int batch, int max_len,
+                    void* stream);
+
+/* Bytes of device workspace paged_attention_decode needs for this call
+ * shape (independent of the context lengths' values).  0 on invalid
+ * arguments. */
+size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
+                                       int num_q_heads);
+
+/* Paged-attention decode for one layer
+ * ([vllmini] "The CUDA Block Kernel": for each (sequence, head) the kernel
+ * resolves the sequence's logical token positions through its block table
+ * into physical pages and computes dot-product attention over them;
+ * [kv-cache] section 2: the kernel fetches the physical blocks named by the
+ * block table).
+ *   out, q       : device, [batch][num_q_heads][head_dim], pool dtype.
+ *   num_q_heads  : a multiple of kv_heads; query head h reads KV head
+ *                  h / (num_q_heads / kv_heads).
+ *   scale        : multiplies q.k before the softmax.
+ *   workspace    : device, >= paged_attention_workspace_bytes(...) bytes,
+ *                  256-byte aligned; contents need no initialisation.
+ * out[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) V_t over t < T_b,
+ * computed with fp32 accumulation; bf16 outputs are rounded to nearest
+ * even.  T_b = 0 gives a zero row.  Long contexts are split across many
+ * wavefronts; a second pass merges the partial results. */
+int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
+                           int layer, const int32_t* block_tables,
+                           int max_blocks_per_seq, const int32_t* context_lens,
+                           int batch, int num_q_heads, float scale,
+                           void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* Block-table resolution on its own ([vllmini] "PagedAttention Metaphor":
+ * logical offsets resolved to physical page offsets on the fly).
+ *   slots : device, [batch][max_len] int64; slots[b][t] =
+ *           table[b][t / block_size] * block_size + t % block_size for
+ *           t < T_b, else -1.
+ * Bit-exact; exists so the resolver can be checked on its own. */
+int paged_kv_resolve(int64_t* slots, const int32_t* block_tables,
+                     int max_blocks_per_seq, const int32_t* context_lens,
+                     int batch, int block_size, int max_len, void* stream);
+
+/* Static description of a status code. */
+const char* pagedkv_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDKV_H */

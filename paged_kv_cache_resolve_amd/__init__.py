@@ -1,0 +1,230 @@
+"""Paged-KV-cache attention decode on AMD Instinct MI355X (gfx950).
+
+Thin Python binding over libpagedkv.so: it checks tensors (device, dtype,
+shape, contiguity), passes their device pointers and the current HIP stream
+to the C ABI, and raises on a non-zero status.  Every step of the path runs
+in the library's HIP kernels; PyTorch only supplies device memory and
+streams.
+
+    pool = kv_pool_create(num_blocks, block_size, layers, kv_heads, head_dim, dtype)
+    kv_append(pool, layer, k_new, v_new, block_tables, positions)
+    paged_attention_decode(out, q, pool, layer, block_tables, context_lens, scale)
+    k_all, v_all, mask = paged_kv_gather(pool, layer, block_tables, context_lens, max_len)
+"""
+
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import OutOfBlocksError, PagedKVError  # noqa: F401
+
+_L = _lib.load()
+
+__all__ = [
+    "KVPool", "kv_pool_create", "kv_append", "paged_kv_gather", "paged_attention_decode",
+    "paged_attention_workspace_bytes", "paged_kv_resolve", "PagedKVError", "OutOfBlocksError",
+    "library",
+]
+
+_DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+
+
+def library() -> ctypes.CDLL:
+    """The loaded libpagedkv.so."""
+    return _L
+
+
+def _check(status: int, what: str) -> None:
+    if status == _lib.OK:
+        return
+    if status == _lib.ERR_OUT_OF_BLOCKS:
+        raise OutOfBlocksError(status, what, _L)
+    raise PagedKVError(status, what, _L)
+
+
+def _stream(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dev_tensor(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+class KVPool:
+    """One preallocated pool of fixed-size KV blocks in device memory
+    ([num_blocks, 2 (K/V), layers, kv_heads, block_size, head_dim]) plus the
+    library's host free-block stack."""
+
+    def __init__(self, num_blocks: int, block_size: int = 16, layers: int = 24,
+                 kv_heads: int = 2, head_dim: int = 64, dtype: torch.dtype = torch.bfloat16,
+                 device="cuda", data: torch.Tensor | None = None):
+        if dtype not in _DTYPES:
+            raise ValueError(f"unsupported dtype {dtype}")
+        self.num_blocks, self.block_size, self.layers = num_blocks, block_size, layers
+        self.kv_heads, self.head_dim, self.dtype = kv_heads, head_dim, dtype
+        shape = (num_blocks, 2, layers, kv_heads, block_size, head_dim)
+        if data is None:
+            device = torch.device(device)
+            if device.type != "cuda":
+                raise ValueError("the pool must live in GPU memory")
+            data = torch.zeros(shape, dtype=dtype, device=device)
+        if data.device.type != "cuda":
+            raise ValueError("the pool must live in GPU memory")
+        self.device = data.device
+        _dev_tensor(data, "data", self.device, dtype, shape)
+        self.data = data
+        self._handle = ctypes.c_void_p()
+        nbytes = data.numel() * data.element_size()
+        _check(_L.kv_pool_create(ctypes.byref(self._handle), num_blocks, block_size, layers,
+                                 kv_heads, head_dim, _DTYPES[dtype], ctypes.c_void_p(data.data_ptr()),
+                                 nbytes), "kv_pool_create")
+
+    @property
+    def handle(self) -> ctypes.c_void_p:
+        return self._handle
+
+    def allocate_block(self) -> int:
+        out = ctypes.c_int32()
+        _check(_L.kv_pool_alloc_block(self._handle, ctypes.byref(out)), "kv_pool_alloc_block")
+        return out.value
+
+    def free_block(self, block_id: int) -> None:
+        _check(_L.kv_pool_free_block(self._handle, int(block_id)), "kv_pool_free_block")
+
+    @property
+    def num_free(self) -> int:
+        n = _L.kv_pool_num_free(self._handle)
+        _check(min(n, 0), "kv_pool_num_free")
+        return n
+
+    def __del__(self):
+        h = getattr(self, "_handle", None)
+        if h is not None and h.value:
+            _L.kv_pool_destroy(h)
+            self._handle = ctypes.c_void_p()
+
+
+def kv_pool_create(num_blocks: int, block_size: int = 16, layers: int = 24, kv_heads: int = 2,
+                   head_dim: int = 64, dtype: torch.dtype = torch.bfloat16,
+                   device="cuda") -> KVPool:
+    """Preallocate a zero-filled pool on the GPU and describe it to the library."""
+    return KVPool(num_blocks, block_size, layers, kv_heads, head_dim, dtype, device)
+
+
+def _tables_args(pool, block_tables, batch):
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch:
+        raise ValueError("block_tables must be [batch, max_blocks_per_seq]")
+    return _dev_tensor(block_tables, "block_tables", pool.device, torch.int32), int(block_tables.shape[1])
+
+
+def kv_append(pool: KVPool, layer: int, k_new: torch.Tensor, v_new: torch.Tensor,
+              block_tables: torch.Tensor, positions: torch.Tensor) -> None:
+    """Write k_new/v_new [batch, kv_heads, head_dim] at token positions[b]."""
+    batch = int(positions.shape[0])
+    shape = (batch, pool.kv_heads, pool.head_dim)
+    kp = _dev_tensor(k_new, "k_new", pool.device, pool.dtype, shape)
+    vp = _dev_tensor(v_new, "v_new", pool.device, pool.dtype, shape)
+    tp, mb = _tables_args(pool, block_tables, batch)
+    pp = _dev_tensor(positions, "positions", pool.device, torch.int32, (batch,))
+    _check(_L.kv_append(pool.handle, layer, kp, vp, tp, mb, pp, batch, _stream(pool.device)),
+           "kv_append")
+
+
+def paged_kv_gather(pool: KVPool, layer: int, block_tables: torch.Tensor,
+                    context_lens: torch.Tensor, max_len: int | None = None, out=None):
+    """Gather every sequence's K/V into contiguous [batch, max_len, kv_heads,
+    head_dim] tensors plus a uint8 [batch, max_len] mask (1 = cached token).
+    ``max_len`` defaults to max(context_lens) (read back from the device)."""
+    batch = int(context_lens.shape[0])
+    if max_len is None:
+        max_len = int(context_lens.max().item()) if batch else 0
+    shape = (batch, max_len, pool.kv_heads, pool.head_dim)
+    if out is None:
+        k = torch.empty(shape, dtype=pool.dtype, device=pool.device)
+        v = torch.empty(shape, dtype=pool.dtype, device=pool.device)
+        mask = torch.empty((batch, max_len), dtype=torch.uint8, device=pool.device)
+    else:
+        k, v, mask = out
+    kp = _dev_tensor(k, "k_out", pool.device, pool.dtype, shape)
+    vp = _dev_tensor(v, "v_out", pool.device, pool.dtype, shape)
+    mp = _dev_tensor(mask, "mask", pool.device, torch.uint8, (batch, max_len))
+    tp, mb = _tables_args(pool, block_tables, batch)
+    lp = _dev_tensor(context_lens, "context_lens", pool.device, torch.int32, (batch,))
+    _check(_L.paged_kv_gather(kp, vp, mp, pool.handle, layer, tp, mb, lp, batch, max_len,
+                              _stream(pool.device)), "paged_kv_gather")
+    return k, v, mask
+
+
+def paged_attention_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int) -> int:
+    n = _L.paged_attention_workspace_bytes(pool.handle, batch, num_q_heads)
+    if n == 0 and batch >= 0:
+        raise PagedKVError(_lib.ERR_INVALID_ARG, "paged_attention_workspace_bytes", _L)
+    return n
+
+
+_WORKSPACES: dict = {}
+
+
+def _workspace(pool: KVPool, nbytes: int) -> torch.Tensor:
+    key = (pool.device, torch.cuda.current_stream(pool.device).cuda_stream)
+    ws = _WORKSPACES.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=pool.device)
+        _WORKSPACES[key] = ws
+    return ws
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, pool: KVPool, layer: int,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """out[b, h] = softmax_t(scale * q[b, h] . K_t) V_t over the T_b cached
+    tokens of sequence b, resolved through its block table.  q and out are
+    [batch, num_q_heads, head_dim] in the pool dtype.  A workspace is taken
+    from a per-stream cache unless one is given."""
+    if q.dim() != 3:
+        raise ValueError("q must be [batch, num_q_heads, head_dim]")
+    batch, hq, d = (int(x) for x in q.shape)
+    if d != pool.head_dim:
+        raise ValueError("q head_dim does not match the pool")
+    qp = _dev_tensor(q, "q", pool.device, pool.dtype)
+    op = _dev_tensor(out, "out", pool.device, pool.dtype, q.shape)
+    tp, mb = _tables_args(pool, block_tables, batch)
+    lp = _dev_tensor(context_lens, "context_lens", pool.device, torch.int32, (batch,))
+    need = paged_attention_workspace_bytes(pool, batch, hq)
+    if workspace is None:
+        workspace = _workspace(pool, need)
+    wp = _dev_tensor(workspace, "workspace", pool.device, torch.uint8)
+    _check(_L.paged_attention_decode(op, qp, pool.handle, layer, tp, mb, lp, batch, hq,
+                                     ctypes.c_float(scale), wp, workspace.numel(),
+                                     _stream(pool.device)), "paged_attention_decode")
+    return out
+
+
+def paged_kv_resolve(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,
+                     max_len: int) -> torch.Tensor:
+    """int64 [batch, max_len] global slot ids (physical block * block_size +
+    offset), -1 past each sequence's length."""
+    device = block_tables.device
+    batch = int(context_lens.shape[0])
+    slots = torch.empty((batch, max_len), dtype=torch.int64, device=device)
+    sp = _dev_tensor(slots, "slots", device, torch.int64)
+    if block_tables.dim() != 2 or block_tables.shape[0] != batch:
+        raise ValueError("block_tables must be [batch, max_blocks_per_seq]")
+    tp = _dev_tensor(block_tables, "block_tables", device, torch.int32)
+    lp = _dev_tensor(context_lens, "context_lens", device, torch.int32, (batch,))
+    _check(_L.paged_kv_resolve(sp, tp, int(block_tables.shape[1]), lp, batch, block_size, max_len,
+                               _stream(device)), "paged_kv_resolve")
+    return slots

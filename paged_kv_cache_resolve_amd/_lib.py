@@ -1,0 +1,73 @@
+"""ctypes view of libpagedkv.so (the C ABI declared in include/pagedkv.h).
+
+Loading fails loudly: there is no fallback implementation.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpagedkv.so")
+
+OK = 0
+ERR_INVALID_ARG = -1
+ERR_OUT_OF_BLOCKS = -2
+ERR_UNSUPPORTED = -3
+ERR_WORKSPACE = -4
+ERR_HIP = -5
+
+F32 = 0
+BF16 = 1
+
+_c_int = ctypes.c_int
+_c_size = ctypes.c_size_t
+_vp = ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+
+# name -> (restype, argtypes)
+SIGNATURES = {
+    "kv_pool_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
+    "kv_pool_create": (_c_int, [ctypes.POINTER(_vp), _c_int, _c_int, _c_int, _c_int, _c_int,
+                                _c_int, _vp, _c_size]),
+    "kv_pool_destroy": (_c_int, [_vp]),
+    "kv_pool_geometry": (_c_int, [_vp, ctypes.POINTER(_c_int), ctypes.POINTER(_c_int),
+                                  ctypes.POINTER(_c_int), ctypes.POINTER(_c_int),
+                                  ctypes.POINTER(_c_int), ctypes.POINTER(_c_int),
+                                  ctypes.POINTER(_vp)]),
+    "kv_pool_alloc_block": (_c_int, [_vp, _i32p]),
+    "kv_pool_free_block": (_c_int, [_vp, ctypes.c_int32]),
+    "kv_pool_num_free": (_c_int, [_vp]),
+    "kv_append": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp]),
+    "paged_kv_gather": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int,
+                                 _vp]),
+    "paged_attention_workspace_bytes": (_c_size, [_vp, _c_int, _c_int]),
+    "paged_attention_decode": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int,
+                                        ctypes.c_float, _vp, _c_size, _vp]),
+    "paged_kv_resolve": (_c_int, [_vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp]),
+    "pagedkv_status_string": (ctypes.c_char_p, [_c_int]),
+}
+
+
+def load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing; build it with `python -m paged_kv_cache_resolve_amd.build` "
+            "(there is no fallback implementation)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+class PagedKVError(RuntimeError):
+    def __init__(self, status: int, what: str, lib: ctypes.CDLL):
+        self.status = status
+        msg = lib.pagedkv_status_string(status).decode()
+        super().__init__(f"{what}: {msg} (status {status})")
+
+
+class OutOfBlocksError(PagedKVError, MemoryError):
+    pass

@@ -1,0 +1,228 @@
+// extern "C" entry points of libpagedkv: argument validation, the host
+// free-block stack, workspace layout and kernel dispatch.
+
+#include <math.h>
+#include <string.h>
+
+#include <new>
+
+#include "internal.h"
+
+using namespace pagedkv;
+
+namespace {
+
+bool valid_dtype(pagedkv_dtype_t t) { return t == PAGEDKV_F32 || t == PAGEDKV_BF16; }
+
+size_t pool_bytes_checked(int nb, int bs, int layers, int hkv, int d, pagedkv_dtype_t t) {
+  if (nb < 1 || bs < 1 || layers < 1 || hkv < 1 || d < 1 || !valid_dtype(t)) return 0;
+  const unsigned __int128 n = (unsigned __int128)nb * 2 * layers * hkv * bs * d * elem_size(t);
+  if (n > (unsigned __int128)INT64_MAX) return 0;
+  return (size_t)n;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? PAGEDKV_OK : PAGEDKV_ERR_HIP; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+namespace pagedkv {
+
+// Workspace: [prefix: batch+1 int32][ml: slots*G*2 f32][o: slots*G*D f32],
+// each section 256-byte aligned; slots = batch*kv_heads + kMaxWaves.
+size_t decode_workspace_bytes(int batch, int kv_heads, int group, int head_dim) {
+  const size_t slots = (size_t)batch * kv_heads + kMaxWaves;
+  return align256(sizeof(int32_t) * (size_t)(batch + 1)) +
+         align256(sizeof(float) * slots * group * 2) +
+         align256(sizeof(float) * slots * group * head_dim);
+}
+
+void decode_workspace_carve(void* ws, int batch, int kv_heads, int group, int head_dim,
+                            int32_t** prefix, float** ml, float** o) {
+  const size_t slots = (size_t)batch * kv_heads + kMaxWaves;
+  char* p = static_cast<char*>(ws);
+  *prefix = reinterpret_cast<int32_t*>(p);
+  p += align256(sizeof(int32_t) * (size_t)(batch + 1));
+  *ml = reinterpret_cast<float*>(p);
+  p += align256(sizeof(float) * slots * group * 2);
+  *o = reinterpret_cast<float*>(p);
+}
+
+}  // namespace pagedkv
+
+extern "C" {
+
+size_t kv_pool_bytes(int num_blocks, int block_size, int layers, int kv_heads, int head_dim,
+                     pagedkv_dtype_t dtype) {
+  return pool_bytes_checked(num_blocks, block_size, layers, kv_heads, head_dim, dtype);
+}
+
+int kv_pool_create(kv_pool_t** out, int num_blocks, int block_size, int layers, int kv_heads,
+                   int head_dim, pagedkv_dtype_t dtype, void* device_base, size_t device_bytes) {
+  if (!out) return PAGEDKV_ERR_INVALID_ARG;
+  *out = nullptr;
+  const size_t need = pool_bytes_checked(num_blocks, block_size, layers, kv_heads, head_dim, dtype);
+  if (need == 0 || !device_base || device_bytes < need) return PAGEDKV_ERR_INVALID_ARG;
+  if (head_dim % (dtype == PAGEDKV_F32 ? 4 : 8) != 0) return PAGEDKV_ERR_INVALID_ARG;
+  if (reinterpret_cast<uintptr_t>(device_base) % 16 != 0) return PAGEDKV_ERR_INVALID_ARG;
+  kv_pool* p = new (std::nothrow) kv_pool;
+  if (!p) return PAGEDKV_ERR_INVALID_ARG;
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->layers = layers;
+  p->kv_heads = kv_heads;
+  p->head_dim = head_dim;
+  p->dtype = dtype;
+  p->base = static_cast<char*>(device_base);
+  p->bytes = device_bytes;
+  try {
+    p->free_stack.resize(num_blocks);
+    p->is_free.assign(num_blocks, 1);
+  } catch (...) {
+    delete p;
+    return PAGEDKV_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < num_blocks; ++i) p->free_stack[i] = i;   // top = num_blocks - 1
+  *out = p;
+  return PAGEDKV_OK;
+}
+
+int kv_pool_destroy(kv_pool_t* pool) {
+  delete pool;
+  return PAGEDKV_OK;
+}
+
+int kv_pool_geometry(const kv_pool_t* pool, int* num_blocks, int* block_size, int* layers,
+                     int* kv_heads, int* head_dim, pagedkv_dtype_t* dtype, void** device_base) {
+  if (!pool) return PAGEDKV_ERR_INVALID_ARG;
+  if (num_blocks) *num_blocks = pool->num_blocks;
+  if (block_size) *block_size = pool->block_size;
+  if (layers) *layers = pool->layers;
+  if (kv_heads) *kv_heads = pool->kv_heads;
+  if (head_dim) *head_dim = pool->head_dim;
+  if (dtype) *dtype = pool->dtype;
+  if (device_base) *device_base = pool->base;
+  return PAGEDKV_OK;
+}
+
+int kv_pool_alloc_block(kv_pool_t* pool, int32_t* block_id) {
+  if (!pool || !block_id) return PAGEDKV_ERR_INVALID_ARG;
+  if (pool->free_stack.empty()) return PAGEDKV_ERR_OUT_OF_BLOCKS;
+  const int32_t id = pool->free_stack.back();
+  pool->free_stack.pop_back();
+  pool->is_free[id] = 0;
+  *block_id = id;
+  return PAGEDKV_OK;
+}
+
+int kv_pool_free_block(kv_pool_t* pool, int32_t block_id) {
+  if (!pool || block_id < 0 || block_id >= pool->num_blocks) return PAGEDKV_ERR_INVALID_ARG;
+  if (pool->is_free[block_id]) return PAGEDKV_ERR_INVALID_ARG;
+  pool->is_free[block_id] = 1;
+  pool->free_stack.push_back(block_id);
+  return PAGEDKV_OK;
+}
+
+int kv_pool_num_free(const kv_pool_t* pool) {
+  if (!pool) return PAGEDKV_ERR_INVALID_ARG;
+  return (int)pool->free_stack.size();
+}
+
+int kv_append(kv_pool_t* pool, int layer, const void* k_new, const void* v_new,
+              const int32_t* block_tables, int max_blocks_per_seq, const int32_t* positions,
+              int batch, void* stream) {
+  if (!pool || batch < 0 || layer < 0 || layer >= pool->layers || max_blocks_per_seq < 1)
+    return PAGEDKV_ERR_INVALID_ARG;
+  if (batch == 0) return PAGEDKV_OK;
+  if (!k_new || !v_new || !block_tables || !positions) return PAGEDKV_ERR_INVALID_ARG;
+  return hip_status(launch_append(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq,
+                                  positions, batch, static_cast<hipStream_t>(stream)));
+}
+
+int paged_kv_gather(void* k_out, void* v_out, uint8_t* mask, const kv_pool_t* pool, int layer,
+                    const int32_t* block_tables, int max_blocks_per_seq,
+                    const int32_t* context_lens, int batch, int max_len, void* stream) {
+  if (!pool || batch < 0 || max_len < 0 || layer < 0 || layer >= pool->layers ||
+      max_blocks_per_seq < 1 || batch > 65535)
+    return PAGEDKV_ERR_INVALID_ARG;
+  if (batch == 0 || max_len == 0) return PAGEDKV_OK;
+  if (!k_out || !v_out || !mask || !block_tables || !context_lens) return PAGEDKV_ERR_INVALID_ARG;
+  const int units = pool->head_dim * elem_size(pool->dtype) / 16;
+  if (units > 256 || (units & (units - 1)) != 0) return PAGEDKV_ERR_UNSUPPORTED;
+  return hip_status(launch_gather(k_out, v_out, mask, pool, layer, block_tables,
+                                  max_blocks_per_seq, context_lens, batch, max_len,
+                                  static_cast<hipStream_t>(stream)));
+}
+
+size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch, int num_q_heads) {
+  if (!pool || batch < 0 || num_q_heads < 1 || num_q_heads % pool->kv_heads != 0) return 0;
+  return decode_workspace_bytes(batch, pool->kv_heads, num_q_heads / pool->kv_heads,
+                                pool->head_dim);
+}
+
+int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool, int layer,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int batch, int num_q_heads, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (!pool || batch < 0 || layer < 0 || layer >= pool->layers || max_blocks_per_seq < 1 ||
+      num_q_heads < 1 || num_q_heads % pool->kv_heads != 0 || !isfinite(scale))
+    return PAGEDKV_ERR_INVALID_ARG;
+  if (batch == 0) return PAGEDKV_OK;
+  if (!out || !q || !block_tables || !context_lens) return PAGEDKV_ERR_INVALID_ARG;
+  if (batch > kMaxBatchLds) return PAGEDKV_ERR_UNSUPPORTED;
+  const int group = num_q_heads / pool->kv_heads;
+  const bool use_mfma = mfma_supported(pool, group);
+  if (!use_mfma && !generic_supported(pool, group)) return PAGEDKV_ERR_UNSUPPORTED;
+  const size_t need = decode_workspace_bytes(batch, pool->kv_heads, group, pool->head_dim);
+  if (!workspace || workspace_bytes < need) return PAGEDKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PAGEDKV_ERR_WORKSPACE;
+
+  DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  p.pool = geom_of(pool);
+  p.q = q;
+  p.out = out;
+  p.block_tables = block_tables;
+  p.context_lens = context_lens;
+  decode_workspace_carve(workspace, batch, pool->kv_heads, group, pool->head_dim, &p.ws_prefix,
+                         &p.ws_ml, &p.ws_o);
+  p.layer = layer;
+  p.max_blocks_per_seq = max_blocks_per_seq;
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.group = group;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.dtype = pool->dtype;
+  p.min_chunks = 0;   // launcher default
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = use_mfma ? launch_decode_mfma(p, s) : launch_decode_generic(p, s);
+  if (e != hipSuccess) return PAGEDKV_ERR_HIP;
+  e = launch_decode_reduce(p, use_mfma ? kMfmaChunk : kGenericChunk, s);
+  return hip_status(e);
+}
+
+int paged_kv_resolve(int64_t* slots, const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* context_lens, int batch, int block_size, int max_len,
+                     void* stream) {
+  if (batch < 0 || max_len < 0 || block_size < 1 || max_blocks_per_seq < 1 || batch > 65535)
+    return PAGEDKV_ERR_INVALID_ARG;
+  if (batch == 0 || max_len == 0) return PAGEDKV_OK;
+  if (!slots || !block_tables || !context_lens) return PAGEDKV_ERR_INVALID_ARG;
+  return hip_status(launch_resolve(slots, block_tables, max_blocks_per_seq, context_lens, batch,
+                                   block_size, max_len, static_cast<hipStream_t>(stream)));
+}
+
+const char* pagedkv_status_string(int status) {
+  switch (status) {
+    case PAGEDKV_OK: return "ok";
+    case PAGEDKV_ERR_INVALID_ARG: return "invalid argument";
+    case PAGEDKV_ERR_OUT_OF_BLOCKS: return "Out of KV-Cache Physical Blocks";
+    case PAGEDKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case PAGEDKV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case PAGEDKV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,240 @@
+// Paged-attention decode, pass 1, general shapes (fp32 or bf16 pools, any
+// block size, head_dim a multiple of 4 up to 256, up to 16 query heads per KV
+// head), plain VALU arithmetic.
+//
+// Same computation as the MFMA kernel ("vllmini", section "The CUDA Block
+// Kernel": per (sequence, head), resolve logical positions through the block
+// table and attend over the physical pages) and the same work split
+// (decode_split.h), with 64-token chunks and one wavefront per workgroup:
+//   * scores: lane t owns token t of the chunk, resolves its own block-table
+//     entry, and forms the G dot products against q (held in LDS, already
+//     multiplied by scale*log2(e));
+//   * online softmax per head with wavefront max/sum reductions;
+//   * weighted V sum: lane owns dims lane, lane+64, ...; token rows are
+//     walked in order with addresses broadcast by v_readlane.
+
+#include <math.h>
+
+#include "decode_split.h"
+#include "internal.h"
+
+namespace pagedkv {
+namespace {
+
+constexpr int kGenDimsPerLane = 4;   // head_dim <= 256
+
+template <typename TS> __device__ __forceinline__ float to_f32(TS x);
+template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) {
+  return __uint_as_float((uint32_t)x << 16);
+}
+template <typename TS> __device__ __forceinline__ TS from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
+  return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+
+// Four consecutive elements as floats (16-byte or 8-byte load).
+__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ float4 load4(const uint16_t* p) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+template <typename TS>
+__device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int lane,
+                                int64_t wave, int b, int g, int j0, int j1, int nb) {
+  const int G = p.group;
+  const int D = p.pool.head_dim;
+  const int BS = p.pool.block_size;
+  const int T = p.context_lens[b];
+  const TS* pool = reinterpret_cast<const TS*>(p.pool.base);
+  const int64_t head_off = (int64_t)p.layer * p.pool.layer_stride + (int64_t)g * p.pool.head_stride;
+  const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
+
+  // q rows of the group, pre-multiplied by scale*log2(e)
+  const TS* q = static_cast<const TS*>(p.q) + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
+  for (int i = lane; i < G * D; i += 64) qs[i] = to_f32<TS>(q[i]) * p.scale_log2;
+  __syncthreads();
+
+  float acc[kMaxGroup][kGenDimsPerLane];
+  float m[kMaxGroup], l[kMaxGroup];
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    m[h] = -INFINITY;
+    l[h] = 0.f;
+#pragma unroll
+    for (int i = 0; i < kGenDimsPerLane; ++i) acc[h][i] = 0.f;
+  }
+
+  for (int j = j0; j < j1; ++j) {
+    const int tok = j * kGenericChunk + lane;
+    const bool valid = tok < T;
+    int64_t row = 0;   // element offset of this lane's token row (K); V adds kv_stride
+    if (valid) {
+      const int phys = trow[tok / BS];
+      row = (int64_t)phys * p.pool.block_stride + head_off + (int64_t)(tok % BS) * D;
+    }
+    float s[kMaxGroup];
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) s[h] = 0.f;
+    if (valid) {
+      for (int d = 0; d < D; d += 4) {
+        const float4 k = load4(pool + row + d);
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h) {
+          if (h < G) {
+            const float4 qq = *reinterpret_cast<const float4*>(qs + h * D + d);
+            s[h] += qq.x * k.x + qq.y * k.y + qq.z * k.z + qq.w * k.w;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < kMaxGroup; ++h) {
+      if (h < G) {
+        const float sv = valid ? s[h] : -INFINITY;
+        const float mn = fmaxf(m[h], wave_max(sv));
+        const float alpha = __builtin_amdgcn_exp2f(m[h] - mn);
+        const float pv = __builtin_amdgcn_exp2f(sv - mn);
+        l[h] = l[h] * alpha + wave_sum(pv);
+        m[h] = mn;
+#pragma unroll
+        for (int i = 0; i < kGenDimsPerLane; ++i) acc[h][i] *= alpha;
+        ps[h * 64 + lane] = pv;
+      }
+    }
+    __syncthreads();
+    const int ntok = min(64, T - j * kGenericChunk);
+    const uint32_t row_lo = (uint32_t)(row & 0xffffffffu);
+    const uint32_t row_hi = (uint32_t)(row >> 32);
+    for (int t = 0; t < ntok; ++t) {
+      const int64_t r = ((int64_t)(uint32_t)__builtin_amdgcn_readlane((int)row_hi, t) << 32) |
+                        (uint32_t)__builtin_amdgcn_readlane((int)row_lo, t);
+      const TS* vrow = pool + r + p.pool.kv_stride;
+#pragma unroll
+      for (int i = 0; i < kGenDimsPerLane; ++i) {
+        const int d = lane + 64 * i;
+        if (d < D) {
+          const float v = to_f32<TS>(vrow[d]);
+#pragma unroll
+          for (int h = 0; h < kMaxGroup; ++h)
+            if (h < G) acc[h][i] += ps[h * 64 + t] * v;
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  const int pair = b * p.pool.kv_heads + g;
+  const bool whole = (j0 == 0 && j1 == nb);
+  const int64_t slot = pair + wave;
+#pragma unroll
+  for (int h = 0; h < kMaxGroup; ++h) {
+    if (h >= G) continue;
+    if (whole) {
+      TS* o = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + (int64_t)g * G + h) * D;
+      const float inv = 1.0f / l[h];
+#pragma unroll
+      for (int i = 0; i < kGenDimsPerLane; ++i) {
+        const int d = lane + 64 * i;
+        if (d < D) o[d] = from_f32<TS>(acc[h][i] * inv);
+      }
+    } else {
+      float* o = p.ws_o + (slot * G + h) * D;
+#pragma unroll
+      for (int i = 0; i < kGenDimsPerLane; ++i) {
+        const int d = lane + 64 * i;
+        if (d < D) o[d] = acc[h][i];
+      }
+      if (lane == 0) {
+        p.ws_ml[(slot * G + h) * 2 + 0] = m[h];
+        p.ws_ml[(slot * G + h) * 2 + 1] = l[h];
+      }
+    }
+  }
+}
+
+template <typename TS>
+__global__ __launch_bounds__(64) void decode_generic_kernel(DecodeParams p) {
+  extern __shared__ int32_t lds[];
+  __shared__ int32_t scan[64];
+  int32_t* prefix = lds;
+  // q (G x D floats) and probabilities (G x 64 floats) after the prefix
+  const int pre_words = ((p.batch + 1) + 3) & ~3;
+  float* qs = reinterpret_cast<float*>(lds + pre_words);
+  float* ps = qs + p.group * p.pool.head_dim;
+
+  block_chunk_prefix<64>(p.context_lens, p.batch, kGenericChunk, prefix, scan);
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= p.batch; i += 64) p.ws_prefix[i] = prefix[i];
+
+  const int lane = threadIdx.x;
+  const int64_t wave = blockIdx.x;
+  const int H = p.pool.kv_heads;
+  const int64_t C = (int64_t)H * prefix[p.batch];
+  const int64_t We = waves_eff(C, p.waves, p.min_chunks);
+  if (wave >= We) return;
+  int64_t c = wave_begin(wave, C, We);
+  const int64_t c_end = wave_begin(wave + 1, C, We);
+  int b = seq_of_chunk(prefix, p.batch, c, H);
+  while (c < c_end) {
+    const int pb = prefix[b];
+    const int nb = prefix[b + 1] - pb;
+    const int64_t base = (int64_t)H * pb;
+    const int rel = (int)(c - base);
+    const int g = rel / nb;
+    const int j0 = rel - g * nb;
+    const int64_t left = c_end - c;
+    const int j1 = left < (int64_t)(nb - j0) ? j0 + (int)left : nb;
+    generic_segment<TS>(p, qs, ps, lane, wave, b, g, j0, j1, nb);
+    __syncthreads();
+    c += j1 - j0;
+    if (c >= base + (int64_t)H * nb) {
+      ++b;
+      while (b < p.batch && prefix[b + 1] == prefix[b]) ++b;
+    }
+  }
+}
+
+}  // namespace
+
+bool generic_supported(const kv_pool* pool, int group) {
+  return group >= 1 && group <= kMaxGroup && pool->head_dim % 4 == 0 &&
+         pool->head_dim <= 64 * kGenDimsPerLane;
+}
+
+hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
+  const int pre_words = ((p.batch + 1) + 3) & ~3;
+  const size_t lds = sizeof(int32_t) * pre_words +
+                     sizeof(float) * (size_t)p.group * (p.pool.head_dim + 64);
+  const bool f32 = p.dtype == PAGEDKV_F32;
+  const void* fn = f32 ? reinterpret_cast<const void*>(&decode_generic_kernel<float>)
+                       : reinterpret_cast<const void*>(&decode_generic_kernel<uint16_t>);
+  int wgs = 0;
+  hipError_t e = resident_workgroups(fn, 64, lds, &wgs);
+  if (e != hipSuccess) return e;
+  int waves = wgs;
+  if (waves > kMaxWaves) waves = kMaxWaves;
+  p.waves = waves;
+  if (p.min_chunks < 1) p.min_chunks = 2;
+  if (f32)
+    hipLaunchKernelGGL(decode_generic_kernel<float>, dim3(waves), dim3(64), lds, s, p);
+  else
+    hipLaunchKernelGGL(decode_generic_kernel<uint16_t>, dim3(waves), dim3(64), lds, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace pagedkv

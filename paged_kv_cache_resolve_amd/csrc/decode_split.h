@@ -1,0 +1,76 @@
+// Device helpers for the decode work split (see DecodeParams in internal.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pagedkv {
+
+__device__ __forceinline__ int chunks_of(int T, int ct) {
+  return T > 0 ? (T + ct - 1) / ct : 0;
+}
+
+// prefix[b] = sum_{b' < b} chunks_of(T_b', ct) for b in [0, batch], computed by
+// one workgroup of NT threads into LDS.  `scan` is NT ints of LDS scratch.
+// Every thread of the workgroup must call this; it ends with a barrier.
+template <int NT>
+__device__ void block_chunk_prefix(const int32_t* __restrict__ lens, int batch,
+                                   int ct, int32_t* prefix, int32_t* scan) {
+  const int tid = threadIdx.x;
+  const int per = (batch + NT - 1) / NT;
+  const int lo = min(batch, tid * per);
+  const int hi = min(batch, lo + per);
+  int local = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int n = chunks_of(lens[i], ct);
+    prefix[i + 1] = n;
+    local += n;
+  }
+  scan[tid] = local;
+  __syncthreads();
+  // Hillis-Steele inclusive scan over the NT per-thread sums.
+  for (int d = 1; d < NT; d <<= 1) {
+    const int add = tid >= d ? scan[tid - d] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  int run = scan[tid] - local;   // exclusive offset of this thread's segment
+  for (int i = lo; i < hi; ++i) {
+    run += prefix[i + 1];
+    prefix[i + 1] = run;
+  }
+  if (tid == 0) prefix[0] = 0;
+  __syncthreads();
+}
+
+// Number of wavefronts that receive work: all W, unless that would leave
+// fewer than min_chunks chunks per wavefront.
+__device__ __forceinline__ int64_t waves_eff(int64_t C, int W, int min_chunks) {
+  if (C <= 0) return 0;
+  const int64_t cap = (C + min_chunks - 1) / min_chunks;
+  return cap < W ? cap : W;
+}
+
+__device__ __forceinline__ int64_t wave_begin(int64_t w, int64_t C, int64_t We) {
+  return w * C / We;
+}
+
+// The wavefront whose range holds chunk c (largest w with begin(w) <= c).
+__device__ __forceinline__ int64_t wave_of_chunk(int64_t c, int64_t C, int64_t We) {
+  return ((c + 1) * We - 1) / C;
+}
+
+// Largest b in [0, batch) with kv_heads * prefix[b] <= c and a non-empty
+// chunk range (prefix[b + 1] > prefix[b]).  Requires c < kv_heads * prefix[batch].
+__device__ __forceinline__ int seq_of_chunk(const int32_t* prefix, int batch,
+                                            int64_t c, int kv_heads) {
+  int lo = 0, hi = batch;   // invariant: answer in [lo, hi)
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)kv_heads * prefix[mid] <= c) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+}  // namespace pagedkv

@@ -1,0 +1,124 @@
+// Internal declarations shared by the host entry points and the kernel
+// launchers of libpagedkv.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+#include "pagedkv.h"
+
+struct kv_pool {
+  int num_blocks;
+  int block_size;
+  int layers;
+  int kv_heads;
+  int head_dim;
+  pagedkv_dtype_t dtype;
+  char* base;          // device address of element [0][0][0][0][0][0]
+  size_t bytes;
+  std::vector<int32_t> free_stack;   // top = back()
+  std::vector<uint8_t> is_free;
+};
+
+namespace pagedkv {
+
+// Geometry of the pool passed to kernels by value.  Strides in elements.
+struct PoolGeom {
+  const char* base;
+  int64_t block_stride;  // 2 * layers * kv_heads * block_size * head_dim
+  int64_t kv_stride;     // layers * kv_heads * block_size * head_dim
+  int64_t layer_stride;  // kv_heads * block_size * head_dim
+  int64_t head_stride;   // block_size * head_dim
+  int block_size;
+  int head_dim;
+  int kv_heads;
+  int num_blocks;
+};
+
+inline PoolGeom geom_of(const kv_pool* p) {
+  PoolGeom g;
+  g.base = p->base;
+  g.head_stride = (int64_t)p->block_size * p->head_dim;
+  g.layer_stride = g.head_stride * p->kv_heads;
+  g.kv_stride = g.layer_stride * p->layers;
+  g.block_stride = g.kv_stride * 2;
+  g.block_size = p->block_size;
+  g.head_dim = p->head_dim;
+  g.kv_heads = p->kv_heads;
+  g.num_blocks = p->num_blocks;
+  return g;
+}
+
+inline int elem_size(pagedkv_dtype_t t) { return t == PAGEDKV_F32 ? 4 : 2; }
+
+// ---------------------------------------------------------------------------
+// Decode work split.
+//
+// A "chunk" is CT consecutive tokens of one (sequence b, KV head g) pair.
+// Pair p = b * kv_heads + g has n_b = ceil(T_b / CT) chunks; pairs are laid
+// end to end in p order, so the chunk space has C = kv_heads * sum_b n_b
+// entries.  W_eff wavefronts each take one contiguous, equal-sized range of
+// that space ([w*C/W_eff, (w+1)*C/W_eff)); a wavefront that covers a whole
+// pair writes the output directly, otherwise it leaves a partial
+// (max, sum, unnormalised output) in slot p + w of the workspace, which is
+// unique because wave ranges and pairs are both ordered.  The second pass
+// merges the partials of every split pair.
+// ---------------------------------------------------------------------------
+struct DecodeParams {
+  PoolGeom pool;
+  const void* q;
+  void* out;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t* ws_prefix;     // [batch + 1]: prefix sums of n_b (written by pass 1)
+  float* ws_ml;           // [slots][G][2]: running max (log2 units) and sum
+  float* ws_o;            // [slots][G][D]: unnormalised partial outputs
+  int layer;
+  int max_blocks_per_seq;
+  int batch;
+  int num_q_heads;
+  int group;              // G = num_q_heads / kv_heads
+  float scale_log2;       // scale * log2(e)
+  int waves;              // W (launched), W_eff <= W is derived on device
+  int min_chunks;         // minimum chunks per wavefront
+  pagedkv_dtype_t dtype;  // element type of pool, q and out
+};
+
+constexpr int kMaxWaves = 8192;          // upper bound on W (256 CUs x 32)
+constexpr int kMaxGroup = 16;            // query heads per KV head
+constexpr int kMfmaChunk = 16;           // tokens per chunk, MFMA kernel
+constexpr int kGenericChunk = 64;        // tokens per chunk, VALU kernel
+constexpr int kMaxBatchLds = 16384;      // sequences whose prefix fits in LDS
+
+size_t decode_workspace_bytes(int batch, int kv_heads, int group, int head_dim);
+void decode_workspace_carve(void* ws, int batch, int kv_heads, int group,
+                            int head_dim, int32_t** prefix, float** ml,
+                            float** o);
+
+// Launchers (return a hipError_t-derived status via hipGetLastError).
+hipError_t launch_append(const kv_pool* pool, int layer, const void* k_new,
+                         const void* v_new, const int32_t* tables, int mb,
+                         const int32_t* positions, int batch, hipStream_t s);
+hipError_t launch_gather(void* k_out, void* v_out, uint8_t* mask,
+                         const kv_pool* pool, int layer, const int32_t* tables,
+                         int mb, const int32_t* lens, int batch, int max_len,
+                         hipStream_t s);
+hipError_t launch_resolve(int64_t* slots, const int32_t* tables, int mb,
+                          const int32_t* lens, int batch, int block_size,
+                          int max_len, hipStream_t s);
+
+// Workgroups the device holds at once for kernel `fn` (cached per device).
+hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out);
+
+// Decode pass 1 variants and pass 2.  The *_supported predicates say which
+// shapes each pass-1 kernel handles.
+bool mfma_supported(const kv_pool* pool, int group);
+bool generic_supported(const kv_pool* pool, int group);
+hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s);
+hipError_t launch_decode_reduce(const DecodeParams& p, int chunk_tokens,
+                                hipStream_t s);
+
+}  // namespace pagedkv

@@ -1,0 +1,293 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.  Resolve, gather and append must match bit for bit;
+attention must match within max-abs 1e-4 (fp32) or 2e-2 + 2e-2|ref| (bf16).
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_resolve_amd as pk
+from workloads import make_workload
+
+from gpu_helpers import (DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say,
+                         t_dtype)
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU"),
+]
+
+NAN_BITS = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0)}
+
+
+def poison(w):
+    """NaN into every pool slot no sequence owns (all layers, K and V) and
+    garbage into unused table entries; returns the workload, modified."""
+    slots = oracle.resolve_slots(w.block_tables, w.context_lens, w.BS, max(w.max_len, 1))
+    used = np.zeros(w.NB * w.BS, dtype=bool)
+    used[slots[slots >= 0]] = True
+    used = used.reshape(w.NB, w.BS)
+    blk, off = np.nonzero(~used)
+    w.pool[blk, :, :, :, off, :] = NAN_BITS[w.dtype]
+    w.block_tables = np.where(w.block_tables < 0, np.int32(2**31 - 1), w.block_tables).astype(np.int32)
+    return w
+
+
+def custom(dtype, S, Hq, Hkv, D, BS, lens, L=1, layer=0, seed_offset=0, nb_slack=3):
+    lens = np.asarray(lens, dtype=np.int32)
+    mb = max(1, max(math.ceil(int(t) / BS) for t in lens))
+    nb = sum(math.ceil(int(t) / BS) for t in lens) + nb_slack
+    return make_workload(0, dtype=dtype, S=S, Hq=Hq, Hkv=Hkv, D=D, BS=BS, L=L, layer=layer,
+                         context_lens=lens, MB=mb, NB=nb, tables="perm", seed_offset=seed_offset)
+
+
+# ----------------------------------------------------------------------------
+# resolve
+# ----------------------------------------------------------------------------
+
+def test_resolve_page_examples():
+    say("resolve page examples")
+    tables = torch.tensor([[14, 89, 3], [4, 1, 7]], dtype=torch.int32, device="cuda")
+    lens = torch.tensor([41, 41], dtype=torch.int32, device="cuda")
+    got = pk.paged_kv_resolve(tables, lens, 16, 48).cpu().numpy()
+    ref = oracle.resolve_slots(tables.cpu().numpy(), lens.cpu().numpy(), 16, 48)
+    assert got.tobytes() == ref.tobytes()
+    assert got[0, 16] == 1424 and got[1, 40] == 120 and got[0, 41] == -1
+
+
+@pytest.mark.parametrize("idx", [0, 1, 4])
+def test_resolve_workloads(idx):
+    say(f"resolve workload {idx}")
+    w = make_workload(idx, with_pool=False)
+    max_len = w.max_len + 7
+    tables = torch.from_numpy(w.block_tables).cuda()
+    lens = torch.from_numpy(w.context_lens).cuda()
+    got = pk.paged_kv_resolve(tables, lens, w.BS, max_len).cpu().numpy()
+    ref = oracle.resolve_slots(w.block_tables, w.context_lens, w.BS, max_len)
+    assert got.tobytes() == ref.tobytes()
+
+
+# ----------------------------------------------------------------------------
+# gather
+# ----------------------------------------------------------------------------
+
+def _check_gather(w, max_len=None, rows=None):
+    dw = DeviceWorkload(w)
+    max_len = w.max_len if max_len is None else max_len
+    k, v, mask = pk.paged_kv_gather(dw.pool, w.layer, dw.tables, dw.lens, max_len)
+    rows = list(range(w.S)) if rows is None else rows
+    sub = lambda a: a[rows]  # noqa: E731
+    rk, rv, rm = oracle.paged_kv_gather(w.pool, w.layer, w.block_tables[rows], w.context_lens[rows],
+                                        max_len)
+    idx = torch.tensor(rows, device="cuda")
+    assert dev_to_np(k.index_select(0, idx)).tobytes() == rk.tobytes()
+    assert dev_to_np(v.index_select(0, idx)).tobytes() == rv.tobytes()
+    assert sub(mask.cpu().numpy()).tobytes() == rm.tobytes()
+
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_gather_workloads(idx):
+    say(f"gather workload {idx}")
+    _check_gather(poison(make_workload(idx)), )
+
+
+@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("bf16", 64, 32), ("f32", 64, 16),
+                                        ("bf16", 32, 8), ("f32", 128, 1)])
+def test_gather_shapes_and_padding(dtype, D, BS):
+    say(f"gather {dtype} D={D} BS={BS}")
+    w = poison(custom(dtype, 6, 4, 2, D, BS, [0, 1, BS - 1 if BS > 1 else 1, BS, BS + 1, 3 * BS + 5],
+                      L=2, layer=1))
+    _check_gather(w, max_len=w.max_len + 3)
+
+
+# ----------------------------------------------------------------------------
+# append
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("idx", [0, 1])
+def test_append_whole_pool(idx):
+    say(f"append workload {idx}")
+    w = make_workload(idx)
+    dw = DeviceWorkload(w)
+    pk.kv_append(dw.pool, w.layer, dw.k_new, dw.v_new, dw.tables, dw.positions)
+    ref = oracle.kv_append(w.pool, w.layer, w.block_tables, w.positions, w.k_new, w.v_new)
+    assert dev_to_np(dw.pool.data).tobytes() == ref.tobytes()
+
+
+def test_append_skips_negative_positions():
+    say("append negative positions")
+    w = custom("bf16", 4, 4, 2, 64, 16, [5, 17, 1, 40], L=3, layer=2)
+    dw = DeviceWorkload(w)
+    pos = np.array([4, -1, 0, -7], np.int32)
+    pk.kv_append(dw.pool, w.layer, dw.k_new, dw.v_new, dw.tables, torch.from_numpy(pos).cuda())
+    ref = oracle.kv_append(w.pool, w.layer, w.block_tables, pos, w.k_new, w.v_new)
+    assert dev_to_np(dw.pool.data).tobytes() == ref.tobytes()
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+
+def _oracle_decode(w, seqs=None):
+    return oracle.paged_attention_decode(w.pool, w.dtype, w.layer, w.block_tables, w.context_lens,
+                                         w.q, w.scale, seqs=seqs)
+
+
+def test_decode_tiny_fp32():
+    say("decode workload 0 (fp32)")
+    w = poison(make_workload(0))
+    dw = DeviceWorkload(w)
+    assert_attention_close(dw.decode(), _oracle_decode(w), w.dtype, what="w0")
+
+
+def test_append_then_decode_churned_pool():
+    """Workload 1: append the new token, then decode layer 11 over it."""
+    say("append+decode workload 1")
+    w = make_workload(1)
+    dw = DeviceWorkload(w)
+    pk.kv_append(dw.pool, w.layer, dw.k_new, dw.v_new, dw.tables, dw.positions)
+    out = dw.decode()
+    oracle.kv_append(w.pool, w.layer, w.block_tables, w.positions, w.k_new, w.v_new, in_place=True)
+    assert_attention_close(out, _oracle_decode(w), w.dtype, what="w1")
+
+
+@pytest.mark.parametrize("idx,S", [(2, 6), (3, 2), (4, 24)])
+def test_decode_reduced_batches(idx, S):
+    """Named shapes with fewer sequences, every output compared."""
+    say(f"decode workload {idx} with S={S}")
+    w = poison(make_workload(idx, S=S))
+    dw = DeviceWorkload(w)
+    assert_attention_close(dw.decode(), _oracle_decode(w), w.dtype, what=f"w{idx} S={S}")
+
+
+@pytest.mark.parametrize("idx,nsample", [(2, 16), (3, 3)])
+def test_decode_full_size_sampled(idx, nsample):
+    """Full-size workloads in the configuration the benchmark times; the
+    oracle checks a seeded sample of sequences (all heads, all dims)."""
+    say(f"decode workload {idx} full size")
+    w = make_workload(idx)
+    dw = DeviceWorkload(w)
+    out = dw.decode()
+    rng = np.random.default_rng(99 + idx)
+    seqs = sorted(rng.choice(w.S, size=min(nsample, w.S), replace=False).tolist())
+    seqs = sorted(set(seqs) | {int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))})
+    ref = _oracle_decode(w, seqs=seqs)
+    assert_attention_close(out, ref, w.dtype, rows=seqs, what=f"w{idx} full")
+    again = dw.decode()
+    assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "decode not deterministic"
+
+
+def test_high_concurrency_step_full_size():
+    """Workload 4: append the new token into each tail block, decode, then
+    gather; decode checked on sampled sequences, gather bit-exact on them."""
+    say("workload 4 append -> decode -> gather")
+    w = make_workload(4)
+    dw = DeviceWorkload(w)
+    pk.kv_append(dw.pool, w.layer, dw.k_new, dw.v_new, dw.tables, dw.positions)
+    out = dw.decode()
+    k, v, mask = pk.paged_kv_gather(dw.pool, w.layer, dw.tables, dw.lens, w.max_len)
+    torch.cuda.synchronize()
+    oracle.kv_append(w.pool, w.layer, w.block_tables, w.positions, w.k_new, w.v_new, in_place=True)
+    rng = np.random.default_rng(104)
+    seqs = sorted(set(rng.choice(w.S, size=12, replace=False).tolist())
+                  | {int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))})
+    assert_attention_close(out, _oracle_decode(w, seqs=seqs), w.dtype, rows=seqs, what="w4")
+    rk, rv, rm = oracle.paged_kv_gather(w.pool, w.layer, w.block_tables[seqs], w.context_lens[seqs],
+                                        w.max_len)
+    idx = torch.tensor(seqs, device="cuda")
+    assert dev_to_np(k.index_select(0, idx)).tobytes() == rk.tobytes()
+    assert dev_to_np(v.index_select(0, idx)).tobytes() == rv.tobytes()
+    assert mask.index_select(0, idx).cpu().numpy().tobytes() == rm.tobytes()
+    assert int(mask.sum().item()) == int(w.context_lens.astype(np.int64).sum())
+
+
+# shapes that exercise both pass-1 kernels, tails, empty sequences and poison
+EDGE_CASES = [
+    # dtype, Hq, Hkv, D, BS
+    ("bf16", 8, 2, 128, 16),    # MFMA, G = 4
+    ("bf16", 14, 2, 64, 16),    # MFMA, G = 7
+    ("bf16", 16, 1, 128, 32),   # MFMA, G = 16
+    ("bf16", 4, 4, 128, 64),    # MFMA, G = 1
+    ("bf16", 8, 2, 64, 8),      # generic bf16 (block size 8)
+    ("bf16", 6, 2, 96, 16),     # generic bf16 (head_dim 96)
+    ("f32", 4, 4, 64, 16),      # generic fp32, MHA
+    ("f32", 32, 8, 128, 16),    # generic fp32, G = 4
+]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,BS", EDGE_CASES)
+def test_decode_edge_lengths_with_poison(dtype, Hq, Hkv, D, BS):
+    say(f"decode edges {dtype} Hq={Hq} Hkv={Hkv} D={D} BS={BS}")
+    lens = [0, 1, BS - 1, BS, BS + 1, 15, 16, 17, 63, 64, 65, 1000, 4 * BS + 3, 0]
+    w = poison(custom(dtype, len(lens), Hq, Hkv, D, BS, lens, L=2, layer=1))
+    dw = DeviceWorkload(w)
+    out = dw.decode()
+    ref = _oracle_decode(w)
+    assert_attention_close(out, ref, dtype, what="edges")
+    zero_rows = [i for i, t in enumerate(lens) if t == 0]
+    assert not dev_to_np(out)[zero_rows].any(), "empty sequences must give zero rows"
+
+
+@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("f32", 64, 16)])
+def test_decode_block_permutation_invariance(dtype, D, BS):
+    say(f"decode permutation invariance {dtype}")
+    w = custom(dtype, 9, 8, 2, D, BS, [300, 1, 17, 0, 900, 64, 33, 2048, 5], nb_slack=40)
+    dw = DeviceWorkload(w)
+    a = dw.decode()
+    perm = np.random.default_rng(3).permutation(w.NB)
+    pool2 = np.empty_like(w.pool)
+    pool2[perm] = w.pool
+    w.pool = pool2
+    w.block_tables = np.where(w.block_tables >= 0, perm[np.maximum(w.block_tables, 0)], -1).astype(np.int32)
+    b = DeviceWorkload(w).decode()
+    assert dev_to_np(a).tobytes() == dev_to_np(b).tobytes()
+
+
+def test_decode_scale_zero_is_mean_of_v():
+    say("decode scale 0")
+    w = custom("bf16", 3, 8, 2, 128, 16, [37, 300, 1])
+    w.scale = 0.0
+    dw = DeviceWorkload(w)
+    out = dw.decode()
+    ref = _oracle_decode(w)
+    assert_attention_close(out, ref, "bf16", what="scale0")
+
+
+def test_decode_many_short_sequences():
+    say("decode 5000 short sequences")
+    rng = np.random.default_rng(8)
+    lens = rng.integers(0, 41, size=5000)
+    w = custom("bf16", 5000, 8, 2, 64, 16, lens)
+    dw = DeviceWorkload(w)
+    out = dw.decode()
+    seqs = sorted(rng.choice(5000, size=200, replace=False).tolist())
+    assert_attention_close(out, _oracle_decode(w, seqs=seqs), "bf16", rows=seqs, what="many")
+
+
+def test_decode_rejects_mismatched_dtype():
+    say("decode dtype mismatch")
+    w = custom("bf16", 2, 4, 2, 64, 16, [5, 9])
+    dw = DeviceWorkload(w)
+    with pytest.raises(ValueError):
+        pk.paged_attention_decode(torch.empty(2, 4, 64, device="cuda"), dw.q.float(), dw.pool, 0,
+                                  dw.tables, dw.lens, 0.125)
+
+
+def test_output_dtype_rounding_bf16():
+    """bf16 outputs are the fp32 result rounded to nearest even: the GPU
+    output must be one of the two bf16 neighbours of the fp64 oracle value
+    (the fp32 accumulation error is far below the bf16 spacing here)."""
+    say("decode bf16 rounding")
+    w = custom("bf16", 2, 4, 4, 64, 16, [1, 1])
+    dw = DeviceWorkload(w)
+    out = dev_to_np(dw.decode())
+    # T = 1: the output is exactly the single V row (weight 1), so bits match
+    for b in range(2):
+        K, V = oracle.gather_sequence(w.pool, 0, w.block_tables[b], 1)
+        assert out[b].tobytes() == np.ascontiguousarray(V[0]).tobytes()
