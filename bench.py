@@ -60,8 +60,10 @@ def gather_bytes(w, max_len: int) -> int:
     return read + write
 
 
-def cpu_baseline(w, budget_tokens: int):
-    """The oracle, as it stands, on a bounded sample of the same batch."""
+def cpu_baseline(w, budget_tokens: int, min_seconds: float = 10.0):
+    """The oracle, as it stands, on a bounded sample of the same batch: whole
+    sequences in a seeded order until `budget_tokens` cached tokens, run
+    repeatedly until `min_seconds` of CPU work; the median run is reported."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -75,22 +77,26 @@ def cpu_baseline(w, budget_tokens: int):
         toks += int(w.context_lens[b])
         if toks >= budget_tokens:
             break
-    t0 = time.perf_counter()
-    oracle.paged_attention_decode(w.pool, w.dtype, w.layer, w.block_tables, w.context_lens, w.q,
-                                  w.scale, seqs=seqs)
-    dt = time.perf_counter() - t0
+    runs = []
+    while sum(runs) < min_seconds and len(runs) < 5:
+        t0 = time.perf_counter()
+        oracle.paged_attention_decode(w.pool, w.dtype, w.layer, w.block_tables, w.context_lens,
+                                      w.q, w.scale, seqs=seqs)
+        runs.append(time.perf_counter() - t0)
+    dt = float(np.median(runs))
     e = 4 if w.dtype == "f32" else 2
     sample_bytes = sum(2 * int(w.context_lens[b]) * w.Hkv * w.D * e for b in seqs) + \
         len(seqs) * w.Hq * w.D * 2 * e
     return {
-        "value": sample_bytes / dt / 1e9,
+        "value": round(sample_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": int(blas_threads),
         "kind": "oracle",
-        "sample": f"{len(seqs)} of {w.S} sequences ({toks} cached tokens), fp64 numpy, "
-                  f"{dt:.1f} s wall; tokens/s {len(seqs) / dt:.3g}",
-        "tokens_per_s": len(seqs) / dt,
-        "seconds": dt,
+        "sample": f"{len(seqs)} of {w.S} sequences ({toks} cached tokens) of the same batch, "
+                  f"fp64 numpy gather-then-attend, median of {len(runs)} runs "
+                  f"({sum(runs):.1f} s of CPU work)",
+        "tokens_per_s": round(len(seqs) / dt, 3),
+        "seconds_per_run": round(dt, 3),
     }
 
 
@@ -104,6 +110,8 @@ def main(argv=None) -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gather", action="store_true")
     ap.add_argument("--cpu-budget-tokens", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -240,8 +248,18 @@ def main(argv=None) -> int:
         except torch.cuda.OutOfMemoryError:
             result["gather"] = None
 
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = n
+        del src, dst
+
     if not args.no_cpu_baseline:
-        budget = args.cpu_budget_tokens or 60000
+        budget = args.cpu_budget_tokens or 600000
         result["cpu_baseline"] = cpu_baseline(w0, budget)
 
     print(json.dumps(result), flush=True)

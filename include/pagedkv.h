@@ -152,11 +152,13 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  *                  h / (num_q_heads / kv_heads).
  *   scale        : multiplies q.k before the softmax.
  *   workspace    : device, >= paged_attention_workspace_bytes(...) bytes,
- *                  256-byte aligned; contents need no initialisation.
+ *                  256-byte aligned; contents need no initialisation.  Calls
+ *                  that share a workspace must not overlap.
  * out[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) V_t over t < T_b,
  * computed with fp32 accumulation; bf16 outputs are rounded to nearest
- * even.  T_b = 0 gives a zero row.  Long contexts are split across many
- * wavefronts; a second pass merges the partial results. */
+ * even.  T_b = 0 gives a zero row.  Work is split evenly over all
+ * wavefronts the GPU holds at once; a sequence split across wavefronts is
+ * merged by a second kernel on the same stream (log-sum-exp weights). */
 int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
                            int layer, const int32_t* block_tables,
                            int max_blocks_per_seq, const int32_t* context_lens,

@@ -27,16 +27,19 @@ SOURCES = [
     "copy_kernels.hip",
     "decode_mfma.hip",
     "decode_generic.hip",
-    "decode_reduce.hip",
+    "decode_merge.hip",
 ]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 
-# Packed fp32 VALU instructions are kept out of the generated code.
+# Packed fp32 VALU instructions are kept out of the generated code.  MFMA
+# results are kept in VGPRs (the decode kernel rescales its accumulator with
+# VALU ops every chunk; AGPR accumulators would need copies both ways).
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function",
 ]
 

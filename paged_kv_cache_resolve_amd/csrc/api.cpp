@@ -198,8 +198,7 @@ int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool, int 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = use_mfma ? launch_decode_mfma(p, s) : launch_decode_generic(p, s);
   if (e != hipSuccess) return PAGEDKV_ERR_HIP;
-  e = launch_decode_reduce(p, use_mfma ? kMfmaChunk : kGenericChunk, s);
-  return hip_status(e);
+  return hip_status(launch_decode_merge(p, s));
 }
 
 int paged_kv_resolve(int64_t* slots, const int32_t* block_tables, int max_blocks_per_seq,

@@ -4,8 +4,8 @@
 //
 // Same computation as the MFMA kernel ("vllmini", section "The CUDA Block
 // Kernel": per (sequence, head), resolve logical positions through the block
-// table and attend over the physical pages) and the same work split
-// (decode_split.h), with 64-token chunks and one wavefront per workgroup:
+// table and attend over the physical pages) and the same head-group work
+// split (internal.h), with 64-token chunks and one wavefront per workgroup:
 //   * scores: lane t owns token t of the chunk, resolves its own block-table
 //     entry, and forms the G dot products against q (held in LDS, already
 //     multiplied by scale*log2(e));
@@ -55,7 +55,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 
 template <typename TS>
 __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int lane,
-                                int64_t wave, int b, int g, int j0, int j1, int nb) {
+                                int64_t unit, int b, int g, int j0, int j1, int nb) {
   const int G = p.group;
   const int D = p.pool.head_dim;
   const int BS = p.pool.block_size;
@@ -138,9 +138,8 @@ __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int
     __syncthreads();
   }
 
-  const int pair = b * p.pool.kv_heads + g;
   const bool whole = (j0 == 0 && j1 == nb);
-  const int64_t slot = pair + wave;
+  const int64_t slot = partial_slot(b, g, unit, p.pool.kv_heads);
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h >= G) continue;
@@ -182,27 +181,25 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeParams p) {
     for (int i = threadIdx.x; i <= p.batch; i += 64) p.ws_prefix[i] = prefix[i];
 
   const int lane = threadIdx.x;
-  const int64_t wave = blockIdx.x;
   const int H = p.pool.kv_heads;
-  const int64_t C = (int64_t)H * prefix[p.batch];
-  const int64_t We = waves_eff(C, p.waves, p.min_chunks);
-  if (wave >= We) return;
-  int64_t c = wave_begin(wave, C, We);
-  const int64_t c_end = wave_begin(wave + 1, C, We);
-  int b = seq_of_chunk(prefix, p.batch, c, H);
+  const int64_t unit = blockIdx.x / H;
+  const int g = (int)(blockIdx.x - unit * H);
+  const int64_t C = prefix[p.batch];
+  const int64_t Ue = waves_eff(C, p.units, p.min_chunks);
+  if (unit >= Ue) return;
+  int64_t c = wave_begin(unit, C, Ue);
+  const int64_t c_end = wave_begin(unit + 1, C, Ue);
+  int b = seq_of_chunk(prefix, p.batch, c);
   while (c < c_end) {
     const int pb = prefix[b];
     const int nb = prefix[b + 1] - pb;
-    const int64_t base = (int64_t)H * pb;
-    const int rel = (int)(c - base);
-    const int g = rel / nb;
-    const int j0 = rel - g * nb;
+    const int j0 = (int)(c - pb);
     const int64_t left = c_end - c;
     const int j1 = left < (int64_t)(nb - j0) ? j0 + (int)left : nb;
-    generic_segment<TS>(p, qs, ps, lane, wave, b, g, j0, j1, nb);
+    generic_segment<TS>(p, qs, ps, lane, unit, b, g, j0, j1, nb);
     __syncthreads();
     c += j1 - j0;
-    if (c >= base + (int64_t)H * nb) {
+    if (j1 == nb) {
       ++b;
       while (b < p.batch && prefix[b + 1] == prefix[b]) ++b;
     }
@@ -228,7 +225,11 @@ hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   int waves = wgs;
   if (waves > kMaxWaves) waves = kMaxWaves;
-  p.waves = waves;
+  p.units = waves / p.pool.kv_heads;   // head groups
+  if (p.units < 1) {
+    p.units = 1;
+    waves = p.pool.kv_heads;
+  }
   if (p.min_chunks < 1) p.min_chunks = 2;
   if (f32)
     hipLaunchKernelGGL(decode_generic_kernel<float>, dim3(waves), dim3(64), lds, s, p);

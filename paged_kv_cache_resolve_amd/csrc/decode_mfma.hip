@@ -1,4 +1,4 @@
-// Paged-attention decode, pass 1, bf16 pools, MFMA tiles on gfx950.
+// Paged-attention decode for bf16 pools: MFMA tiles on gfx950, one kernel.
 //
 // What is computed ("vllmini: Building a Minimalist PagedAttention and KV
 // Cache Engine", section "The CUDA Block Kernel"; "KV Cache and Attention
@@ -7,24 +7,32 @@
 // physical blocks of the pool, and scaled q.K scores, a max-subtracted
 // softmax and the weighted sum of V rows are formed.
 //
-// Mapping onto CDNA4.  One wavefront streams a contiguous range of 16-token
-// chunks of one or more (sequence, KV head) pairs (decode_split.h).  All G
-// query heads of the KV head are computed from the same K/V bytes, so each
-// K/V byte is read from HBM once.  Per chunk:
-//   * K tile [16 tokens x D] is loaded straight into the A-operand layout of
-//     v_mfma_f32_16x16x32_bf16 (row = token = lane % 16, eight consecutive
-//     dims per lane); Q^T (16 head columns, G used, rest zero) is the B
-//     operand.  The result holds score(token 4*(lane/16)+r, head lane%16).
-//   * Online softmax over those scores in fp32 (exp2 domain), with a
-//     wave-uniform rescale only when some head's running max grows.
-//   * The probabilities, rounded to bf16, are already in the B-operand
-//     layout of v_mfma_f32_16x16x16_bf16 (k = token); V is loaded with
-//     fully coalesced 16-byte rows (lane = token 4*(lane/16)+r, dims
-//     VD*(lane%16)..) and transposed to the A operand with v_perm_b32.
-//     The accumulator holds out^T: lane = head lane%16, 4*VD contiguous dims.
-// The partition's block-table entries are prefetched into a VGPR (one entry
-// per lane, the next window loaded one window ahead) and read back with
-// v_readlane, so chunk addresses come from scalar registers.
+// Mapping onto CDNA4.
+//  * Work split (internal.h, decode_split.h): the kv_heads wavefronts of a
+//    head group take the same contiguous, equal-sized range of 16-token
+//    chunks of the sequences laid end to end, one KV head each, and stream
+//    through it without stopping at sequence boundaries.  All G query heads
+//    of a KV head are computed from the same K/V bytes, so each byte is read
+//    from HBM once, and the group reads each block's heads side by side.
+//  * Per chunk:
+//      - the K tile [16 tokens x D] is loaded straight into the A-operand
+//        layout of v_mfma_f32_16x16x32_bf16 (row = token = lane % 16, eight
+//        consecutive dims per lane) and multiplied by Q^T (16 head columns, G
+//        used, the rest zero), giving score(token 4*(lane/16)+r, head lane%16);
+//      - online softmax in fp32 in the exp2 domain (the accumulator is
+//        rescaled branch-free; the factor is 1 unless a running max grew);
+//      - the probabilities, rounded to bf16, already sit in the B-operand
+//        layout of v_mfma_f32_16x16x16_bf16 (k = token); V rows are loaded
+//        fully coalesced (lane = token 4*(lane/16)+r, dims VD*(lane%16)..)
+//        and transposed to the A operand with v_perm_b32.  The accumulator
+//        holds out^T: lane = head lane%16, 4*VD contiguous dims;
+//      - the next chunk's K and V (and, at a pair boundary, the next pair's
+//        q) are in flight while this chunk is computed; the block-table entry
+//        of the chunk after that is already being fetched by a scalar load.
+//  * When a pair ends inside the wavefront's range the normalised output is
+//    written directly; a pair cut by a range edge leaves a partial (running
+//    max, sum, unnormalised output) in the workspace, and the merge kernel
+//    (decode_merge.hip) combines the partials of every such pair.
 
 #include <math.h>
 
@@ -38,20 +46,25 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+constexpr int kWaves = 4;           // independent wavefronts per workgroup
+constexpr int kThreads = 64 * kWaves;
+
 template <int D> struct VRow;
 template <> struct VRow<128> { using type = uint4; };   // 8 bf16 per lane
 template <> struct VRow<64> { using type = uint2; };    // 4 bf16 per lane
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) {
-  return __builtin_bit_cast(bf16x8_t, v);
-}
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Block tables are read-only while a decode runs; reading them through the
+// constant address space lets uniform indices become scalar loads.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
-__device__ __forceinline__ uint32_t dword_of(const uint2& v, int i) {
-  return i == 0 ? v.x : v.y;
-}
+__device__ __forceinline__ uint32_t dword_of(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
 
 // Round two floats to bf16 (nearest even) and pack: lo = a, hi = b.
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
@@ -61,145 +74,158 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   v[1] = (__bf16)b;
   return __builtin_bit_cast(uint32_t, v);
 }
+__device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
 
+// Combine a value with the lane 16 (resp. 32) apart, on the VALU.
+__device__ __forceinline__ float max_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 template <int D>
 struct ChunkBuf {
-  uint4 k[D / 32];
+  bf16x8_t k[D / 32];
   typename VRow<D>::type v[4];
 };
 
-template <int D>
-__device__ __forceinline__ void zero_row(typename VRow<D>::type& v);
+template <int D> __device__ __forceinline__ void zero_row(typename VRow<D>::type& v);
 template <> __device__ __forceinline__ void zero_row<128>(uint4& v) { v = make_uint4(0, 0, 0, 0); }
 template <> __device__ __forceinline__ void zero_row<64>(uint2& v) { v = make_uint2(0, 0); }
 
-template <int D>
-__device__ __forceinline__ void store_out_row(uint16_t* dst, const float* vals);
-// 32 bf16 = 4 x 16-byte stores.
-template <>
-__device__ __forceinline__ void store_out_row<128>(uint16_t* dst, const float* v) {
-  uint4* d = reinterpret_cast<uint4*>(dst);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    d[i] = make_uint4(pack_bf16x2(v[8 * i + 0], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
-                      pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
-}
-// 16 bf16 = 2 x 16-byte stores.
-template <>
-__device__ __forceinline__ void store_out_row<64>(uint16_t* dst, const float* v) {
-  uint4* d = reinterpret_cast<uint4*>(dst);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-    d[i] = make_uint4(pack_bf16x2(v[8 * i + 0], v[8 * i + 1]), pack_bf16x2(v[8 * i + 2], v[8 * i + 3]),
-                      pack_bf16x2(v[8 * i + 4], v[8 * i + 5]), pack_bf16x2(v[8 * i + 6], v[8 * i + 7]));
-}
+// Position in the chunk space of one KV head: chunk j of sequence b, which
+// has nb chunks and T tokens.  All fields are wave-uniform.
+struct Cursor {
+  int b, j, nb, T;
+
+  // Step to the next chunk.  The caller guarantees one exists.
+  __device__ __forceinline__ void advance(const int32_t* prefix, const_i32_ptr lens, int batch) {
+    if (++j < nb) return;
+    j = 0;
+    do { ++b; } while (b < batch - 1 && prefix[b + 1] == prefix[b]);
+    b = uni(b);
+    nb = uni(prefix[b + 1] - prefix[b]);
+    T = uni(lens[b]);
+  }
+};
 
 template <int D>
-struct Segment {
-  static constexpr int NK = D / 32;   // K loads (16 B) per lane per chunk
+struct Stream {
+  static constexpr int NK = D / 32;   // 16-byte K loads per lane per chunk
   static constexpr int VD = D / 16;   // V dims per lane
   static constexpr int NW = VD / 2;   // dwords per lane per V row
 
   const DecodeParams& p;
   const int lane, n, quad;
-  const int b, g, j0, j1, T;
-  const char* khead;        // K slab of (layer, g) in block 0, in bytes
-  const int32_t* trow;
-  int tb0;                  // first logical block held in `tbl`
-  int tbl, tbl_next;        // block-table window (one entry per lane)
-  int last_blk;
+  const int g;              // KV head served by this wavefront
+  const int64_t unit;       // head group (chunk range) of this wavefront
 
   bf16x8_t qop[NK];
   f32x4_t acc[VD];
   float m, l;
 
-  __device__ Segment(const DecodeParams& p_, int lane_, int b_, int g_, int j0_, int j1_)
-      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), b(b_), g(g_), j0(j0_), j1(j1_),
-        T(p_.context_lens[b_]) {
-    const int BS = p.pool.block_size;
-    khead = p.pool.base + 2 * ((int64_t)p.layer * p.pool.layer_stride + (int64_t)g * p.pool.head_stride);
-    trow = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-    tb0 = (j0 * 16) / BS;
-    last_blk = (j1 * 16 - 1) / BS;
-    tbl = tb0 + lane <= last_blk ? trow[tb0 + lane] : 0;
-    tbl_next = tb0 + 64 + lane <= last_blk ? trow[tb0 + 64 + lane] : 0;
+  __device__ Stream(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
+      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), unit(unit_) {}
 
-    const int G = p.group;
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           ((int64_t)b * p.num_q_heads + (int64_t)g * G + n) * D + 8 * quad;
-#pragma unroll
-    for (int j = 0; j < NK; ++j) {
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (n < G) v = *reinterpret_cast<const uint4*>(qrow + 32 * j);
-      qop[j] = as_bf16x8(v);
-    }
+  __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int c = 0; c < VD; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     m = -INFINITY;
     l = 0.f;
   }
 
-  // Byte address of the K slab rows of chunk j (tokens 16j .. 16j+15).
-  __device__ __forceinline__ const char* chunk_base(int j) {
-    const int BS = p.pool.block_size;
-    const int blk = (j * 16) / BS;
-    if (blk - tb0 >= 64) {           // uniform: slide the table window
-      tb0 += 64;
-      tbl = tbl_next;
-      tbl_next = tb0 + 64 + lane <= last_blk ? trow[tb0 + 64 + lane] : 0;
-    }
-    const int phys = __builtin_amdgcn_readlane(tbl, blk - tb0);
-    return khead + 2 * ((int64_t)phys * p.pool.block_stride + (int64_t)((j * 16) % BS) * D);
+  // q of the pair's G heads in the B-operand layout.  MFMA columns n >= G
+  // carry a copy of head G-1: every column goes through its own softmax and
+  // accumulator and only columns n < G are ever written, so the copies cost
+  // nothing and need neither a branch nor masking.
+  __device__ __forceinline__ void load_q(const Cursor& c) {
+    const int G = p.group;
+    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
+                           ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + min(n, G - 1)) * D +
+                           8 * quad;
+#pragma unroll
+    for (int i = 0; i < NK; ++i) qop[i] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * i);
   }
 
-  __device__ __forceinline__ void load(ChunkBuf<D>& cb, int j) {
-    const char* kb = chunk_base(j);
-    const char* vb = kb + 2 * p.pool.kv_stride;
-    const char* kl = kb + 2 * (n * D + 8 * quad);
+  // Physical block of chunk c: a scalar load of the block-table entry.
+  __device__ __forceinline__ int phys_of(const Cursor& c) const {
+    const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
+    return uni(trow[(c.j * 16) / p.pool.block_size]);
+  }
+
+  // Byte address of the K rows of chunk c stored in physical block `phys`.
+  __device__ __forceinline__ const char* chunk_base(const Cursor& c, int phys) const {
+    return p.pool.base + 2 * ((int64_t)p.layer * p.pool.layer_stride +
+                              (int64_t)g * p.pool.head_stride +
+                              (int64_t)phys * p.pool.block_stride +
+                              (int64_t)((c.j * 16) % p.pool.block_size) * D);
+  }
+
+  __device__ __forceinline__ void issue_k(ChunkBuf<D>& cb, const char* kb) const {
+    const char* kl = kb + (uint32_t)(2 * (n * D + 8 * quad));
 #pragma unroll
-    for (int i = 0; i < NK; ++i) cb.k[i] = *reinterpret_cast<const uint4*>(kl + 64 * i);
-    const char* vl = vb + 2 * (4 * quad * D + VD * n);
+    for (int i = 0; i < NK; ++i) cb.k[i] = *reinterpret_cast<const bf16x8_t*>(kl + 64 * i);
+  }
+  __device__ __forceinline__ void issue_v(ChunkBuf<D>& cb, const char* kb) const {
+    const char* vl = kb + 2 * p.pool.kv_stride + (uint32_t)(2 * (4 * quad * D + VD * n));
 #pragma unroll
     for (int r = 0; r < 4; ++r)
       cb.v[r] = *reinterpret_cast<const typename VRow<D>::type*>(vl + 2 * r * D);
   }
 
-  __device__ __forceinline__ void compute(ChunkBuf<D>& cb, int j) {
+  __device__ __forceinline__ f32x4_t qk(const ChunkBuf<D>& cb) const {
     f32x4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < NK; ++i)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cb.k[i]), qop[i], s, 0, 0, 0);
+      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb.k[i], qop[i], s, 0, 0, 0);
+    return s;
+  }
 
-    const int tok0 = j * 16 + 4 * quad;
-    const bool tail = j * 16 + 16 > T;   // uniform
+  // Scores -> bf16 probabilities in the B-operand layout, then the weighted
+  // V sum; updates m, l, acc.  TAIL masks tokens at or past T (only the last
+  // chunk of a pair can hold them); masked V rows are zeroed, not weighted
+  // by zero, so unused pool slots never reach the sum.
+  template <bool TAIL>
+  __device__ __forceinline__ void attend(f32x4_t s, ChunkBuf<D>& cb, const Cursor& c) {
+    const int tok0 = c.j * 16 + 4 * quad;
     float sv[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       sv[r] = s[r] * p.scale_log2;
-      if (tail && tok0 + r >= T) sv[r] = -INFINITY;
+      if (TAIL && tok0 + r >= c.T) sv[r] = -INFINITY;
     }
     float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 16));
-    bmax = fmaxf(bmax, __shfl_xor(bmax, 32));
-    if (__any(bmax > m)) {
+    bmax = max_x32(max_x16(bmax));
+    {
+      // branch-free rescale (alpha = 1 when no running max grows)
       const float mn = fmaxf(m, bmax);
-      const float alpha = exp2f(m - mn);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
-      for (int c = 0; c < VD; ++c) acc[c] *= alpha;
+      for (int i = 0; i < VD; ++i) acc[i] *= alpha;
       l *= alpha;
       m = mn;
     }
-    const uint32_t p01 = pack_bf16x2(exp2f(sv[0] - m), exp2f(sv[1] - m));
-    const uint32_t p23 = pack_bf16x2(exp2f(sv[2] - m), exp2f(sv[3] - m));
+    const uint32_t p01 = pack_bf16x2(__builtin_amdgcn_exp2f(sv[0] - m), __builtin_amdgcn_exp2f(sv[1] - m));
+    const uint32_t p23 = pack_bf16x2(__builtin_amdgcn_exp2f(sv[2] - m), __builtin_amdgcn_exp2f(sv[3] - m));
     l += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
     const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
-
-    if (tail) {
+    if (TAIL) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (tok0 + r >= T) zero_row<D>(cb.v[r]);
+        if (tok0 + r >= c.T) zero_row<D>(cb.v[r]);
     }
 #pragma unroll
     for (int w = 0; w < NW; ++w) {
@@ -209,50 +235,59 @@ struct Segment {
                                   __builtin_amdgcn_perm(v3, v2, 0x05040100u));
       const uint2 od = make_uint2(__builtin_amdgcn_perm(v1, v0, 0x07060302u),
                                   __builtin_amdgcn_perm(v3, v2, 0x07060302u));
-      acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          __builtin_bit_cast(s16x4_t, ev), pop, acc[2 * w], 0, 0, 0);
-      acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-          __builtin_bit_cast(s16x4_t, od), pop, acc[2 * w + 1], 0, 0, 0);
+      acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, ev), pop,
+                                                             acc[2 * w], 0, 0, 0);
+      acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, od), pop,
+                                                                 acc[2 * w + 1], 0, 0, 0);
     }
   }
 
-  __device__ void run() {
-    ChunkBuf<D> c0, c1;
-    load(c0, j0);
-    for (int j = j0; j < j1; j += 2) {
-      if (j + 1 < j1) load(c1, j + 1);
-      compute(c0, j);
-      if (j + 1 >= j1) break;
-      if (j + 2 < j1) load(c0, j + 2);
-      compute(c1, j + 1);
-    }
+  __device__ __forceinline__ void attend_chunk(f32x4_t s, ChunkBuf<D>& cb, const Cursor& c) {
+    if (c.j == c.nb - 1 && (c.T & 15) != 0)
+      attend<true>(s, cb, c);
+    else
+      attend<false>(s, cb, c);
   }
 
-  __device__ void finish(int nb, int64_t wave) {
+  // End of this wavefront's part of sequence c.b: normalised output if it
+  // saw the whole sequence, else a partial in its (sequence, head, unit) slot.
+  __device__ void flush(const Cursor& c, bool whole) {
     const int G = p.group;
-    float lt = l + __shfl_xor(l, 16);
-    lt += __shfl_xor(lt, 32);
+    const float lt = sum_x32(sum_x16(l));
     if (n >= G) return;
-    // lane holds dims 4*VD*quad + VD*r + c of head n as acc[c][r]
-    float vals[4 * VD];
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < VD; ++c) vals[VD * r + c] = acc[c][r];
-    const int pair = b * p.pool.kv_heads + g;
-    if (j0 == 0 && j1 == nb) {
+    // lane holds dims 4*VD*quad + VD*r + i of head n as acc[i][r]
+    if (whole) {
       const float inv = 1.0f / lt;
-#pragma unroll
-      for (int i = 0; i < 4 * VD; ++i) vals[i] *= inv;
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
-                      ((int64_t)b * p.num_q_heads + (int64_t)g * G + n) * D + 4 * VD * quad;
-      store_out_row<D>(dst, vals);
+                      ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + n) * D + 4 * VD * quad;
+      uint4* d4 = reinterpret_cast<uint4*>(dst);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int h = 0; h < VD / 8; ++h) {
+          const int i0 = 8 * h;
+          d4[r * (VD / 8) + h] = make_uint4(
+              pack_bf16x2(acc[i0 + 0][r] * inv, acc[i0 + 1][r] * inv),
+              pack_bf16x2(acc[i0 + 2][r] * inv, acc[i0 + 3][r] * inv),
+              pack_bf16x2(acc[i0 + 4][r] * inv, acc[i0 + 5][r] * inv),
+              pack_bf16x2(acc[i0 + 6][r] * inv, acc[i0 + 7][r] * inv));
+        }
+      if (VD == 4) {   // head_dim 64: 4 values per row r, 2 rows per 16-byte store
+        uint2* d2 = reinterpret_cast<uint2*>(dst);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          d2[r] = make_uint2(pack_bf16x2(acc[0][r] * inv, acc[1][r] * inv),
+                             pack_bf16x2(acc[2][r] * inv, acc[3][r] * inv));
+      }
     } else {
-      const int64_t slot = pair + wave;
+      const int64_t slot = partial_slot(c.b, g, unit, p.pool.kv_heads);
       float4* o = reinterpret_cast<float4*>(p.ws_o + (slot * G + n) * D + 4 * VD * quad);
 #pragma unroll
-      for (int i = 0; i < VD; ++i)
-        o[i] = make_float4(vals[4 * i], vals[4 * i + 1], vals[4 * i + 2], vals[4 * i + 3]);
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int h = 0; h < VD / 4; ++h)
+          o[r * (VD / 4) + h] = make_float4(acc[4 * h][r], acc[4 * h + 1][r], acc[4 * h + 2][r],
+                                            acc[4 * h + 3][r]);
       if (quad == 0) {
         p.ws_ml[(slot * G + n) * 2 + 0] = m;
         p.ws_ml[(slot * G + n) * 2 + 1] = lt;
@@ -262,42 +297,78 @@ struct Segment {
 };
 
 template <int D>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ int32_t prefix[];
-  __shared__ int32_t scan[256];
-  block_chunk_prefix<256>(p.context_lens, p.batch, kMfmaChunk, prefix, scan);
+  __shared__ int32_t scan[kThreads];
+  const int H = p.pool.kv_heads;
+
+  block_chunk_prefix<kThreads>(p.context_lens, p.batch, kMfmaChunk, prefix, scan);
   if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= p.batch; i += 256) p.ws_prefix[i] = prefix[i];
+    for (int i = threadIdx.x; i <= p.batch; i += kThreads) p.ws_prefix[i] = prefix[i];
 
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int H = p.pool.kv_heads;
-  const int64_t C = (int64_t)H * prefix[p.batch];
-  const int64_t We = waves_eff(C, p.waves, p.min_chunks);
-  if (wave >= We) return;
-  int64_t c = wave_begin(wave, C, We);
-  const int64_t c_end = wave_begin(wave + 1, C, We);
-  int b = seq_of_chunk(prefix, p.batch, c, H);
-  while (c < c_end) {
-    const int pb = prefix[b];
-    const int nb = prefix[b + 1] - pb;
-    const int64_t base = (int64_t)H * pb;
-    const int rel = (int)(c - base);
-    const int g = rel / nb;
-    const int j0 = rel - g * nb;
-    const int64_t left = c_end - c;
-    const int j1 = left < (int64_t)(nb - j0) ? j0 + (int)left : nb;
-    {
-      Segment<D> seg(p, lane, b, g, j0, j1);
-      seg.run();
-      seg.finish(nb, wave);
-    }
-    c += j1 - j0;
-    if (c >= base + (int64_t)H * nb) {
-      ++b;
-      while (b < p.batch && prefix[b + 1] == prefix[b]) ++b;
-    }
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + uni(threadIdx.x >> 6);
+  const int64_t unit = wave / H;
+  const int g = (int)(wave - unit * H);
+  const int64_t C = uni(prefix[p.batch]);
+  const int64_t Ue = waves_eff(C, p.units, p.min_chunks);
+  if (unit >= Ue) return;
+  const int64_t c0 = wave_begin(unit, C, Ue);
+  const int rem = (int)(wave_begin(unit + 1, C, Ue) - c0);   // >= 1
+
+  const const_i32_ptr lens = (const_i32_ptr)p.context_lens;
+  Cursor cur;
+  cur.b = uni(seq_of_chunk(prefix, p.batch, c0));
+  cur.nb = uni(prefix[cur.b + 1] - prefix[cur.b]);
+  cur.j = uni((int)(c0 - prefix[cur.b]));
+  cur.T = uni(lens[cur.b]);
+
+  Stream<D> st(p, lane, g, unit);
+  st.reset();
+  st.load_q(cur);
+  ChunkBuf<D> cb;
+  const char* kb = st.chunk_base(cur, st.phys_of(cur));
+  st.issue_k(cb, kb);
+  st.issue_v(cb, kb);
+  Cursor nx = cur;
+  int phys_nx = 0;
+  if (rem > 1) {
+    nx.advance(prefix, lens, p.batch);
+    phys_nx = st.phys_of(nx);
   }
+  bool whole_start = cur.j == 0;   // this wave has seen the current sequence from chunk 0
+
+  for (int i = 0; i + 1 < rem; ++i) {
+    const f32x4_t s = st.qk(cb);
+    __builtin_amdgcn_sched_barrier(0);
+    kb = st.chunk_base(nx, phys_nx);
+    st.issue_k(cb, kb);
+    // q is dead until the next chunk's QK, so a new sequence's q loads in place
+    const bool sw = nx.b != cur.b;
+    if (sw) st.load_q(nx);
+    __builtin_amdgcn_sched_barrier(0);
+    Cursor n2 = nx;
+    int phys_n2 = 0;
+    if (i + 2 < rem) {
+      n2.advance(prefix, lens, p.batch);
+      phys_n2 = st.phys_of(n2);
+    }
+    st.attend_chunk(s, cb, cur);
+    __builtin_amdgcn_sched_barrier(0);
+    st.issue_v(cb, kb);
+    __builtin_amdgcn_sched_barrier(0);
+    if (sw) {
+      st.flush(cur, whole_start);
+      st.reset();
+      whole_start = true;
+    }
+    cur = nx;
+    nx = n2;
+    phys_nx = phys_n2;
+  }
+  const f32x4_t s = st.qk(cb);
+  st.attend_chunk(s, cb, cur);
+  st.flush(cur, whole_start && cur.j == cur.nb - 1);
 }
 
 }  // namespace
@@ -308,21 +379,23 @@ bool mfma_supported(const kv_pool* pool, int group) {
 }
 
 hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
-  const size_t lds = sizeof(int32_t) * (p.batch + 1);
+  const size_t lds = sizeof(int32_t) * (size_t)(p.batch + 1);
   const void* fn = p.pool.head_dim == 128 ? reinterpret_cast<const void*>(&decode_mfma_kernel<128>)
                                           : reinterpret_cast<const void*>(&decode_mfma_kernel<64>);
   int wgs = 0;
-  hipError_t e = resident_workgroups(fn, 256, lds, &wgs);
+  hipError_t e = resident_workgroups(fn, kThreads, lds, &wgs);
   if (e != hipSuccess) return e;
-  int waves = wgs * 4;
-  if (waves > kMaxWaves) waves = kMaxWaves;
-  p.waves = waves;
+  if (wgs > kMaxWaves / kWaves) wgs = kMaxWaves / kWaves;
+  p.units = wgs * kWaves / p.pool.kv_heads;   // head groups
+  if (p.units < 1) {                          // more KV heads than resident waves
+    p.units = 1;
+    wgs = (p.pool.kv_heads + kWaves - 1) / kWaves;
+  }
   if (p.min_chunks < 1) p.min_chunks = 4;
-  const dim3 grid((waves + 3) / 4), block(256);
   if (p.pool.head_dim == 128)
-    hipLaunchKernelGGL(decode_mfma_kernel<128>, grid, block, lds, s, p);
+    hipLaunchKernelGGL(decode_mfma_kernel<128>, dim3(wgs), dim3(kThreads), lds, s, p);
   else
-    hipLaunchKernelGGL(decode_mfma_kernel<64>, grid, block, lds, s, p);
+    hipLaunchKernelGGL(decode_mfma_kernel<64>, dim3(wgs), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 

@@ -61,16 +61,22 @@ __device__ __forceinline__ int64_t wave_of_chunk(int64_t c, int64_t C, int64_t W
   return ((c + 1) * We - 1) / C;
 }
 
-// Largest b in [0, batch) with kv_heads * prefix[b] <= c and a non-empty
-// chunk range (prefix[b + 1] > prefix[b]).  Requires c < kv_heads * prefix[batch].
-__device__ __forceinline__ int seq_of_chunk(const int32_t* prefix, int batch,
-                                            int64_t c, int kv_heads) {
+// Largest b in [0, batch) with prefix[b] <= c, which is the sequence that
+// holds chunk c (an empty sequence has prefix[b + 1] == prefix[b] and is
+// skipped).  Requires c < prefix[batch].
+__device__ __forceinline__ int seq_of_chunk(const int32_t* prefix, int batch, int64_t c) {
   int lo = 0, hi = batch;   // invariant: answer in [lo, hi)
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
-    if ((int64_t)kv_heads * prefix[mid] <= c) lo = mid; else hi = mid;
+    if (prefix[mid] <= c) lo = mid; else hi = mid;
   }
   return lo;
+}
+
+// Partial slot of (sequence b, KV head g) written by unit u.  For a fixed g
+// both b and u increase along the chunk space, so b + u is unique per g.
+__device__ __forceinline__ int64_t partial_slot(int b, int g, int64_t u, int kv_heads) {
+  return ((int64_t)b + u) * kv_heads + g;
 }
 
 }  // namespace pagedkv

@@ -56,15 +56,18 @@ inline int elem_size(pagedkv_dtype_t t) { return t == PAGEDKV_F32 ? 4 : 2; }
 // ---------------------------------------------------------------------------
 // Decode work split.
 //
-// A "chunk" is CT consecutive tokens of one (sequence b, KV head g) pair.
-// Pair p = b * kv_heads + g has n_b = ceil(T_b / CT) chunks; pairs are laid
-// end to end in p order, so the chunk space has C = kv_heads * sum_b n_b
-// entries.  W_eff wavefronts each take one contiguous, equal-sized range of
-// that space ([w*C/W_eff, (w+1)*C/W_eff)); a wavefront that covers a whole
-// pair writes the output directly, otherwise it leaves a partial
-// (max, sum, unnormalised output) in slot p + w of the workspace, which is
-// unique because wave ranges and pairs are both ordered.  The second pass
-// merges the partials of every split pair.
+// A "chunk" is CT consecutive tokens of one sequence; sequence b has
+// n_b = ceil(T_b / CT) chunks, and the sequences' chunks laid end to end form
+// a chunk space of C = sum_b n_b entries.  Wavefronts come in head groups:
+// wavefront w serves KV head w % kv_heads for unit w / kv_heads, and unit u
+// takes the contiguous, equal-sized range [u*C/U_eff, (u+1)*C/U_eff) of the
+// chunk space.  The kv_heads wavefronts of a unit therefore stream the same
+// blocks at the same time, and since the pool stores the heads of a block
+// side by side, HBM sees long contiguous runs.  A wavefront that sees a
+// whole (sequence, head) pair writes the output directly; otherwise it
+// leaves a partial (max, sum, unnormalised output) in the workspace slot
+// (b + u) * kv_heads + g, and the merge kernel combines the partials of
+// every pair that was split between units.
 // ---------------------------------------------------------------------------
 struct DecodeParams {
   PoolGeom pool;
@@ -81,12 +84,13 @@ struct DecodeParams {
   int num_q_heads;
   int group;              // G = num_q_heads / kv_heads
   float scale_log2;       // scale * log2(e)
-  int waves;              // W (launched), W_eff <= W is derived on device
-  int min_chunks;         // minimum chunks per wavefront
+  int units;              // units (head groups of wavefronts) launched; the
+                          // number that receives work is derived on device
+  int min_chunks;         // minimum chunks per unit
   pagedkv_dtype_t dtype;  // element type of pool, q and out
 };
 
-constexpr int kMaxWaves = 8192;          // upper bound on W (256 CUs x 32)
+constexpr int kMaxWaves = 8192;          // upper bound on wavefronts (256 CUs x 32)
 constexpr int kMaxGroup = 16;            // query heads per KV head
 constexpr int kMfmaChunk = 16;           // tokens per chunk, MFMA kernel
 constexpr int kGenericChunk = 64;        // tokens per chunk, VALU kernel
@@ -118,7 +122,6 @@ bool mfma_supported(const kv_pool* pool, int group);
 bool generic_supported(const kv_pool* pool, int group);
 hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s);
-hipError_t launch_decode_reduce(const DecodeParams& p, int chunk_tokens,
-                                hipStream_t s);
+hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s);
 
 }  // namespace pagedkv
