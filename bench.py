@@ -26,6 +26,15 @@ import numpy as np
 
 HBM_PEAK_GBS = 8000.0
 MALL_BYTES = 256 << 20
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_mfma.hip")
+
+# HBM bytes per decode pass-1 launch, from two rocprofv3 PMC passes
+# (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000; the factors make a 1 GiB device
+# copy read and write 1 GiB), averaged over the rotated input replicas.  Only
+# valid for the pass-1 kernel source whose SHA-256 is recorded; otherwise the
+# JSON reports null.
+MEASURED_TRAFFIC = {}
 
 WORKLOADS = {
     "tiny_fp32_mha": 0,
@@ -34,6 +43,19 @@ WORKLOADS = {
     "long_context_bf16": 3,
     "high_concurrency_bf16": 4,
 }
+
+
+def pass1_source_sha() -> str:
+    import hashlib
+    with open(PASS1_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    rec = MEASURED_TRAFFIC.get(workload)
+    if rec is None or rec["kernel_sha256"] != pass1_source_sha():
+        return None
+    return rec["bytes"]
 
 
 def decode_bytes(w) -> int:
@@ -124,7 +146,7 @@ def main(argv=None) -> int:
         print("bench.py: no GPU visible", file=sys.stderr, flush=True)
         return 2
 
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, ROOT)
     import paged_kv_cache_resolve_amd as pk
     from workloads import make_workload
 
@@ -219,7 +241,7 @@ def main(argv=None) -> int:
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(args.workload),
             "algorithmic_bytes_per_launch": int(dec_bytes),
         },
     }

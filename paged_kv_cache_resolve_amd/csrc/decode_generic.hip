@@ -231,6 +231,14 @@ hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
     waves = p.pool.kv_heads;
   }
   if (p.min_chunks < 1) p.min_chunks = 2;
+  // no more units than the largest possible chunk count can keep busy
+  const int64_t max_chunks = (int64_t)p.batch *
+      (((int64_t)p.max_blocks_per_seq * p.pool.block_size + kGenericChunk - 1) / kGenericChunk);
+  const int64_t useful = (max_chunks + p.min_chunks - 1) / p.min_chunks;
+  if (useful < p.units) {
+    p.units = (int)(useful < 1 ? 1 : useful);
+    waves = p.units * p.pool.kv_heads;
+  }
   if (f32)
     hipLaunchKernelGGL(decode_generic_kernel<float>, dim3(waves), dim3(64), lds, s, p);
   else

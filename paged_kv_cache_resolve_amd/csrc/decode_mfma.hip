@@ -48,6 +48,10 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kWaves = 4;           // independent wavefronts per workgroup
 constexpr int kThreads = 64 * kWaves;
+#ifndef PAGEDKV_TILES_PER_STEP
+#define PAGEDKV_TILES_PER_STEP 2
+#endif
+constexpr int kTilesPerStep = PAGEDKV_TILES_PER_STEP;   // 16-token MFMA tiles per chunk
 
 template <int D> struct VRow;
 template <> struct VRow<128> { using type = uint4; };   // 8 bf16 per lane
@@ -96,10 +100,11 @@ __device__ __forceinline__ float sum_x32(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-template <int D>
+// K and V registers of one step: TILES tiles of 16 tokens.
+template <int D, int TILES>
 struct ChunkBuf {
-  bf16x8_t k[D / 32];
-  typename VRow<D>::type v[4];
+  bf16x8_t k[TILES][D / 32];
+  typename VRow<D>::type v[TILES][4];
 };
 
 template <int D> __device__ __forceinline__ void zero_row(typename VRow<D>::type& v);
@@ -122,9 +127,11 @@ struct Cursor {
   }
 };
 
-template <int D>
+// One wavefront's stream over its chunk range for KV head g.  A chunk is
+// TILES x 16 tokens; tile t of chunk j holds tokens 16 * (TILES * j + t) ...
+template <int D, int TILES>
 struct Stream {
-  static constexpr int NK = D / 32;   // 16-byte K loads per lane per chunk
+  static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
   static constexpr int VD = D / 16;   // V dims per lane
   static constexpr int NW = VD / 2;   // dwords per lane per V row
 
@@ -160,54 +167,79 @@ struct Stream {
     for (int i = 0; i < NK; ++i) qop[i] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * i);
   }
 
-  // Physical block of chunk c: a scalar load of the block-table entry.
-  __device__ __forceinline__ int phys_of(const Cursor& c) const {
+  // Physical blocks of chunk c's tiles: scalar loads of block-table
+  // entries.  A tile that starts at or past T (the sequence's last chunk can
+  // be partly empty) reuses tile 0's block: its loads stay inside the pool
+  // and all of its tokens are masked.
+  __device__ __forceinline__ void fetch_phys(const Cursor& c, int* ph) const {
     const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
-    return uni(trow[(c.j * 16) / p.pool.block_size]);
+    const int tok0 = c.j * (16 * TILES);
+    ph[0] = uni(trow[tok0 / p.pool.block_size]);
+#pragma unroll
+    for (int t = 1; t < TILES; ++t) {
+      const int tok = tok0 + 16 * t;
+      ph[t] = tok < c.T ? uni(trow[tok / p.pool.block_size]) : ph[0];
+    }
   }
 
-  // Byte address of the K rows of chunk c stored in physical block `phys`.
-  __device__ __forceinline__ const char* chunk_base(const Cursor& c, int phys) const {
+  // Byte address of the K rows of tile t of chunk c.
+  __device__ __forceinline__ const char* tile_base(const Cursor& c, const int* ph, int t) const {
+    const int tok = c.j * (16 * TILES) + 16 * t;
     return p.pool.base + 2 * ((int64_t)p.layer * p.pool.layer_stride +
                               (int64_t)g * p.pool.head_stride +
-                              (int64_t)phys * p.pool.block_stride +
-                              (int64_t)((c.j * 16) % p.pool.block_size) * D);
+                              (int64_t)ph[t] * p.pool.block_stride +
+                              (int64_t)(tok % p.pool.block_size) * D);
   }
 
-  __device__ __forceinline__ void issue_k(ChunkBuf<D>& cb, const char* kb) const {
-    const char* kl = kb + (uint32_t)(2 * (n * D + 8 * quad));
+  __device__ __forceinline__ void issue_k(ChunkBuf<D, TILES>& cb, const Cursor& c,
+                                          const int* ph) const {
 #pragma unroll
-    for (int i = 0; i < NK; ++i) cb.k[i] = *reinterpret_cast<const bf16x8_t*>(kl + 64 * i);
-  }
-  __device__ __forceinline__ void issue_v(ChunkBuf<D>& cb, const char* kb) const {
-    const char* vl = kb + 2 * p.pool.kv_stride + (uint32_t)(2 * (4 * quad * D + VD * n));
+    for (int t = 0; t < TILES; ++t) {
+      const char* kl = tile_base(c, ph, t) + (uint32_t)(2 * (n * D + 8 * quad));
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      cb.v[r] = *reinterpret_cast<const typename VRow<D>::type*>(vl + 2 * r * D);
-  }
-
-  __device__ __forceinline__ f32x4_t qk(const ChunkBuf<D>& cb) const {
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < NK; ++i)
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb.k[i], qop[i], s, 0, 0, 0);
-    return s;
-  }
-
-  // Scores -> bf16 probabilities in the B-operand layout, then the weighted
-  // V sum; updates m, l, acc.  TAIL masks tokens at or past T (only the last
-  // chunk of a pair can hold them); masked V rows are zeroed, not weighted
-  // by zero, so unused pool slots never reach the sum.
-  template <bool TAIL>
-  __device__ __forceinline__ void attend(f32x4_t s, ChunkBuf<D>& cb, const Cursor& c) {
-    const int tok0 = c.j * 16 + 4 * quad;
-    float sv[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      sv[r] = s[r] * p.scale_log2;
-      if (TAIL && tok0 + r >= c.T) sv[r] = -INFINITY;
+      for (int i = 0; i < NK; ++i) cb.k[t][i] = *reinterpret_cast<const bf16x8_t*>(kl + 64 * i);
     }
-    float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+  }
+  __device__ __forceinline__ void issue_v(ChunkBuf<D, TILES>& cb, const Cursor& c,
+                                          const int* ph) const {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const char* vl = tile_base(c, ph, t) + 2 * p.pool.kv_stride +
+                       (uint32_t)(2 * (4 * quad * D + VD * n));
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        cb.v[t][r] = *reinterpret_cast<const typename VRow<D>::type*>(vl + 2 * r * D);
+    }
+  }
+
+  __device__ __forceinline__ void qk(const ChunkBuf<D, TILES>& cb, f32x4_t* s) const {
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < NK; ++i)
+        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb.k[t][i], qop[i], s[t], 0, 0, 0);
+    }
+  }
+
+  // Scores -> bf16 probabilities (already in the B-operand layout of the PV
+  // product), then the weighted V sum; updates m, l, acc.  TAIL masks tokens
+  // at or past T; masked V rows are zeroed, not weighted by zero, so unused
+  // pool slots never reach the sum.
+  template <bool TAIL>
+  __device__ __forceinline__ void attend(const f32x4_t* s, ChunkBuf<D, TILES>& cb, const Cursor& c) {
+    float sv[TILES][4];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        sv[t][r] = s[t][r] * p.scale_log2;
+        if (TAIL && c.j * (16 * TILES) + 16 * t + 4 * quad + r >= c.T) sv[t][r] = -INFINITY;
+      }
+    float bmax = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
+#pragma unroll
+    for (int t = 1; t < TILES; ++t)
+      bmax = fmaxf(bmax, fmaxf(fmaxf(sv[t][0], sv[t][1]), fmaxf(sv[t][2], sv[t][3])));
     bmax = max_x32(max_x16(bmax));
     {
       // branch-free rescale (alpha = 1 when no running max grows)
@@ -218,32 +250,66 @@ struct Stream {
       l *= alpha;
       m = mn;
     }
-    const uint32_t p01 = pack_bf16x2(__builtin_amdgcn_exp2f(sv[0] - m), __builtin_amdgcn_exp2f(sv[1] - m));
-    const uint32_t p23 = pack_bf16x2(__builtin_amdgcn_exp2f(sv[2] - m), __builtin_amdgcn_exp2f(sv[3] - m));
-    l += (bf16_lo(p01) + bf16_hi(p01)) + (bf16_lo(p23) + bf16_hi(p23));
-    const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(p01, p23));
+    uint32_t pw[TILES][2];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      pw[t][0] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[t][0] - m), __builtin_amdgcn_exp2f(sv[t][1] - m));
+      pw[t][1] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[t][2] - m), __builtin_amdgcn_exp2f(sv[t][3] - m));
+      l += (bf16_lo(pw[t][0]) + bf16_hi(pw[t][0])) + (bf16_lo(pw[t][1]) + bf16_hi(pw[t][1]));
+    }
     if (TAIL) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (tok0 + r >= c.T) zero_row<D>(cb.v[r]);
-    }
+      for (int t = 0; t < TILES; ++t)
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const uint32_t v0 = dword_of(cb.v[0], w), v1 = dword_of(cb.v[1], w);
-      const uint32_t v2 = dword_of(cb.v[2], w), v3 = dword_of(cb.v[3], w);
-      const uint2 ev = make_uint2(__builtin_amdgcn_perm(v1, v0, 0x05040100u),
-                                  __builtin_amdgcn_perm(v3, v2, 0x05040100u));
-      const uint2 od = make_uint2(__builtin_amdgcn_perm(v1, v0, 0x07060302u),
-                                  __builtin_amdgcn_perm(v3, v2, 0x07060302u));
-      acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, ev), pop,
-                                                             acc[2 * w], 0, 0, 0);
-      acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, od), pop,
-                                                                 acc[2 * w + 1], 0, 0, 0);
+        for (int r = 0; r < 4; ++r)
+          if (c.j * (16 * TILES) + 16 * t + 4 * quad + r >= c.T) zero_row<D>(cb.v[t][r]);
+    }
+    if constexpr (TILES == 1) {
+      // k = 4 tokens per lane: v_mfma_f32_16x16x16_bf16
+      const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(pw[0][0], pw[0][1]));
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const uint32_t v0 = dword_of(cb.v[0][0], w), v1 = dword_of(cb.v[0][1], w);
+        const uint32_t v2 = dword_of(cb.v[0][2], w), v3 = dword_of(cb.v[0][3], w);
+        const uint2 ev = make_uint2(__builtin_amdgcn_perm(v1, v0, 0x05040100u),
+                                    __builtin_amdgcn_perm(v3, v2, 0x05040100u));
+        const uint2 od = make_uint2(__builtin_amdgcn_perm(v1, v0, 0x07060302u),
+                                    __builtin_amdgcn_perm(v3, v2, 0x07060302u));
+        acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, ev), pop,
+                                                               acc[2 * w], 0, 0, 0);
+        acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, od),
+                                                                   pop, acc[2 * w + 1], 0, 0, 0);
+      }
+    } else {
+      // k = 8 tokens per lane (4 of each tile, in the order the lane holds
+      // its scores): v_mfma_f32_16x16x32_bf16
+      const bf16x8_t pop =
+          __builtin_bit_cast(bf16x8_t, make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        uint32_t ev[4], od[4];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const uint32_t v0 = dword_of(cb.v[t][0], w), v1 = dword_of(cb.v[t][1], w);
+          const uint32_t v2 = dword_of(cb.v[t][2], w), v3 = dword_of(cb.v[t][3], w);
+          ev[2 * t] = __builtin_amdgcn_perm(v1, v0, 0x05040100u);
+          ev[2 * t + 1] = __builtin_amdgcn_perm(v3, v2, 0x05040100u);
+          od[2 * t] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
+          od[2 * t + 1] = __builtin_amdgcn_perm(v3, v2, 0x07060302u);
+        }
+        acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, make_uint4(ev[0], ev[1], ev[2], ev[3])), pop, acc[2 * w],
+            0, 0, 0);
+        acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8_t, make_uint4(od[0], od[1], od[2], od[3])), pop,
+            acc[2 * w + 1], 0, 0, 0);
+      }
     }
   }
 
-  __device__ __forceinline__ void attend_chunk(f32x4_t s, ChunkBuf<D>& cb, const Cursor& c) {
-    if (c.j == c.nb - 1 && (c.T & 15) != 0)
+  __device__ __forceinline__ void attend_chunk(const f32x4_t* s, ChunkBuf<D, TILES>& cb,
+                                               const Cursor& c) {
+    if (c.j == c.nb - 1 && (c.T % (16 * TILES)) != 0)
       attend<true>(s, cb, c);
     else
       attend<false>(s, cb, c);
@@ -260,19 +326,15 @@ struct Stream {
       const float inv = 1.0f / lt;
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
                       ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + n) * D + 4 * VD * quad;
-      uint4* d4 = reinterpret_cast<uint4*>(dst);
+      if constexpr (VD == 8) {
+        uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int h = 0; h < VD / 8; ++h) {
-          const int i0 = 8 * h;
-          d4[r * (VD / 8) + h] = make_uint4(
-              pack_bf16x2(acc[i0 + 0][r] * inv, acc[i0 + 1][r] * inv),
-              pack_bf16x2(acc[i0 + 2][r] * inv, acc[i0 + 3][r] * inv),
-              pack_bf16x2(acc[i0 + 4][r] * inv, acc[i0 + 5][r] * inv),
-              pack_bf16x2(acc[i0 + 6][r] * inv, acc[i0 + 7][r] * inv));
-        }
-      if (VD == 4) {   // head_dim 64: 4 values per row r, 2 rows per 16-byte store
+        for (int r = 0; r < 4; ++r)
+          d4[r] = make_uint4(pack_bf16x2(acc[0][r] * inv, acc[1][r] * inv),
+                             pack_bf16x2(acc[2][r] * inv, acc[3][r] * inv),
+                             pack_bf16x2(acc[4][r] * inv, acc[5][r] * inv),
+                             pack_bf16x2(acc[6][r] * inv, acc[7][r] * inv));
+      } else {
         uint2* d2 = reinterpret_cast<uint2*>(dst);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
@@ -296,13 +358,13 @@ struct Stream {
   }
 };
 
-template <int D>
+template <int D, int TILES>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ int32_t prefix[];
   __shared__ int32_t scan[kThreads];
   const int H = p.pool.kv_heads;
 
-  block_chunk_prefix<kThreads>(p.context_lens, p.batch, kMfmaChunk, prefix, scan);
+  block_chunk_prefix<kThreads>(p.context_lens, p.batch, 16 * TILES, prefix, scan);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= p.batch; i += kThreads) p.ws_prefix[i] = prefix[i];
 
@@ -323,39 +385,42 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   cur.j = uni((int)(c0 - prefix[cur.b]));
   cur.T = uni(lens[cur.b]);
 
-  Stream<D> st(p, lane, g, unit);
+  Stream<D, TILES> st(p, lane, g, unit);
   st.reset();
   st.load_q(cur);
-  ChunkBuf<D> cb;
-  const char* kb = st.chunk_base(cur, st.phys_of(cur));
-  st.issue_k(cb, kb);
-  st.issue_v(cb, kb);
+  ChunkBuf<D, TILES> cb;
+  int ph[TILES], ph_nx[TILES], ph_n2[TILES];
+  st.fetch_phys(cur, ph);
+  st.issue_k(cb, cur, ph);
+  st.issue_v(cb, cur, ph);
   Cursor nx = cur;
-  int phys_nx = 0;
+#pragma unroll
+  for (int t = 0; t < TILES; ++t) ph_nx[t] = 0;
   if (rem > 1) {
     nx.advance(prefix, lens, p.batch);
-    phys_nx = st.phys_of(nx);
+    st.fetch_phys(nx, ph_nx);
   }
   bool whole_start = cur.j == 0;   // this wave has seen the current sequence from chunk 0
 
+  f32x4_t s[TILES];
   for (int i = 0; i + 1 < rem; ++i) {
-    const f32x4_t s = st.qk(cb);
+    st.qk(cb, s);
     __builtin_amdgcn_sched_barrier(0);
-    kb = st.chunk_base(nx, phys_nx);
-    st.issue_k(cb, kb);
+    st.issue_k(cb, nx, ph_nx);
     // q is dead until the next chunk's QK, so a new sequence's q loads in place
     const bool sw = nx.b != cur.b;
     if (sw) st.load_q(nx);
     __builtin_amdgcn_sched_barrier(0);
     Cursor n2 = nx;
-    int phys_n2 = 0;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) ph_n2[t] = 0;
     if (i + 2 < rem) {
       n2.advance(prefix, lens, p.batch);
-      phys_n2 = st.phys_of(n2);
+      st.fetch_phys(n2, ph_n2);
     }
     st.attend_chunk(s, cb, cur);
     __builtin_amdgcn_sched_barrier(0);
-    st.issue_v(cb, kb);
+    st.issue_v(cb, nx, ph_nx);
     __builtin_amdgcn_sched_barrier(0);
     if (sw) {
       st.flush(cur, whole_start);
@@ -364,12 +429,15 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     }
     cur = nx;
     nx = n2;
-    phys_nx = phys_n2;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) ph_nx[t] = ph_n2[t];
   }
-  const f32x4_t s = st.qk(cb);
+  st.qk(cb, s);
   st.attend_chunk(s, cb, cur);
   st.flush(cur, whole_start && cur.j == cur.nb - 1);
 }
+
+size_t mfma_lds_bytes(int batch) { return sizeof(int32_t) * (size_t)(batch + 1); }
 
 }  // namespace
 
@@ -378,24 +446,36 @@ bool mfma_supported(const kv_pool* pool, int group) {
          pool->block_size % 16 == 0 && group >= 1 && group <= kMaxGroup;
 }
 
+int mfma_chunk_tokens() { return 16 * kTilesPerStep; }
+
 hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
-  const size_t lds = sizeof(int32_t) * (size_t)(p.batch + 1);
-  const void* fn = p.pool.head_dim == 128 ? reinterpret_cast<const void*>(&decode_mfma_kernel<128>)
-                                          : reinterpret_cast<const void*>(&decode_mfma_kernel<64>);
+  const size_t lds = mfma_lds_bytes(p.batch);
+  const void* fn = p.pool.head_dim == 128
+                       ? reinterpret_cast<const void*>(&decode_mfma_kernel<128, kTilesPerStep>)
+                       : reinterpret_cast<const void*>(&decode_mfma_kernel<64, kTilesPerStep>);
   int wgs = 0;
   hipError_t e = resident_workgroups(fn, kThreads, lds, &wgs);
   if (e != hipSuccess) return e;
-  if (wgs > kMaxWaves / kWaves) wgs = kMaxWaves / kWaves;
+  const int dev_wgs = wgs;
+  wgs = decode_workgroups(dev_wgs);
   p.units = wgs * kWaves / p.pool.kv_heads;   // head groups
   if (p.units < 1) {                          // more KV heads than resident waves
     p.units = 1;
     wgs = (p.pool.kv_heads + kWaves - 1) / kWaves;
   }
-  if (p.min_chunks < 1) p.min_chunks = 4;
+  if (p.min_chunks < 1) p.min_chunks = 2;
+  // no more units than the largest possible chunk count can keep busy
+  const int64_t max_chunks = (int64_t)p.batch *
+      (((int64_t)p.max_blocks_per_seq * p.pool.block_size + 16 * kTilesPerStep - 1) / (16 * kTilesPerStep));
+  const int64_t useful = (max_chunks + p.min_chunks - 1) / p.min_chunks;
+  if (useful < p.units) {
+    p.units = (int)(useful < 1 ? 1 : useful);
+    wgs = (p.units * p.pool.kv_heads + kWaves - 1) / kWaves;
+  }
   if (p.pool.head_dim == 128)
-    hipLaunchKernelGGL(decode_mfma_kernel<128>, dim3(wgs), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<128, kTilesPerStep>), dim3(wgs), dim3(kThreads), lds, s, p);
   else
-    hipLaunchKernelGGL(decode_mfma_kernel<64>, dim3(wgs), dim3(kThreads), lds, s, p);
+    hipLaunchKernelGGL((decode_mfma_kernel<64, kTilesPerStep>), dim3(wgs), dim3(kThreads), lds, s, p);
   return hipGetLastError();
 }
 

@@ -92,7 +92,7 @@ struct DecodeParams {
 
 constexpr int kMaxWaves = 8192;          // upper bound on wavefronts (256 CUs x 32)
 constexpr int kMaxGroup = 16;            // query heads per KV head
-constexpr int kMfmaChunk = 16;           // tokens per chunk, MFMA kernel
+constexpr int kDecodeWgPerCu = 1;        // decode workgroups (4 wavefronts) per CU
 constexpr int kGenericChunk = 64;        // tokens per chunk, VALU kernel
 constexpr int kMaxBatchLds = 16384;      // sequences whose prefix fits in LDS
 
@@ -115,6 +115,10 @@ hipError_t launch_resolve(int64_t* slots, const int32_t* tables, int mb,
 
 // Workgroups the device holds at once for kernel `fn` (cached per device).
 hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out);
+// Decode pass-1 workgroups to launch: kDecodeWgPerCu per CU (the
+// PAGEDKV_DECODE_WG_PER_CU environment variable overrides it, for launch-shape
+// sweeps), never more than `resident`.
+int decode_workgroups(int resident);
 
 // Decode pass 1 variants and pass 2.  The *_supported predicates say which
 // shapes each pass-1 kernel handles.

@@ -1,6 +1,8 @@
 // Per-device launch sizing for the persistent decode kernels, cached so that
 // a decode call does not query the runtime every time.
 
+#include <stdlib.h>
+
 #include <mutex>
 #include <unordered_map>
 
@@ -57,6 +59,22 @@ hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out
   g_blocks[key] = total;
   *out = total;
   return hipSuccess;
+}
+
+int decode_workgroups(int resident) {
+  static const int per_cu = [] {
+    const char* v = getenv("PAGEDKV_DECODE_WG_PER_CU");
+    const int x = v ? atoi(v) : 0;
+    return x > 0 ? x : kDecodeWgPerCu;
+  }();
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return resident;
+  const int want = cus * per_cu;
+  int n = want < resident ? want : resident;
+  if (n > kMaxWaves / 4) n = kMaxWaves / 4;
+  return n < 1 ? 1 : n;
 }
 
 }  // namespace pagedkv
