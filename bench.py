@@ -34,7 +34,16 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # copy read and write 1 GiB), averaged over the rotated input replicas.  Only
 # valid for the pass-1 kernel source whose SHA-256 is recorded; otherwise the
 # JSON reports null.
-MEASURED_TRAFFIC = {}
+MEASURED_TRAFFIC = {
+    "llama8b_decode_bf16": {
+        "kernel_sha256": "ab046a43a16a225431b28367a12e03c211a21061357545731a11ccaa6c21cd5c",
+        "bytes": 585279804,
+    },
+    "long_context_bf16": {
+        "kernel_sha256": "ab046a43a16a225431b28367a12e03c211a21061357545731a11ccaa6c21cd5c",
+        "bytes": 2210701425,
+    },
+}
 
 WORKLOADS = {
     "tiny_fp32_mha": 0,
