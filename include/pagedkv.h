@@ -166,6 +166,30 @@ int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
                            void* workspace, size_t workspace_bytes,
                            void* stream);
 
+/* One decode step: append each sequence's new token, then decode
+ * ([kv-cache] section 2: generation fills the tail block one token at a
+ * time; [vllmini] "The CUDA Block Kernel": attention over the blocks the
+ * table names).  The result, in `out` and in the pool, equals
+ *     kv_append(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq,
+ *               positions, batch, stream);
+ *     paged_attention_decode(out, q, pool, layer, block_tables, ...);
+ * for every input, positions included (negative = no token for b; a
+ * position at or past T_b is written but not attended, as in the two-call
+ * form).  Arguments are those of the two calls; k_new, v_new and positions
+ * must all be non-null when batch > 0.
+ * For bf16 pools with head_dim 64 or 128 and block_size a multiple of 16 the
+ * decode kernel reads each new K/V row from k_new / v_new instead of the
+ * pool and the merge kernel stores them into the pool afterwards, which
+ * saves the separate append launch; other shapes run the two launches. */
+int paged_attention_decode_append(void* out, const void* q, const void* k_new,
+                                  const void* v_new, const int32_t* positions,
+                                  kv_pool_t* pool, int layer,
+                                  const int32_t* block_tables,
+                                  int max_blocks_per_seq,
+                                  const int32_t* context_lens, int batch,
+                                  int num_q_heads, float scale, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Block-table resolution on its own ([vllmini] "PagedAttention Metaphor":
  * logical offsets resolved to physical page offsets on the fly).
  *   slots : device, [batch][max_len] int64; slots[b][t] =

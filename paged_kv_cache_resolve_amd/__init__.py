@@ -9,6 +9,8 @@ streams.
     pool = kv_pool_create(num_blocks, block_size, layers, kv_heads, head_dim, dtype)
     kv_append(pool, layer, k_new, v_new, block_tables, positions)
     paged_attention_decode(out, q, pool, layer, block_tables, context_lens, scale)
+    paged_attention_decode_append(out, q, pool, layer, block_tables, context_lens, scale,
+                                  k_new, v_new, positions)   # both of the above in one call
     k_all, v_all, mask = paged_kv_gather(pool, layer, block_tables, context_lens, max_len)
 """
 
@@ -25,6 +27,7 @@ _L = _lib.load()
 
 __all__ = [
     "KVPool", "kv_pool_create", "kv_append", "paged_kv_gather", "paged_attention_decode",
+    "paged_attention_decode_append",
     "paged_attention_workspace_bytes", "paged_kv_resolve", "PagedKVError", "OutOfBlocksError",
     "library",
 ]
@@ -187,13 +190,7 @@ def _workspace(pool: KVPool, nbytes: int) -> torch.Tensor:
     return ws
 
 
-def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, pool: KVPool, layer: int,
-                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                           workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """out[b, h] = softmax_t(scale * q[b, h] . K_t) V_t over the T_b cached
-    tokens of sequence b, resolved through its block table.  q and out are
-    [batch, num_q_heads, head_dim] in the pool dtype.  A workspace is taken
-    from a per-stream cache unless one is given."""
+def _decode_args(out, q, pool, block_tables, context_lens, workspace):
     if q.dim() != 3:
         raise ValueError("q must be [batch, num_q_heads, head_dim]")
     batch, hq, d = (int(x) for x in q.shape)
@@ -207,9 +204,43 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, pool: KVPool, lay
     if workspace is None:
         workspace = _workspace(pool, need)
     wp = _dev_tensor(workspace, "workspace", pool.device, torch.uint8)
+    return batch, hq, qp, op, tp, mb, lp, wp, workspace.numel()
+
+
+def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, pool: KVPool, layer: int,
+                           block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """out[b, h] = softmax_t(scale * q[b, h] . K_t) V_t over the T_b cached
+    tokens of sequence b, resolved through its block table.  q and out are
+    [batch, num_q_heads, head_dim] in the pool dtype.  A workspace is taken
+    from a per-stream cache unless one is given."""
+    batch, hq, qp, op, tp, mb, lp, wp, wn = _decode_args(out, q, pool, block_tables,
+                                                         context_lens, workspace)
     _check(_L.paged_attention_decode(op, qp, pool.handle, layer, tp, mb, lp, batch, hq,
-                                     ctypes.c_float(scale), wp, workspace.numel(),
-                                     _stream(pool.device)), "paged_attention_decode")
+                                     ctypes.c_float(scale), wp, wn, _stream(pool.device)),
+           "paged_attention_decode")
+    return out
+
+
+def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, pool: KVPool, layer: int,
+                                  block_tables: torch.Tensor, context_lens: torch.Tensor,
+                                  scale: float, k_new: torch.Tensor, v_new: torch.Tensor,
+                                  positions: torch.Tensor,
+                                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """kv_append(pool, layer, k_new, v_new, block_tables, positions) followed
+    by paged_attention_decode(out, q, ...), as one library call (the decode
+    kernel reads the new rows from k_new / v_new where it can, saving the
+    separate append launch)."""
+    batch, hq, qp, op, tp, mb, lp, wp, wn = _decode_args(out, q, pool, block_tables,
+                                                         context_lens, workspace)
+    shape = (batch, pool.kv_heads, pool.head_dim)
+    kp = _dev_tensor(k_new, "k_new", pool.device, pool.dtype, shape)
+    vp = _dev_tensor(v_new, "v_new", pool.device, pool.dtype, shape)
+    pp = _dev_tensor(positions, "positions", pool.device, torch.int32, (batch,))
+    _check(_L.paged_attention_decode_append(op, qp, kp, vp, pp, pool.handle, layer, tp, mb, lp,
+                                            batch, hq, ctypes.c_float(scale), wp, wn,
+                                            _stream(pool.device)),
+           "paged_attention_decode_append")
     return out
 
 

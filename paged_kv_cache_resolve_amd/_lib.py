@@ -44,6 +44,9 @@ SIGNATURES = {
     "paged_attention_workspace_bytes": (_c_size, [_vp, _c_int, _c_int]),
     "paged_attention_decode": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int,
                                         ctypes.c_float, _vp, _c_size, _vp]),
+    "paged_attention_decode_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int,
+                                               _vp, _c_int, _c_int, ctypes.c_float, _vp, _c_size,
+                                               _vp]),
     "paged_kv_resolve": (_c_int, [_vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp]),
     "pagedkv_status_string": (ctypes.c_char_p, [_c_int]),
 }

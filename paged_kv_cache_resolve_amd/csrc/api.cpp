@@ -161,15 +161,23 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch, int num
                                 pool->head_dim);
 }
 
-int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool, int layer,
-                           const int32_t* block_tables, int max_blocks_per_seq,
-                           const int32_t* context_lens, int batch, int num_q_heads, float scale,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Shared body of the decode entry points.  With k_new != nullptr the call
+// also appends each sequence's new token (the fused form).
+int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
+                const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
+                int batch, int num_q_heads, float scale, void* workspace, size_t workspace_bytes,
+                void* stream, const void* k_new, const void* v_new, const int32_t* positions) {
   if (!pool || batch < 0 || layer < 0 || layer >= pool->layers || max_blocks_per_seq < 1 ||
       num_q_heads < 1 || num_q_heads % pool->kv_heads != 0 || !isfinite(scale))
     return PAGEDKV_ERR_INVALID_ARG;
   if (batch == 0) return PAGEDKV_OK;
   if (!out || !q || !block_tables || !context_lens) return PAGEDKV_ERR_INVALID_ARG;
+  const bool append = k_new != nullptr || v_new != nullptr || positions != nullptr;
+  if (append && (!k_new || !v_new || !positions)) return PAGEDKV_ERR_INVALID_ARG;
   if (batch > kMaxBatchLds) return PAGEDKV_ERR_UNSUPPORTED;
   const int group = num_q_heads / pool->kv_heads;
   const bool use_mfma = mfma_supported(pool, group);
@@ -196,9 +204,50 @@ int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool, int 
   p.dtype = pool->dtype;
   p.min_chunks = 0;   // launcher default
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = use_mfma ? launch_decode_mfma(p, s) : launch_decode_generic(p, s);
+  hipError_t e;
+  if (use_mfma) {
+    if (append) {
+      p.k_new = k_new;
+      p.v_new = v_new;
+      p.positions = positions;
+    }
+    e = launch_decode_mfma(p, s);
+  } else {
+    // the VALU kernel reads the pool only: append first, as its own launch
+    if (append) {
+      e = launch_append(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq, positions,
+                        batch, s);
+      if (e != hipSuccess) return PAGEDKV_ERR_HIP;
+    }
+    e = launch_decode_generic(p, s);
+  }
   if (e != hipSuccess) return PAGEDKV_ERR_HIP;
   return hip_status(launch_decode_merge(p, s));
+}
+
+}  // namespace
+
+extern "C" {
+
+int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool, int layer,
+                           const int32_t* block_tables, int max_blocks_per_seq,
+                           const int32_t* context_lens, int batch, int num_q_heads, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_call(out, q, pool, layer, block_tables, max_blocks_per_seq, context_lens, batch,
+                     num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr,
+                     nullptr);
+}
+
+int paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
+                                  const int32_t* positions, kv_pool_t* pool, int layer,
+                                  const int32_t* block_tables, int max_blocks_per_seq,
+                                  const int32_t* context_lens, int batch, int num_q_heads,
+                                  float scale, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (batch > 0 && (!k_new || !v_new || !positions)) return PAGEDKV_ERR_INVALID_ARG;
+  return decode_call(out, q, pool, layer, block_tables, max_blocks_per_seq, context_lens, batch,
+                     num_q_heads, scale, workspace, workspace_bytes, stream, k_new, v_new,
+                     positions);
 }
 
 int paged_kv_resolve(int64_t* slots, const int32_t* block_tables, int max_blocks_per_seq,

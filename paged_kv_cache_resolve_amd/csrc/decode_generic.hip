@@ -120,19 +120,32 @@ __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int
     const int ntok = min(64, T - j * kGenericChunk);
     const uint32_t row_lo = (uint32_t)(row & 0xffffffffu);
     const uint32_t row_hi = (uint32_t)(row >> 32);
-    for (int t = 0; t < ntok; ++t) {
-      const int64_t r = ((int64_t)(uint32_t)__builtin_amdgcn_readlane((int)row_hi, t) << 32) |
-                        (uint32_t)__builtin_amdgcn_readlane((int)row_lo, t);
-      const TS* vrow = pool + r + p.pool.kv_stride;
+    // V rows 16 at a time: the 16 loads of a batch are independent, so they
+    // are in flight together instead of one round trip per token.
+    for (int t0 = 0; t0 < ntok; t0 += 16) {
+      float v[16][kGenDimsPerLane];
 #pragma unroll
-      for (int i = 0; i < kGenDimsPerLane; ++i) {
-        const int d = lane + 64 * i;
-        if (d < D) {
-          const float v = to_f32<TS>(vrow[d]);
+      for (int u = 0; u < 16; ++u) {
+        const int t = min(t0 + u, ntok - 1);   // repeats past ntok are skipped below
+        const int64_t r = ((int64_t)(uint32_t)__builtin_amdgcn_readlane((int)row_hi, t) << 32) |
+                          (uint32_t)__builtin_amdgcn_readlane((int)row_lo, t);
+        const TS* vrow = pool + r + p.pool.kv_stride;
 #pragma unroll
-          for (int h = 0; h < kMaxGroup; ++h)
-            if (h < G) acc[h][i] += ps[h * 64 + t] * v;
+        for (int i = 0; i < kGenDimsPerLane; ++i) {
+          const int d = lane + 64 * i;
+          v[u][i] = d < D ? to_f32<TS>(vrow[d]) : 0.f;
         }
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        if (t0 + u >= ntok) break;
+#pragma unroll
+        for (int h = 0; h < kMaxGroup; ++h)
+          if (h < G) {
+            const float pw = ps[h * 64 + t0 + u];
+#pragma unroll
+            for (int i = 0; i < kGenDimsPerLane; ++i) acc[h][i] += pw * v[u][i];
+          }
       }
     }
     __syncthreads();

@@ -7,6 +7,10 @@
 //     out = (sum_k w_k o_k) / (sum_k w_k l_k),
 // the softmax-weighted V sum over the whole context, accumulated here with
 // an online (running-max) update.  Empty sequences (T_b = 0) get zero rows.
+//
+// For a fused append, this pass also stores each sequence's new K/V rows
+// into the pool: pass 1 read them from the k_new / v_new inputs, so the pool
+// copy is only needed by later calls.
 
 #include <math.h>
 
@@ -39,6 +43,28 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   const int g = h / G;
   const int hn = h - g * G;
   TS* out = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + h) * D;
+
+  if (p.positions != nullptr && hn == 0) {
+    // the first wave of each (b, g) writes the new token of that KV head
+    const int pos = p.positions[b];
+    if (pos >= 0) {
+      const int units = D * (int)sizeof(TS) / 16;   // 16-byte units per row
+      const int phys = p.block_tables[(int64_t)b * p.max_blocks_per_seq + pos / p.pool.block_size];
+      const int64_t row = (int64_t)phys * p.pool.block_stride + (int64_t)p.layer * p.pool.layer_stride +
+                          (int64_t)g * p.pool.head_stride +
+                          (int64_t)(pos % p.pool.block_size) * D;
+      const int64_t src = ((int64_t)b * H + g) * D;
+      for (int i = lane; i < 2 * units; i += 64) {
+        const int kv = i >= units;
+        const int u = i - kv * units;
+        const uint4* from = reinterpret_cast<const uint4*>(
+            static_cast<const TS*>(kv ? p.v_new : p.k_new) + src);
+        uint4* to = reinterpret_cast<uint4*>(
+            reinterpret_cast<TS*>(const_cast<char*>(p.pool.base)) + row + kv * p.pool.kv_stride);
+        to[u] = from[u];
+      }
+    }
+  }
 
   const int pb = p.ws_prefix[b];
   const int nb = p.ws_prefix[b + 1] - pb;

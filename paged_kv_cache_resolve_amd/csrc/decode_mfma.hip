@@ -112,24 +112,35 @@ template <> __device__ __forceinline__ void zero_row<128>(uint4& v) { v = make_u
 template <> __device__ __forceinline__ void zero_row<64>(uint2& v) { v = make_uint2(0, 0); }
 
 // Position in the chunk space of one KV head: chunk j of sequence b, which
-// has nb chunks and T tokens.  All fields are wave-uniform.
+// has nb chunks and T tokens; pos is b's appended token (fused append only,
+// else -1).  All fields are wave-uniform.
 struct Cursor {
-  int b, j, nb, T;
+  int b, j, nb, T, pos;
+
+  __device__ __forceinline__ void load_seq(const int32_t* prefix, const_i32_ptr lens,
+                                           const_i32_ptr positions) {
+    nb = uni(prefix[b + 1] - prefix[b]);
+    T = uni(lens[b]);
+    pos = positions ? uni(positions[b]) : -1;
+  }
 
   // Step to the next chunk.  The caller guarantees one exists.
-  __device__ __forceinline__ void advance(const int32_t* prefix, const_i32_ptr lens, int batch) {
+  __device__ __forceinline__ void advance(const int32_t* prefix, const_i32_ptr lens,
+                                          const_i32_ptr positions, int batch) {
     if (++j < nb) return;
     j = 0;
     do { ++b; } while (b < batch - 1 && prefix[b + 1] == prefix[b]);
     b = uni(b);
-    nb = uni(prefix[b + 1] - prefix[b]);
-    T = uni(lens[b]);
+    load_seq(prefix, lens, positions);
   }
 };
 
 // One wavefront's stream over its chunk range for KV head g.  A chunk is
 // TILES x 16 tokens; tile t of chunk j holds tokens 16 * (TILES * j + t) ...
-template <int D, int TILES>
+// With APPEND, the row of a sequence's appended token is read from k_new /
+// v_new instead of the pool (a per-lane address choice; the pool row is
+// written by the merge pass).
+template <int D, int TILES, bool APPEND>
 struct Stream {
   static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
   static constexpr int VD = D / 16;   // V dims per lane
@@ -191,11 +202,21 @@ struct Stream {
                               (int64_t)(tok % p.pool.block_size) * D);
   }
 
+  // Row of the new token of (c.b, g) in k_new (kv = 0) or v_new (kv = 1).
+  __device__ __forceinline__ const char* new_row(const Cursor& c, int kv) const {
+    return static_cast<const char*>(kv ? p.v_new : p.k_new) +
+           2 * ((int64_t)c.b * p.pool.kv_heads + g) * D;
+  }
+
   __device__ __forceinline__ void issue_k(ChunkBuf<D, TILES>& cb, const Cursor& c,
                                           const int* ph) const {
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const char* kl = tile_base(c, ph, t) + (uint32_t)(2 * (n * D + 8 * quad));
+      if constexpr (APPEND) {
+        const int tok = c.j * (16 * TILES) + 16 * t + n;
+        if (tok == c.pos) kl = new_row(c, 0) + 2 * 8 * quad;
+      }
 #pragma unroll
       for (int i = 0; i < NK; ++i) cb.k[t][i] = *reinterpret_cast<const bf16x8_t*>(kl + 64 * i);
     }
@@ -207,8 +228,14 @@ struct Stream {
       const char* vl = tile_base(c, ph, t) + 2 * p.pool.kv_stride +
                        (uint32_t)(2 * (4 * quad * D + VD * n));
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        cb.v[t][r] = *reinterpret_cast<const typename VRow<D>::type*>(vl + 2 * r * D);
+      for (int r = 0; r < 4; ++r) {
+        const char* row = vl + 2 * r * D;
+        if constexpr (APPEND) {
+          const int tok = c.j * (16 * TILES) + 16 * t + 4 * quad + r;
+          if (tok == c.pos) row = new_row(c, 1) + 2 * VD * n;
+        }
+        cb.v[t][r] = *reinterpret_cast<const typename VRow<D>::type*>(row);
+      }
     }
   }
 
@@ -358,7 +385,7 @@ struct Stream {
   }
 };
 
-template <int D, int TILES>
+template <int D, int TILES, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ int32_t prefix[];
   __shared__ int32_t scan[kThreads];
@@ -379,13 +406,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int rem = (int)(wave_begin(unit + 1, C, Ue) - c0);   // >= 1
 
   const const_i32_ptr lens = (const_i32_ptr)p.context_lens;
+  const const_i32_ptr poss = APPEND ? (const_i32_ptr)p.positions : nullptr;
   Cursor cur;
   cur.b = uni(seq_of_chunk(prefix, p.batch, c0));
-  cur.nb = uni(prefix[cur.b + 1] - prefix[cur.b]);
+  cur.load_seq(prefix, lens, poss);
   cur.j = uni((int)(c0 - prefix[cur.b]));
-  cur.T = uni(lens[cur.b]);
 
-  Stream<D, TILES> st(p, lane, g, unit);
+  Stream<D, TILES, APPEND> st(p, lane, g, unit);
   st.reset();
   st.load_q(cur);
   ChunkBuf<D, TILES> cb;
@@ -397,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
   for (int t = 0; t < TILES; ++t) ph_nx[t] = 0;
   if (rem > 1) {
-    nx.advance(prefix, lens, p.batch);
+    nx.advance(prefix, lens, poss, p.batch);
     st.fetch_phys(nx, ph_nx);
   }
   bool whole_start = cur.j == 0;   // this wave has seen the current sequence from chunk 0
@@ -415,7 +442,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 #pragma unroll
     for (int t = 0; t < TILES; ++t) ph_n2[t] = 0;
     if (i + 2 < rem) {
-      n2.advance(prefix, lens, p.batch);
+      n2.advance(prefix, lens, poss, p.batch);
       st.fetch_phys(n2, ph_n2);
     }
     st.attend_chunk(s, cb, cur);
@@ -448,11 +475,20 @@ bool mfma_supported(const kv_pool* pool, int group) {
 
 int mfma_chunk_tokens() { return 16 * kTilesPerStep; }
 
+namespace {
+template <int D, bool APPEND>
+void launch_one(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL((decode_mfma_kernel<D, kTilesPerStep, APPEND>), dim3(wgs), dim3(kThreads), lds,
+                     s, p);
+}
+}  // namespace
+
 hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   const size_t lds = mfma_lds_bytes(p.batch);
+  // every instantiation has the same resources: size the grid by one
   const void* fn = p.pool.head_dim == 128
-                       ? reinterpret_cast<const void*>(&decode_mfma_kernel<128, kTilesPerStep>)
-                       : reinterpret_cast<const void*>(&decode_mfma_kernel<64, kTilesPerStep>);
+                       ? reinterpret_cast<const void*>(&decode_mfma_kernel<128, kTilesPerStep, false>)
+                       : reinterpret_cast<const void*>(&decode_mfma_kernel<64, kTilesPerStep, false>);
   int wgs = 0;
   hipError_t e = resident_workgroups(fn, kThreads, lds, &wgs);
   if (e != hipSuccess) return e;
@@ -472,10 +508,12 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
     p.units = (int)(useful < 1 ? 1 : useful);
     wgs = (p.units * p.pool.kv_heads + kWaves - 1) / kWaves;
   }
-  if (p.pool.head_dim == 128)
-    hipLaunchKernelGGL((decode_mfma_kernel<128, kTilesPerStep>), dim3(wgs), dim3(kThreads), lds, s, p);
-  else
-    hipLaunchKernelGGL((decode_mfma_kernel<64, kTilesPerStep>), dim3(wgs), dim3(kThreads), lds, s, p);
+  const bool append = p.positions != nullptr;
+  if (p.pool.head_dim == 128) {
+    if (append) launch_one<128, true>(p, wgs, lds, s); else launch_one<128, false>(p, wgs, lds, s);
+  } else {
+    if (append) launch_one<64, true>(p, wgs, lds, s); else launch_one<64, false>(p, wgs, lds, s);
+  }
   return hipGetLastError();
 }
 

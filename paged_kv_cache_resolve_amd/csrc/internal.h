@@ -88,6 +88,13 @@ struct DecodeParams {
                           // number that receives work is derived on device
   int min_chunks;         // minimum chunks per unit
   pagedkv_dtype_t dtype;  // element type of pool, q and out
+  // Fused append (all null for a plain decode): the new token of sequence b
+  // sits at position positions[b] (negative = none).  Pass 1 reads its K/V
+  // rows from k_new / v_new ([batch][kv_heads][head_dim]) instead of the
+  // pool, and the merge pass writes them into the pool afterwards.
+  const void* k_new;
+  const void* v_new;
+  const int32_t* positions;
 };
 
 constexpr int kMaxWaves = 8192;          // upper bound on wavefronts (256 CUs x 32)

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(L, n), f"{n} missing from libpagedkv.so"
     assert set(names) == set(_lib.SIGNATURES), "binding signatures drift from the header"
@@ -151,6 +151,15 @@ def test_entry_points_validate_before_launch():
     assert dec(ws=None) == _lib.ERR_WORKSPACE
     assert dec(ws=ctypes.c_void_p(p.value + 64)) == _lib.ERR_WORKSPACE  # misaligned
     assert dec(batch=0) == 0                                            # nothing to do
+    fused = lambda **kw: L.paged_attention_decode_append(  # noqa: E731
+        p, p, kw.get("k", p), kw.get("v", p), kw.get("pos", p), h, kw.get("layer", 0), p, 4, p,
+        kw.get("batch", 4), 8, ctypes.c_float(0.125), p, kw.get("wsb", ws_bytes), None)
+    assert fused(k=None) == _lib.ERR_INVALID_ARG
+    assert fused(v=None) == _lib.ERR_INVALID_ARG
+    assert fused(pos=None) == _lib.ERR_INVALID_ARG
+    assert fused(layer=2) == _lib.ERR_INVALID_ARG
+    assert fused(wsb=ws_bytes - 1) == _lib.ERR_WORKSPACE
+    assert fused(batch=0, k=None, v=None, pos=None) == 0
     assert L.kv_append(h, 2, p, p, p, 4, p, 4, None) == _lib.ERR_INVALID_ARG
     assert L.kv_append(h, 0, None, p, p, 4, p, 4, None) == _lib.ERR_INVALID_ARG
     assert L.kv_append(h, 0, p, p, p, 4, p, 0, None) == 0
