@@ -206,6 +206,8 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (use_mfma) {
+    // (the merge kernel stores each new row with one 16-byte unit per lane)
+    if (append && 2 * pool->head_dim * elem_size(pool->dtype) > 64 * 16) return PAGEDKV_ERR_UNSUPPORTED;
     if (append) {
       p.k_new = k_new;
       p.v_new = v_new;

@@ -44,39 +44,49 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   const int hn = h - g * G;
   TS* out = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + h) * D;
 
-  if (p.positions != nullptr && hn == 0) {
-    // the first wave of each (b, g) writes the new token of that KV head
-    const int pos = p.positions[b];
-    if (pos >= 0) {
-      const int units = D * (int)sizeof(TS) / 16;   // 16-byte units per row
-      const int phys = p.block_tables[(int64_t)b * p.max_blocks_per_seq + pos / p.pool.block_size];
-      const int64_t row = (int64_t)phys * p.pool.block_stride + (int64_t)p.layer * p.pool.layer_stride +
-                          (int64_t)g * p.pool.head_stride +
-                          (int64_t)(pos % p.pool.block_size) * D;
-      const int64_t src = ((int64_t)b * H + g) * D;
-      for (int i = lane; i < 2 * units; i += 64) {
-        const int kv = i >= units;
-        const int u = i - kv * units;
-        const uint4* from = reinterpret_cast<const uint4*>(
-            static_cast<const TS*>(kv ? p.v_new : p.k_new) + src);
-        uint4* to = reinterpret_cast<uint4*>(
-            reinterpret_cast<TS*>(const_cast<char*>(p.pool.base)) + row + kv * p.pool.kv_stride);
-        to[u] = from[u];
-      }
-    }
+  // Independent loads first: the sequence's chunk range and, for a fused
+  // append, its position and the new K/V row (one 16-byte unit per lane;
+  // fused appends come with head_dim * element size <= 256 bytes, so one
+  // pass of 64 lanes covers both rows).
+  const bool app = p.positions != nullptr && hn == 0;
+  const int units = D * (int)sizeof(TS) / 16;   // 16-byte units per row
+  const int kv = lane >= units;
+  const int u = lane - kv * units;
+  int pos = -1;
+  uint4 row_unit = make_uint4(0, 0, 0, 0);
+  if (app) {
+    pos = p.positions[b];
+    if (lane < 2 * units)
+      row_unit = reinterpret_cast<const uint4*>(static_cast<const TS*>(kv ? p.v_new : p.k_new) +
+                                                ((int64_t)b * H + g) * D)[u];
   }
-
   const int pb = p.ws_prefix[b];
   const int nb = p.ws_prefix[b + 1] - pb;
   const int64_t C = p.ws_prefix[p.batch];
+  // the first wave of each (b, g) stores the new token of that KV head; the
+  // store is made at every exit so that the table load overlaps the merge
+  const bool store_row = app && pos >= 0 && lane < 2 * units;
+  const int phys =
+      store_row ? p.block_tables[(int64_t)b * p.max_blocks_per_seq + pos / p.pool.block_size] : 0;
+  auto append_row = [&]() {
+    if (!store_row) return;
+    const int64_t row = (int64_t)phys * p.pool.block_stride + (int64_t)p.layer * p.pool.layer_stride +
+                        (int64_t)g * p.pool.head_stride + (int64_t)(pos % p.pool.block_size) * D;
+    reinterpret_cast<uint4*>(reinterpret_cast<TS*>(const_cast<char*>(p.pool.base)) + row +
+                             kv * p.pool.kv_stride)[u] = row_unit;
+  };
   if (nb == 0) {
     for (int d = lane; d < D; d += 64) out[d] = out_cast<TS>(0.f);
+    append_row();
     return;
   }
   const int64_t Ue = waves_eff(C, p.units, p.min_chunks);
   const int64_t uf = wave_of_chunk(pb, C, Ue);
   const int64_t ul = wave_of_chunk(pb + nb - 1, C, Ue);
-  if (uf == ul) return;   // one unit saw the whole sequence and wrote `out`
+  if (uf == ul) {   // one unit saw the whole sequence and wrote `out`
+    append_row();
+    return;
+  }
   const int K = (int)(ul - uf + 1);
 
   // partials of (b, g) from units uf..ul sit kv_heads slots apart
@@ -121,6 +131,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
     const int d = lane + 64 * i;
     if (d < D) out[d] = out_cast<TS>(a[i] * inv);
   }
+  append_row();
 }
 
 }  // namespace
