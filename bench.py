@@ -37,12 +37,12 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "ab046a43a16a225431b28367a12e03c211a21061357545731a11ccaa6c21cd5c",
-        "bytes": 585279804,
+        "kernel_sha256": "ecd03e9d8b6329bc71246ad302385f2811e9b6d11e118adcf35dc58aaaa0740a",
+        "bytes": 585427132,
     },
     "long_context_bf16": {
-        "kernel_sha256": "ab046a43a16a225431b28367a12e03c211a21061357545731a11ccaa6c21cd5c",
-        "bytes": 2210701425,
+        "kernel_sha256": "ecd03e9d8b6329bc71246ad302385f2811e9b6d11e118adcf35dc58aaaa0740a",
+        "bytes": 2210760850,
     },
 }
 

@@ -12,6 +12,8 @@
 //   * online softmax per head with wavefront max/sum reductions;
 //   * weighted V sum: lane owns dims lane, lane+64, ...; token rows are
 //     walked in order with addresses broadcast by v_readlane.
+// Loads are issued in batches (16 K pieces per lane, then 32 / DPL V rows)
+// so that a chunk costs a few memory round trips, not one per load.
 
 #include <math.h>
 
@@ -22,6 +24,7 @@ namespace pagedkv {
 namespace {
 
 constexpr int kGenDimsPerLane = 4;   // head_dim <= 256
+constexpr int kKBatch = 16;          // 4-element K pieces per lane in flight
 
 template <typename TS> __device__ __forceinline__ float to_f32(TS x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
@@ -53,9 +56,11 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-template <typename TS>
-__device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int lane,
+// DPL = dims per lane in the V sum (head_dim <= 64 * DPL).
+template <typename TS, int DPL>
+__device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int lane,
                                 int64_t unit, int b, int g, int j0, int j1, int nb) {
+  constexpr int VB = 32 / DPL;   // V rows in flight per batch
   const int G = p.group;
   const int D = p.pool.head_dim;
   const int BS = p.pool.block_size;
@@ -69,14 +74,14 @@ __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int
   for (int i = lane; i < G * D; i += 64) qs[i] = to_f32<TS>(q[i]) * p.scale_log2;
   __syncthreads();
 
-  float acc[kMaxGroup][kGenDimsPerLane];
+  float acc[kMaxGroup][DPL];
   float m[kMaxGroup], l[kMaxGroup];
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     m[h] = -INFINITY;
     l[h] = 0.f;
 #pragma unroll
-    for (int i = 0; i < kGenDimsPerLane; ++i) acc[h][i] = 0.f;
+    for (int i = 0; i < DPL; ++i) acc[h][i] = 0.f;
   }
 
   for (int j = j0; j < j1; ++j) {
@@ -90,14 +95,23 @@ __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int
     float s[kMaxGroup];
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) s[h] = 0.f;
-    if (valid) {
-      for (int d = 0; d < D; d += 4) {
-        const float4 k = load4(pool + row + d);
+    for (int d0 = 0; d0 < D; d0 += 4 * kKBatch) {
+      float4 kk[kKBatch];
 #pragma unroll
-        for (int h = 0; h < kMaxGroup; ++h) {
-          if (h < G) {
-            const float4 qq = *reinterpret_cast<const float4*>(qs + h * D + d);
-            s[h] += qq.x * k.x + qq.y * k.y + qq.z * k.z + qq.w * k.w;
+      for (int u = 0; u < kKBatch; ++u) {
+        const int d = d0 + 4 * u;
+        kk[u] = valid && d < D ? load4(pool + row + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int u = 0; u < kKBatch; ++u) {
+        const int d = d0 + 4 * u;
+        if (d < D) {
+#pragma unroll
+          for (int h = 0; h < kMaxGroup; ++h) {
+            if (h < G) {
+              const float4 qq = *reinterpret_cast<const float4*>(qs + h * D + d);
+              s[h] += qq.x * kk[u].x + qq.y * kk[u].y + qq.z * kk[u].z + qq.w * kk[u].w;
+            }
           }
         }
       }
@@ -112,7 +126,7 @@ __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int
         l[h] = l[h] * alpha + wave_sum(pv);
         m[h] = mn;
 #pragma unroll
-        for (int i = 0; i < kGenDimsPerLane; ++i) acc[h][i] *= alpha;
+        for (int i = 0; i < DPL; ++i) acc[h][i] *= alpha;
         ps[h * 64 + lane] = pv;
       }
     }
@@ -120,31 +134,30 @@ __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int
     const int ntok = min(64, T - j * kGenericChunk);
     const uint32_t row_lo = (uint32_t)(row & 0xffffffffu);
     const uint32_t row_hi = (uint32_t)(row >> 32);
-    // V rows 16 at a time: the 16 loads of a batch are independent, so they
-    // are in flight together instead of one round trip per token.
-    for (int t0 = 0; t0 < ntok; t0 += 16) {
-      float v[16][kGenDimsPerLane];
+    // V rows VB at a time: the loads of a batch are independent, so they are
+    // in flight together instead of one round trip per token.
+    for (int t0 = 0; t0 < ntok; t0 += VB) {
+      float v[VB][DPL];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
+      for (int u = 0; u < VB; ++u) {
         const int t = min(t0 + u, ntok - 1);   // repeats past ntok are skipped below
         const int64_t r = ((int64_t)(uint32_t)__builtin_amdgcn_readlane((int)row_hi, t) << 32) |
                           (uint32_t)__builtin_amdgcn_readlane((int)row_lo, t);
         const TS* vrow = pool + r + p.pool.kv_stride;
 #pragma unroll
-        for (int i = 0; i < kGenDimsPerLane; ++i) {
+        for (int i = 0; i < DPL; ++i) {
           const int d = lane + 64 * i;
           v[u][i] = d < D ? to_f32<TS>(vrow[d]) : 0.f;
         }
       }
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        if (t0 + u >= ntok) break;
+      for (int u = 0; u < VB; ++u) {
 #pragma unroll
         for (int h = 0; h < kMaxGroup; ++h)
-          if (h < G) {
+          if (h < G && t0 + u < ntok) {
             const float pw = ps[h * 64 + t0 + u];
 #pragma unroll
-            for (int i = 0; i < kGenDimsPerLane; ++i) acc[h][i] += pw * v[u][i];
+            for (int i = 0; i < DPL; ++i) acc[h][i] += pw * v[u][i];
           }
       }
     }
@@ -160,14 +173,14 @@ __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int
       TS* o = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + (int64_t)g * G + h) * D;
       const float inv = 1.0f / l[h];
 #pragma unroll
-      for (int i = 0; i < kGenDimsPerLane; ++i) {
+      for (int i = 0; i < DPL; ++i) {
         const int d = lane + 64 * i;
         if (d < D) o[d] = from_f32<TS>(acc[h][i] * inv);
       }
     } else {
       float* o = p.ws_o + (slot * G + h) * D;
 #pragma unroll
-      for (int i = 0; i < kGenDimsPerLane; ++i) {
+      for (int i = 0; i < DPL; ++i) {
         const int d = lane + 64 * i;
         if (d < D) o[d] = acc[h][i];
       }
@@ -179,7 +192,7 @@ __device__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int
   }
 }
 
-template <typename TS>
+template <typename TS, int DPL>
 __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeParams p) {
   extern __shared__ int32_t lds[];
   __shared__ int32_t scan[64];
@@ -209,7 +222,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeParams p) {
     const int j0 = (int)(c - pb);
     const int64_t left = c_end - c;
     const int j1 = left < (int64_t)(nb - j0) ? j0 + (int)left : nb;
-    generic_segment<TS>(p, qs, ps, lane, unit, b, g, j0, j1, nb);
+    generic_segment<TS, DPL>(p, qs, ps, lane, unit, b, g, j0, j1, nb);
     __syncthreads();
     c += j1 - j0;
     if (j1 == nb) {
@@ -231,8 +244,9 @@ hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
   const size_t lds = sizeof(int32_t) * pre_words +
                      sizeof(float) * (size_t)p.group * (p.pool.head_dim + 64);
   const bool f32 = p.dtype == PAGEDKV_F32;
-  const void* fn = f32 ? reinterpret_cast<const void*>(&decode_generic_kernel<float>)
-                       : reinterpret_cast<const void*>(&decode_generic_kernel<uint16_t>);
+  const int dpl = p.pool.head_dim <= 64 ? 1 : p.pool.head_dim <= 128 ? 2 : 4;
+  const void* fn = f32 ? reinterpret_cast<const void*>(&decode_generic_kernel<float, 4>)
+                       : reinterpret_cast<const void*>(&decode_generic_kernel<uint16_t, 4>);
   int wgs = 0;
   hipError_t e = resident_workgroups(fn, 64, lds, &wgs);
   if (e != hipSuccess) return e;
@@ -252,10 +266,16 @@ hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
     p.units = (int)(useful < 1 ? 1 : useful);
     waves = p.units * p.pool.kv_heads;
   }
-  if (f32)
-    hipLaunchKernelGGL(decode_generic_kernel<float>, dim3(waves), dim3(64), lds, s, p);
-  else
-    hipLaunchKernelGGL(decode_generic_kernel<uint16_t>, dim3(waves), dim3(64), lds, s, p);
+  const dim3 grid(waves), block(64);
+  if (f32) {
+    if (dpl == 1) hipLaunchKernelGGL((decode_generic_kernel<float, 1>), grid, block, lds, s, p);
+    else if (dpl == 2) hipLaunchKernelGGL((decode_generic_kernel<float, 2>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((decode_generic_kernel<float, 4>), grid, block, lds, s, p);
+  } else {
+    if (dpl == 1) hipLaunchKernelGGL((decode_generic_kernel<uint16_t, 1>), grid, block, lds, s, p);
+    else if (dpl == 2) hipLaunchKernelGGL((decode_generic_kernel<uint16_t, 2>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((decode_generic_kernel<uint16_t, 4>), grid, block, lds, s, p);
+  }
   return hipGetLastError();
 }
 
