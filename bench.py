@@ -37,12 +37,12 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "ecd03e9d8b6329bc71246ad302385f2811e9b6d11e118adcf35dc58aaaa0740a",
-        "bytes": 585427132,
+        "kernel_sha256": "33602a10b4bcb0a8acf42f105b002d3b9fabf6a803a4403bc952e5d8b0710723",
+        "bytes": 585622904,
     },
     "long_context_bf16": {
-        "kernel_sha256": "ecd03e9d8b6329bc71246ad302385f2811e9b6d11e118adcf35dc58aaaa0740a",
-        "bytes": 2210760850,
+        "kernel_sha256": "33602a10b4bcb0a8acf42f105b002d3b9fabf6a803a4403bc952e5d8b0710723",
+        "bytes": 2210910225,
     },
 }
 

@@ -78,8 +78,9 @@ __global__ __launch_bounds__(256) void gather_kernel(PoolGeom pool, int layer, i
                                (int64_t)g * pool.head_stride + (int64_t)(t % pool.block_size) * pool.head_dim;
       const u32x4_t* ks = reinterpret_cast<const u32x4_t*>(pool.base + src_elem * elem);
       const u32x4_t* vs = reinterpret_cast<const u32x4_t*>(pool.base + (src_elem + pool.kv_stride) * elem);
-      kk = ks[u];
-      vv = vs[u];
+      // each pool row is read once: non-temporal loads keep it out of the caches
+      kk = __builtin_nontemporal_load(ks + u);
+      vv = __builtin_nontemporal_load(vs + u);
     }
     const int64_t dst = (((int64_t)b * max_len + t) * H + g) * row_bytes;
     __builtin_nontemporal_store(kk, reinterpret_cast<u32x4_t*>(k_out + dst) + u);

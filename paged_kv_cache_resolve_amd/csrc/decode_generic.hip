@@ -37,12 +37,22 @@ template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
 
-// Four consecutive elements as floats (16-byte or 8-byte load).
-__device__ __forceinline__ float4 load4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+// Four consecutive K elements as floats (16-byte or 8-byte load).  K and V
+// are streamed once, so their loads are non-temporal.
+typedef float f32x4_nt __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float4 load4(const float* p) {
+  const f32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_nt*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
 __device__ __forceinline__ float4 load4(const uint16_t* p) {
-  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  const u32x2_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p));
   return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
                      __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
+}
+__device__ __forceinline__ float load1(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float load1(const uint16_t* p) {
+  return __uint_as_float((uint32_t)__builtin_nontemporal_load(p) << 16);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
@@ -147,7 +157,7 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
 #pragma unroll
         for (int i = 0; i < DPL; ++i) {
           const int d = lane + 64 * i;
-          v[u][i] = d < D ? to_f32<TS>(vrow[d]) : 0.f;
+          v[u][i] = d < D ? load1(vrow + d) : 0.f;
         }
       }
 #pragma unroll
