@@ -4,7 +4,8 @@ A step is one pass of the decode hot path over one batch, for one layer: each
 sequence's new token K/V goes into its tail block and paged-attention decode
 runs over the cache (block-table resolve, K/V stream, scaled QK^T, online
 softmax, PV, split merge, output write), both in one library call
-(paged_attention_decode_append).  The batched paged-KV gather is timed
+(paged_attention_decode_append, issued through a DecodePlan: the step's
+buffers are fixed, so they are checked once).  The batched paged-KV gather is timed
 separately and reported beside the step.
 
     python bench.py [--workload llama8b_decode_bf16] [--steps K] [--warmup W]
@@ -184,13 +185,14 @@ def main(argv=None) -> int:
             lens=torch.from_numpy(w.context_lens).cuda(),
             pos=torch.from_numpy(w.positions).cuda(), q=dev(w.q), k=dev(w.k_new), v=dev(w.v_new),
             out=torch.empty(w.S, w.Hq, w.D, dtype=tdt, device="cuda")))
+        r = reps_dev[-1]
+        # the step's buffers are fixed, so a plan checks them once
+        r["plan"] = pk.DecodePlan(r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"],
+                                  w.scale, r["k"], r["v"], r["pos"])
     stream = torch.cuda.current_stream()
 
     def step(i):
-        r = reps_dev[i % len(reps_dev)]
-        w = r["w"]
-        pk.paged_attention_decode_append(r["out"], r["q"], r["pool"], w.layer, r["tables"],
-                                         r["lens"], w.scale, r["k"], r["v"], r["pos"])
+        reps_dev[i % len(reps_dev)]["plan"].run()
 
     def ev_pair():
         return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

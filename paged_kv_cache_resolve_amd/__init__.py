@@ -27,7 +27,7 @@ _L = _lib.load()
 
 __all__ = [
     "KVPool", "kv_pool_create", "kv_append", "paged_kv_gather", "paged_attention_decode",
-    "paged_attention_decode_append",
+    "paged_attention_decode_append", "DecodePlan",
     "paged_attention_workspace_bytes", "paged_kv_resolve", "PagedKVError", "OutOfBlocksError",
     "library",
 ]
@@ -48,22 +48,28 @@ def _check(status: int, what: str) -> None:
     raise PagedKVError(status, what, _L)
 
 
-def _stream(device: torch.device) -> ctypes.c_void_p:
-    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+# The checks below run on every call, so they use the cheapest tensor
+# queries (device index as an int, torch.Size compared as a tuple) and hand
+# ctypes plain integers for pointers.
+
+def _stream(device: torch.device) -> int:
+    """The current HIP stream of `device`, as an integer handle."""
+    return torch.cuda.current_stream(device).cuda_stream
 
 
-def _dev_tensor(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=None):
+def _dev_tensor(t: torch.Tensor, name: str, device: torch.device, dtype=None, shape=None) -> int:
+    """Check a tensor argument and return its device address."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device != device:
+    if not t.is_cuda or t.get_device() != device.index:
         raise ValueError(f"{name} is on {t.device}, expected {device}")
     if dtype is not None and t.dtype != dtype:
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    if shape is not None and t.shape != shape:
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
-    return ctypes.c_void_p(t.data_ptr())
+    return t.data_ptr()
 
 
 class KVPool:
@@ -86,7 +92,7 @@ class KVPool:
             data = torch.zeros(shape, dtype=dtype, device=device)
         if data.device.type != "cuda":
             raise ValueError("the pool must live in GPU memory")
-        self.device = data.device
+        self.device = torch.device("cuda", data.get_device())
         _dev_tensor(data, "data", self.device, dtype, shape)
         self.data = data
         self._handle = ctypes.c_void_p()
@@ -115,7 +121,8 @@ class KVPool:
 
     def __del__(self):
         h = getattr(self, "_handle", None)
-        if h is not None and h.value:
+        # at interpreter exit the module globals may already be cleared
+        if h is not None and h.value and _L is not None:
             _L.kv_pool_destroy(h)
             self._handle = ctypes.c_void_p()
 
@@ -171,18 +178,25 @@ def paged_kv_gather(pool: KVPool, layer: int, block_tables: torch.Tensor,
     return k, v, mask
 
 
+_WS_BYTES: dict = {}
+
+
 def paged_attention_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int) -> int:
-    n = _L.paged_attention_workspace_bytes(pool.handle, batch, num_q_heads)
-    if n == 0 and batch >= 0:
-        raise PagedKVError(_lib.ERR_INVALID_ARG, "paged_attention_workspace_bytes", _L)
+    key = (pool.handle.value, pool.device.index, batch, num_q_heads)
+    n = _WS_BYTES.get(key)
+    if n is None:
+        n = _L.paged_attention_workspace_bytes(pool.handle, batch, num_q_heads)
+        if n == 0 and batch >= 0:
+            raise PagedKVError(_lib.ERR_INVALID_ARG, "paged_attention_workspace_bytes", _L)
+        _WS_BYTES[key] = n
     return n
 
 
 _WORKSPACES: dict = {}
 
 
-def _workspace(pool: KVPool, nbytes: int) -> torch.Tensor:
-    key = (pool.device, torch.cuda.current_stream(pool.device).cuda_stream)
+def _workspace(pool: KVPool, nbytes: int, stream: int) -> torch.Tensor:
+    key = (pool.device.index, stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=pool.device)
@@ -201,10 +215,11 @@ def _decode_args(out, q, pool, block_tables, context_lens, workspace):
     tp, mb = _tables_args(pool, block_tables, batch)
     lp = _dev_tensor(context_lens, "context_lens", pool.device, torch.int32, (batch,))
     need = paged_attention_workspace_bytes(pool, batch, hq)
+    stream = _stream(pool.device)
     if workspace is None:
-        workspace = _workspace(pool, need)
+        workspace = _workspace(pool, need, stream)
     wp = _dev_tensor(workspace, "workspace", pool.device, torch.uint8)
-    return batch, hq, qp, op, tp, mb, lp, wp, workspace.numel()
+    return batch, hq, qp, op, tp, mb, lp, wp, workspace.numel(), stream
 
 
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, pool: KVPool, layer: int,
@@ -214,11 +229,10 @@ def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, pool: KVPool, lay
     tokens of sequence b, resolved through its block table.  q and out are
     [batch, num_q_heads, head_dim] in the pool dtype.  A workspace is taken
     from a per-stream cache unless one is given."""
-    batch, hq, qp, op, tp, mb, lp, wp, wn = _decode_args(out, q, pool, block_tables,
-                                                         context_lens, workspace)
-    _check(_L.paged_attention_decode(op, qp, pool.handle, layer, tp, mb, lp, batch, hq,
-                                     ctypes.c_float(scale), wp, wn, _stream(pool.device)),
-           "paged_attention_decode")
+    batch, hq, qp, op, tp, mb, lp, wp, wn, stream = _decode_args(out, q, pool, block_tables,
+                                                                 context_lens, workspace)
+    _check(_L.paged_attention_decode(op, qp, pool.handle, layer, tp, mb, lp, batch, hq, scale,
+                                     wp, wn, stream), "paged_attention_decode")
     return out
 
 
@@ -231,17 +245,64 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, pool: KVPo
     by paged_attention_decode(out, q, ...), as one library call (the decode
     kernel reads the new rows from k_new / v_new where it can, saving the
     separate append launch)."""
-    batch, hq, qp, op, tp, mb, lp, wp, wn = _decode_args(out, q, pool, block_tables,
-                                                         context_lens, workspace)
+    batch, hq, qp, op, tp, mb, lp, wp, wn, stream = _decode_args(out, q, pool, block_tables,
+                                                                 context_lens, workspace)
     shape = (batch, pool.kv_heads, pool.head_dim)
     kp = _dev_tensor(k_new, "k_new", pool.device, pool.dtype, shape)
     vp = _dev_tensor(v_new, "v_new", pool.device, pool.dtype, shape)
     pp = _dev_tensor(positions, "positions", pool.device, torch.int32, (batch,))
     _check(_L.paged_attention_decode_append(op, qp, kp, vp, pp, pool.handle, layer, tp, mb, lp,
-                                            batch, hq, ctypes.c_float(scale), wp, wn,
-                                            _stream(pool.device)),
+                                            batch, hq, scale, wp, wn, stream),
            "paged_attention_decode_append")
     return out
+
+
+class DecodePlan:
+    """A decode step whose tensors are fixed: they are checked once here, and
+    run() only passes their addresses and the current stream to the library.
+    For loops that reuse the same buffers every step (update their contents
+    in place).  With k_new, v_new and positions the step is
+    paged_attention_decode_append, otherwise paged_attention_decode.  The
+    plan holds references to the tensors, so their storage stays alive."""
+
+    def __init__(self, out: torch.Tensor, q: torch.Tensor, pool: KVPool, layer: int,
+                 block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                 k_new: torch.Tensor | None = None, v_new: torch.Tensor | None = None,
+                 positions: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+        append = k_new is not None or v_new is not None or positions is not None
+        if append and (k_new is None or v_new is None or positions is None):
+            raise ValueError("k_new, v_new and positions go together")
+        batch, hq, qp, op, tp, mb, lp, wp, wn, stream = _decode_args(out, q, pool, block_tables,
+                                                                     context_lens, workspace)
+        self.pool = pool
+        self._keep = (out, q, block_tables, context_lens, k_new, v_new, positions,
+                      workspace if workspace is not None else _workspace(pool, wn, stream))
+        self._device = pool.device
+        # the shared per-stream workspace may only be used on its own stream
+        self._stream = None if workspace is not None else stream
+        if append:
+            shape = (batch, pool.kv_heads, pool.head_dim)
+            kp = _dev_tensor(k_new, "k_new", pool.device, pool.dtype, shape)
+            vp = _dev_tensor(v_new, "v_new", pool.device, pool.dtype, shape)
+            pp = _dev_tensor(positions, "positions", pool.device, torch.int32, (batch,))
+            self._fn = _L.paged_attention_decode_append
+            self._args = (op, qp, kp, vp, pp, pool.handle, layer, tp, mb, lp, batch, hq,
+                          float(scale), wp, wn)
+            self._what = "paged_attention_decode_append"
+        else:
+            self._fn = _L.paged_attention_decode
+            self._args = (op, qp, pool.handle, layer, tp, mb, lp, batch, hq, float(scale), wp, wn)
+            self._what = "paged_attention_decode"
+
+    def run(self) -> torch.Tensor:
+        """Enqueue the step on the current stream; returns `out`.  Without an
+        explicit workspace the plan uses the stream's cached one, so it must
+        run on the stream that was current when it was built."""
+        stream = torch.cuda.current_stream(self._device).cuda_stream
+        if self._stream is not None and stream != self._stream:
+            raise RuntimeError("DecodePlan built on another stream; pass a workspace to share it")
+        _check(self._fn(*self._args, stream), self._what)
+        return self._keep[0]
 
 
 def paged_kv_resolve(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,

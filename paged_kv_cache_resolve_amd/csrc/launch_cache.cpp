@@ -3,6 +3,7 @@
 
 #include <stdlib.h>
 
+#include <atomic>
 #include <mutex>
 #include <unordered_map>
 
@@ -61,16 +62,37 @@ hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out
   return hipSuccess;
 }
 
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cus[kMaxDevices];   // CU count per device, 0 = not yet queried
+
+// CUs of the current device (0 if the runtime cannot tell), queried once.
+int device_cus() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (dev < 0 || dev >= kMaxDevices) {
+    int cus = 0;
+    return hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess
+               ? cus : 0;
+  }
+  int cus = g_cus[dev].load(std::memory_order_relaxed);
+  if (cus == 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return 0;
+    g_cus[dev].store(cus, std::memory_order_relaxed);
+  }
+  return cus;
+}
+}  // namespace
+
 int decode_workgroups(int resident) {
   static const int per_cu = [] {
     const char* v = getenv("PAGEDKV_DECODE_WG_PER_CU");
     const int x = v ? atoi(v) : 0;
     return x > 0 ? x : kDecodeWgPerCu;
   }();
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return resident;
+  const int cus = device_cus();
+  if (cus <= 0) return resident;
   const int want = cus * per_cu;
   int n = want < resident ? want : resident;
   if (n > kMaxWaves / 4) n = kMaxWaves / 4;

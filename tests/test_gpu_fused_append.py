@@ -146,3 +146,34 @@ def test_fused_step_full_size_llama8b():
     pk.paged_attention_decode(out2, dw.q, dw.pool, w.layer, dw.tables, dw.lens, w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+
+
+def test_decode_plan_matches_direct_calls():
+    """DecodePlan runs the same library calls on fixed tensors: bit-identical
+    to the direct calls in deterministic settings (same kernels, same split)."""
+    say("decode plan vs direct calls")
+    w = make_workload(2, S=6)
+    positions = w.positions.copy()
+    a = DeviceWorkload(w)
+    b = DeviceWorkload(w)
+    out_a = torch.empty_like(a.q)
+    out_b = torch.empty_like(b.q)
+    pos_a = torch.from_numpy(positions).cuda()
+    pos_b = torch.from_numpy(positions).cuda()
+    plan = pk.DecodePlan(out_a, a.q, a.pool, w.layer, a.tables, a.lens, w.scale,
+                         a.k_new, a.v_new, pos_a)
+    plan.run()
+    pk.paged_attention_decode_append(out_b, b.q, b.pool, w.layer, b.tables, b.lens, w.scale,
+                                     b.k_new, b.v_new, pos_b)
+    torch.cuda.synchronize()
+    assert dev_to_np(out_a).tobytes() == dev_to_np(out_b).tobytes()
+    assert dev_to_np(a.pool.data).tobytes() == dev_to_np(b.pool.data).tobytes()
+    plain = pk.DecodePlan(out_a, a.q, a.pool, w.layer, a.tables, a.lens, w.scale)
+    plain.run()
+    pk.paged_attention_decode(out_b, b.q, b.pool, w.layer, b.tables, b.lens, w.scale)
+    torch.cuda.synchronize()
+    assert dev_to_np(out_a).tobytes() == dev_to_np(out_b).tobytes()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        with pytest.raises(RuntimeError):
+            plain.run()
