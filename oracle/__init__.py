@@ -16,6 +16,8 @@ Parity status per function:
                                        encoded pool, contiguous equivalence)
   kv_append                            pinned (hand-derived fixture,
                                        whole-pool diff, gather round trip)
+  kv_append_layers, kv_append_tokens   pinned (hand-derived fixtures; equal
+                                       to per-layer / per-token kv_append)
   attend, paged_attention_decode       pinned (torch SDPA in float64,
                                        brute force, closed forms, invariants)
   waste arithmetic                     pinned (the page's worked numbers)
@@ -28,6 +30,8 @@ from .paged import (  # noqa: F401
     attend,
     gather_sequence,
     kv_append,
+    kv_append_layers,
+    kv_append_tokens,
     kv_head_of,
     logical_to_physical,
     naive_waste_ratio,

@@ -166,6 +166,51 @@ def kv_append(pool: np.ndarray, layer: int, block_tables: np.ndarray,
     return out
 
 
+def kv_append_layers(pool: np.ndarray, block_tables: np.ndarray, positions: np.ndarray,
+                     k_new: np.ndarray, v_new: np.ndarray, *, in_place: bool = False
+                     ) -> np.ndarray:
+    """One token per sequence for every layer at once: k_new and v_new are
+    [S, L, Hkv, D]; layer l of sequence b goes where kv_append(layer=l)
+    would put it.  A negative position leaves that sequence untouched.
+
+    [mini-infer] "The Solution" (a physical block holds B tokens of K and V
+    for all layers, so one slot serves every layer of a token).
+    """
+    out = pool if in_place else pool.copy()
+    for layer in range(pool.shape[2]):
+        kv_append(out, layer, block_tables, positions, k_new[:, layer], v_new[:, layer],
+                  in_place=True)
+    return out
+
+
+def kv_append_tokens(pool: np.ndarray, layer: int, block_tables: np.ndarray,
+                     start_positions: np.ndarray, token_offsets: np.ndarray,
+                     k_new: np.ndarray, v_new: np.ndarray, *, in_place: bool = False
+                     ) -> np.ndarray:
+    """Several consecutive tokens per sequence (a prompt, or a chunk of one):
+    rows token_offsets[b] .. token_offsets[b+1]-1 of k_new / v_new ([N, Hkv,
+    D]) are the tokens of sequence b, and row token_offsets[b] + i goes to
+    logical position start_positions[b] + i, resolved through the block
+    table.  A negative start position leaves that sequence untouched.
+
+    [kv-cache] section 2 (a prompt fills whole blocks, only the last one is
+    partly filled); [vllmini] "PagedAttention Metaphor" (logical positions
+    resolve to physical slots through the table).
+    """
+    out = pool if in_place else pool.copy()
+    block_size = pool.shape[4]
+    for b in range(len(start_positions)):
+        start = int(start_positions[b])
+        if start < 0:
+            continue
+        for row in range(int(token_offsets[b]), int(token_offsets[b + 1])):
+            t = start + row - int(token_offsets[b])
+            phys, off = logical_to_physical(block_tables[b], t, block_size)
+            out[phys, 0, layer, :, off, :] = k_new[row]
+            out[phys, 1, layer, :, off, :] = v_new[row]
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Attention
 # ----------------------------------------------------------------------------

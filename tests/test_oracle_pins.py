@@ -255,6 +255,61 @@ def check_append_fixture():
     assert not pool.any()   # not in place by default
 
 
+def check_append_layers_fixture():
+    pool = np.zeros((8, 2, 2, 2, 4, 2), np.float32)
+    table = np.array([[4, 1, 7]], np.int32)
+    k_new = np.array([[[[1, 2], [3, 4]], [[9, 10], [11, 12]]]], np.float32)
+    v_new = np.array([[[[5, 6], [7, 8]], [[13, 14], [15, 16]]]], np.float32)
+    out = oracle.kv_append_layers(pool, table, np.array([6], np.int32), k_new, v_new)
+    flat = out.reshape(-1)
+    expected = {int(i): float(v) for i, v in read_golden("append_layers_example.txt")}
+    nz = {int(i): float(flat[i]) for i in np.flatnonzero(flat)}
+    assert nz == expected, (nz, expected)
+    assert not pool.any()
+
+
+def check_append_tokens_fixture():
+    pool = np.zeros((8, 2, 1, 1, 2, 1), np.float32)
+    tables = np.array([[3, 5], [6, 2]], np.int32)
+    k_new = np.array([1, 2, 3, 4, 5], np.float32).reshape(5, 1, 1)
+    v_new = k_new + 10
+    out = oracle.kv_append_tokens(pool, 0, tables, np.array([1, 0], np.int32),
+                                  np.array([0, 3, 5], np.int32), k_new, v_new)
+    flat = out.reshape(-1)
+    expected = {int(i): float(v) for i, v in read_golden("append_tokens_example.txt")}
+    nz = {int(i): float(flat[i]) for i in np.flatnonzero(flat)}
+    assert nz == expected, (nz, expected)
+    assert not pool.any()
+
+
+def check_multi_appends_equal_single_appends():
+    """The all-layer append equals one kv_append per layer, and the prompt
+    append equals one kv_append per token offset."""
+    rng = np.random.default_rng(23)
+    NB, L, H, BS, D, S = 24, 3, 2, 4, 3, 3
+    pool = rng.standard_normal((NB, 2, L, H, BS, D)).astype(np.float32)
+    tables = rng.permutation(NB)[:S * 6].reshape(S, 6).astype(np.int32)
+    pos = np.array([5, -1, 17], np.int32)
+    k_l = rng.standard_normal((S, L, H, D)).astype(np.float32)
+    v_l = rng.standard_normal((S, L, H, D)).astype(np.float32)
+    ref = pool.copy()
+    for layer in range(L):
+        ref = oracle.kv_append(ref, layer, tables, pos, k_l[:, layer], v_l[:, layer])
+    assert oracle.kv_append_layers(pool, tables, pos, k_l, v_l).tobytes() == ref.tobytes()
+    starts = np.array([0, 7, -2], np.int32)
+    counts = np.array([9, 4, 3], np.int32)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    k_t = rng.standard_normal((int(offs[-1]), H, D)).astype(np.float32)
+    v_t = rng.standard_normal((int(offs[-1]), H, D)).astype(np.float32)
+    ref = pool.copy()
+    for i in range(int(counts.max())):
+        p_i = np.where((starts >= 0) & (i < counts), starts + i, -1).astype(np.int32)
+        rows = np.minimum(offs[:-1] + i, offs[-1] - 1)
+        ref = oracle.kv_append(ref, 2, tables, p_i, k_t[rows], v_t[rows])
+    got = oracle.kv_append_tokens(pool, 2, tables, starts, offs, k_t, v_t)
+    assert got.tobytes() == ref.tobytes()
+
+
 def check_append_then_gather():
     rng = np.random.default_rng(17)
     c = _random_paged_case(rng, S=4, Hq=2, Hkv=2, D=4, BS=4, L=2, layer=1, max_T=13,
@@ -324,6 +379,9 @@ ALL_CHECKS = [
     ("block_permutation_invariance", check_block_permutation_invariance),
     ("append_fixture", check_append_fixture),
     ("append_then_gather", check_append_then_gather),
+    ("append_layers_fixture", check_append_layers_fixture),
+    ("append_tokens_fixture", check_append_tokens_fixture),
+    ("multi_appends_equal_single_appends", check_multi_appends_equal_single_appends),
     ("waste_examples", check_waste_examples),
     ("free_stack", check_free_stack),
     ("widen", check_widen),
@@ -394,6 +452,22 @@ def _mut_append_next_slot(pool, layer, block_tables, positions, k_new, v_new, *,
     return out
 
 
+_orig_append_tokens = P.kv_append_tokens
+
+
+def _mut_append_tokens_shifted(pool, layer, block_tables, start_positions, token_offsets, k_new,
+                               v_new, *, in_place=False):
+    return _orig_append_tokens(pool, layer, block_tables, np.where(start_positions >= 0,
+                               start_positions + 1, start_positions), token_offsets, k_new, v_new,
+                               in_place=in_place)
+
+
+def _mut_append_layers_first_only(pool, block_tables, positions, k_new, v_new, *, in_place=False):
+    out = pool if in_place else pool.copy()
+    P.kv_append(out, 0, block_tables, positions, k_new[:, 0], v_new[:, 0], in_place=True)
+    return out
+
+
 def _mut_waste_floor(n, bs):
     return (n // bs) * bs - n + bs - 1 if n % bs else 0
 
@@ -415,6 +489,8 @@ MUTANTS = [
     ("gather_ignores_layer", "gather_sequence", _mut_gather_layer0),
     ("gather_kv_swapped", "gather_sequence", _mut_gather_kv_swapped),
     ("append_next_slot", "kv_append", _mut_append_next_slot),
+    ("append_tokens_shifted", "kv_append_tokens", _mut_append_tokens_shifted),
+    ("append_layers_first_only", "kv_append_layers", _mut_append_layers_first_only),
     ("waste_floor", "paged_waste_slots", _mut_waste_floor),
     ("widen_low_half", "widen", _mut_widen_low_half),
 ]
