@@ -6,7 +6,8 @@ runs over the cache (block-table resolve, K/V stream, scaled QK^T, online
 softmax, PV, split merge, output write), both in one library call
 (paged_attention_decode_append, issued through a DecodePlan: the step's
 buffers are fixed, so they are checked once).  The batched paged-KV gather is timed
-separately and reported beside the step.
+separately and reported beside the step, and so are the two multi-row appends
+(a prompt's tokens into one layer; one token into every layer).
 
     python bench.py [--workload llama8b_decode_bf16] [--steps K] [--warmup W]
 
@@ -93,6 +94,81 @@ def gather_bytes(w, max_len: int) -> int:
     return read + write
 
 
+def measure_appends(torch, pk, calls: int = 64) -> dict:
+    """The two multi-row appends on Llama-8B KV geometry (8 KV heads,
+    head_dim 128, block 16, bf16) in a 32-layer pool:
+
+    - prompt: kv_append_tokens of 64 prompts x 512 tokens into one layer
+      (rotating over the 32 layers and two input replicas, so neither the
+      rows nor the destination stay in the 256 MB Infinity Cache);
+    - decode: kv_append_layers of one token for 64 sequences in all 32
+      layers, beside the same rows written by 32 kv_append calls.
+
+    Algorithmic bytes: every new row read once and written once, plus the
+    int32 tables, start positions and offsets."""
+    S, T, L, Hkv, D, BS, e = 64, 512, 32, 8, 128, 16, 2
+    mb = T // BS
+    nb = S * mb
+    gen = torch.Generator(device="cpu").manual_seed(77)
+    pool_t = torch.empty(nb, 2, L, Hkv, BS, D, dtype=torch.bfloat16, device="cuda")
+    pool = pk.KVPool(nb, BS, L, Hkv, D, torch.bfloat16, data=pool_t)
+    tables = torch.randperm(nb, generator=gen).to(torch.int32).view(S, mb).cuda()
+    rows = S * T
+    reps = [(torch.randn(rows, Hkv, D, generator=gen).to(torch.bfloat16).cuda(),
+             torch.randn(rows, Hkv, D, generator=gen).to(torch.bfloat16).cuda())
+            for _ in range(2)]
+    starts = torch.zeros(S, dtype=torch.int32, device="cuda")
+    offsets = torch.arange(0, rows + 1, T, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, n):
+        fn(0)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    def prompt(i):
+        k, v = reps[i % 2]
+        pk.kv_append_tokens(pool, (i // 2) % L, k, v, tables, starts, offsets)
+
+    p_ms = timed(prompt, calls)
+    p_bytes = 2 * 2 * rows * Hkv * D * e + 4 * S * mb + 4 * S + 4 * (S + 1)
+
+    kl = torch.randn(S, L, Hkv, D, generator=gen).to(torch.bfloat16).cuda()
+    vl = torch.randn(S, L, Hkv, D, generator=gen).to(torch.bfloat16).cuda()
+    pos = torch.randint(0, T, (S,), generator=gen).to(torch.int32).cuda()
+    l_ms = timed(lambda i: pk.kv_append_layers(pool, kl, vl, tables, pos), calls)
+    l_bytes = 2 * 2 * S * L * Hkv * D * e + 4 * S * 2
+    ks = [kl[:, layer].contiguous() for layer in range(L)]
+    vs = [vl[:, layer].contiguous() for layer in range(L)]
+
+    def per_layer(i):
+        for layer in range(L):
+            pk.kv_append(pool, layer, ks[layer], vs[layer], tables, pos)
+
+    s_ms = timed(per_layer, max(4, calls // 8))
+    del pool, pool_t, reps
+    return {
+        "prompt_append": {
+            "workload": "kv_append_tokens, 64 prompts x 512 tokens, 8 KV heads, head_dim 128, "
+                        "block 16, bf16, 32-layer pool",
+            "ms": round(p_ms, 5), "bytes": p_bytes,
+            "GB_per_s": round(p_bytes / (p_ms * 1e-3) / 1e9, 1),
+            "frac": round(p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "all_layer_append": {
+            "workload": "kv_append_layers, 64 sequences x 32 layers, 8 KV heads, head_dim 128, "
+                        "bf16",
+            "ms": round(l_ms, 5), "bytes": l_bytes,
+            "GB_per_s": round(l_bytes / (l_ms * 1e-3) / 1e9, 1),
+            "ms_as_32_kv_append_calls": round(s_ms, 5)},
+    }
+
+
 def cpu_baseline(w, budget_tokens: int, min_seconds: float = 10.0):
     """The oracle, as it stands, on a bounded sample of the same batch: whole
     sequences in a seeded order until `budget_tokens` cached tokens, run
@@ -142,6 +218,7 @@ def main(argv=None) -> int:
     ap.add_argument("--rotate", type=int, default=0, help="input replicas (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gather", action="store_true")
+    ap.add_argument("--no-appends", action="store_true")
     ap.add_argument("--cpu-budget-tokens", type=int, default=0)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
@@ -303,6 +380,12 @@ def main(argv=None) -> int:
             del outs
         except torch.cuda.OutOfMemoryError:
             result["gather"] = None
+
+    if not args.no_appends:
+        try:
+            result["appends"] = measure_appends(torch, pk)
+        except torch.cuda.OutOfMemoryError:
+            result["appends"] = None
 
     if args.copy_calibration:
         n = args.copy_calibration << 20

@@ -37,6 +37,9 @@
  *     synchronisation.  Block ids outside [0, num_blocks) or lengths beyond
  *     max_blocks_per_seq * block_size are undefined behaviour.  Every
  *     host-visible argument is validated before anything is enqueued.
+ *   - Row arrays (q, out, new K/V rows, gather outputs) are moved in 16-byte
+ *     units and must be 16-byte aligned; a misaligned pointer is rejected
+ *     with PAGEDKV_ERR_INVALID_ARG.
  *   - Calls that share a workspace or write the same output must not run
  *     concurrently on different streams.
  */
@@ -122,6 +125,37 @@ int kv_pool_num_free(const kv_pool_t* pool);
 int kv_append(kv_pool_t* pool, int layer, const void* k_new, const void* v_new,
               const int32_t* block_tables, int max_blocks_per_seq,
               const int32_t* positions, int batch, void* stream);
+
+/* Append one token per sequence for every layer at once ([mini-infer] "The
+ * Solution": a block holds its tokens' K and V for all layers, so one slot
+ * serves every layer).
+ *   k_new, v_new : device, [batch][layers][kv_heads][head_dim], pool dtype.
+ *   positions    : device, [batch] int32; negative = skip b.
+ * Equal to kv_append(pool, l, k_new[:, l], v_new[:, l], ...) for every layer
+ * l, in one launch.  Bit-exact. */
+int kv_append_layers(kv_pool_t* pool, const void* k_new, const void* v_new,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* positions, int batch, void* stream);
+
+/* Append several consecutive tokens per sequence for one layer, e.g. a
+ * prompt or a chunk of one ([kv-cache] section 2: a prompt fills whole blocks
+ * and only the last one is partly filled).
+ *   k_new, v_new   : device, [total_tokens][kv_heads][head_dim], pool dtype;
+ *                    rows token_offsets[b] .. token_offsets[b+1]-1 belong to
+ *                    sequence b.
+ *   start_positions: device, [batch] int32; row token_offsets[b] + i goes to
+ *                    logical position start_positions[b] + i.  Negative = skip b.
+ *   token_offsets  : device, [batch + 1] int32, non-decreasing, from 0 to
+ *                    total_tokens (total_tokens itself is passed by value).
+ * Row r belongs to the last b with token_offsets[b] <= r, so an empty
+ * sequence (equal neighbouring offsets) receives nothing.  The caller must
+ * have placed in the table every block the new positions fall into; like
+ * kv_append, the kernel trusts offsets, positions and table entries.
+ * Bit-exact. */
+int kv_append_tokens(kv_pool_t* pool, int layer, const void* k_new, const void* v_new,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* start_positions, const int32_t* token_offsets,
+                     int batch, int total_tokens, void* stream);
 
 /* Batched gather of paged K/V into contiguous tensors
  * ([mini-infer] "Zero-Copy Batched Attention Gather").

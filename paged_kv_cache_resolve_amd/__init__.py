@@ -26,7 +26,8 @@ from ._lib import OutOfBlocksError, PagedKVError  # noqa: F401
 _L = _lib.load()
 
 __all__ = [
-    "KVPool", "kv_pool_create", "kv_append", "paged_kv_gather", "paged_attention_decode",
+    "KVPool", "kv_pool_create", "kv_append", "kv_append_layers", "kv_append_tokens",
+    "paged_kv_gather", "paged_attention_decode",
     "paged_attention_decode_append", "DecodePlan",
     "paged_attention_workspace_bytes", "paged_kv_resolve", "PagedKVError", "OutOfBlocksError",
     "library",
@@ -151,6 +152,38 @@ def kv_append(pool: KVPool, layer: int, k_new: torch.Tensor, v_new: torch.Tensor
     pp = _dev_tensor(positions, "positions", pool.device, torch.int32, (batch,))
     _check(_L.kv_append(pool.handle, layer, kp, vp, tp, mb, pp, batch, _stream(pool.device)),
            "kv_append")
+
+
+def kv_append_layers(pool: KVPool, k_new: torch.Tensor, v_new: torch.Tensor,
+                     block_tables: torch.Tensor, positions: torch.Tensor) -> None:
+    """Write k_new/v_new [batch, layers, kv_heads, head_dim] at token
+    positions[b] for every layer in one launch."""
+    batch = int(positions.shape[0])
+    shape = (batch, pool.layers, pool.kv_heads, pool.head_dim)
+    kp = _dev_tensor(k_new, "k_new", pool.device, pool.dtype, shape)
+    vp = _dev_tensor(v_new, "v_new", pool.device, pool.dtype, shape)
+    tp, mb = _tables_args(pool, block_tables, batch)
+    pp = _dev_tensor(positions, "positions", pool.device, torch.int32, (batch,))
+    _check(_L.kv_append_layers(pool.handle, kp, vp, tp, mb, pp, batch, _stream(pool.device)),
+           "kv_append_layers")
+
+
+def kv_append_tokens(pool: KVPool, layer: int, k_new: torch.Tensor, v_new: torch.Tensor,
+                     block_tables: torch.Tensor, start_positions: torch.Tensor,
+                     token_offsets: torch.Tensor) -> None:
+    """Write several tokens per sequence: rows token_offsets[b] ..
+    token_offsets[b+1]-1 of k_new/v_new [total, kv_heads, head_dim] go to
+    positions start_positions[b], start_positions[b] + 1, ..."""
+    batch = int(start_positions.shape[0])
+    total = int(k_new.shape[0]) if k_new.dim() == 3 else -1
+    shape = (total, pool.kv_heads, pool.head_dim)
+    kp = _dev_tensor(k_new, "k_new", pool.device, pool.dtype, shape)
+    vp = _dev_tensor(v_new, "v_new", pool.device, pool.dtype, shape)
+    tp, mb = _tables_args(pool, block_tables, batch)
+    sp = _dev_tensor(start_positions, "start_positions", pool.device, torch.int32, (batch,))
+    op = _dev_tensor(token_offsets, "token_offsets", pool.device, torch.int32, (batch + 1,))
+    _check(_L.kv_append_tokens(pool.handle, layer, kp, vp, tp, mb, sp, op, batch, total,
+                               _stream(pool.device)), "kv_append_tokens")
 
 
 def paged_kv_gather(pool: KVPool, layer: int, block_tables: torch.Tensor,

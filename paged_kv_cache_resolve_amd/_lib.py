@@ -39,6 +39,9 @@ SIGNATURES = {
     "kv_pool_free_block": (_c_int, [_vp, ctypes.c_int32]),
     "kv_pool_num_free": (_c_int, [_vp]),
     "kv_append": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp]),
+    "kv_append_layers": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp]),
+    "kv_append_tokens": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _c_int,
+                                  _vp]),
     "paged_kv_gather": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int,
                                  _vp]),
     "paged_attention_workspace_bytes": (_c_size, [_vp, _c_int, _c_int]),

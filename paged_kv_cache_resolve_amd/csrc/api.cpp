@@ -25,6 +25,9 @@ int hip_status(hipError_t e) { return e == hipSuccess ? PAGEDKV_OK : PAGEDKV_ERR
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Row arrays (q, out, new K/V rows, gather outputs) are moved in 16-byte units.
+bool aligned16(const void* p) { return reinterpret_cast<uintptr_t>(p) % 16 == 0; }
+
 }  // namespace
 
 namespace pagedkv {
@@ -136,8 +139,36 @@ int kv_append(kv_pool_t* pool, int layer, const void* k_new, const void* v_new,
     return PAGEDKV_ERR_INVALID_ARG;
   if (batch == 0) return PAGEDKV_OK;
   if (!k_new || !v_new || !block_tables || !positions) return PAGEDKV_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PAGEDKV_ERR_INVALID_ARG;
   return hip_status(launch_append(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq,
                                   positions, batch, static_cast<hipStream_t>(stream)));
+}
+
+int kv_append_layers(kv_pool_t* pool, const void* k_new, const void* v_new,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* positions, int batch, void* stream) {
+  if (!pool || batch < 0 || max_blocks_per_seq < 1) return PAGEDKV_ERR_INVALID_ARG;
+  if (batch == 0) return PAGEDKV_OK;
+  if (!k_new || !v_new || !block_tables || !positions) return PAGEDKV_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PAGEDKV_ERR_INVALID_ARG;
+  return hip_status(launch_append_layers(pool, k_new, v_new, block_tables, max_blocks_per_seq,
+                                         positions, batch, static_cast<hipStream_t>(stream)));
+}
+
+int kv_append_tokens(kv_pool_t* pool, int layer, const void* k_new, const void* v_new,
+                     const int32_t* block_tables, int max_blocks_per_seq,
+                     const int32_t* start_positions, const int32_t* token_offsets, int batch,
+                     int total_tokens, void* stream) {
+  if (!pool || batch < 0 || total_tokens < 0 || layer < 0 || layer >= pool->layers ||
+      max_blocks_per_seq < 1)
+    return PAGEDKV_ERR_INVALID_ARG;
+  if (batch == 0 || total_tokens == 0) return PAGEDKV_OK;
+  if (!k_new || !v_new || !block_tables || !start_positions || !token_offsets)
+    return PAGEDKV_ERR_INVALID_ARG;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PAGEDKV_ERR_INVALID_ARG;
+  return hip_status(launch_append_tokens(pool, layer, k_new, v_new, block_tables,
+                                         max_blocks_per_seq, start_positions, token_offsets,
+                                         batch, total_tokens, static_cast<hipStream_t>(stream)));
 }
 
 int paged_kv_gather(void* k_out, void* v_out, uint8_t* mask, const kv_pool_t* pool, int layer,
@@ -148,6 +179,7 @@ int paged_kv_gather(void* k_out, void* v_out, uint8_t* mask, const kv_pool_t* po
     return PAGEDKV_ERR_INVALID_ARG;
   if (batch == 0 || max_len == 0) return PAGEDKV_OK;
   if (!k_out || !v_out || !mask || !block_tables || !context_lens) return PAGEDKV_ERR_INVALID_ARG;
+  if (!aligned16(k_out) || !aligned16(v_out)) return PAGEDKV_ERR_INVALID_ARG;
   const int units = pool->head_dim * elem_size(pool->dtype) / 16;
   if (units > 256 || (units & (units - 1)) != 0) return PAGEDKV_ERR_UNSUPPORTED;
   return hip_status(launch_gather(k_out, v_out, mask, pool, layer, block_tables,
@@ -178,6 +210,8 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   if (!out || !q || !block_tables || !context_lens) return PAGEDKV_ERR_INVALID_ARG;
   const bool append = k_new != nullptr || v_new != nullptr || positions != nullptr;
   if (append && (!k_new || !v_new || !positions)) return PAGEDKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || (append && (!aligned16(k_new) || !aligned16(v_new))))
+    return PAGEDKV_ERR_INVALID_ARG;
   if (batch > kMaxBatchLds) return PAGEDKV_ERR_UNSUPPORTED;
   const int group = num_q_heads / pool->kv_heads;
   const bool use_mfma = mfma_supported(pool, group);

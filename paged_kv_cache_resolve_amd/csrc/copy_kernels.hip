@@ -47,6 +47,79 @@ __global__ __launch_bounds__(256) void append_kernel(PoolGeom pool, int layer, i
   reinterpret_cast<uint4*>(dst)[u] = reinterpret_cast<const uint4*>(src)[u];
 }
 
+// All-layer append: one thread per 16-byte unit of every layer's new K and V
+// rows; k_new / v_new are [batch][layers][kv_heads][head_dim].
+__global__ __launch_bounds__(256) void append_layers_kernel(PoolGeom pool, int layers, int elem,
+                                                            const char* __restrict__ k_new,
+                                                            const char* __restrict__ v_new,
+                                                            const int32_t* __restrict__ tables,
+                                                            int mb,
+                                                            const int32_t* __restrict__ positions,
+                                                            int batch) {
+  const int units = pool.head_dim * elem / 16;
+  const int64_t total = (int64_t)batch * layers * pool.kv_heads * 2 * units;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int u = (int)(i % units);
+  int64_t r = i / units;
+  const int kv = (int)(r & 1);
+  r >>= 1;
+  const int g = (int)(r % pool.kv_heads);
+  r /= pool.kv_heads;
+  const int layer = (int)(r % layers);
+  const int b = (int)(r / layers);
+  const int pos = positions[b];
+  if (pos < 0) return;
+  const int phys = tables[(int64_t)b * mb + pos / pool.block_size];
+  const int64_t dst_elem = (int64_t)phys * pool.block_stride + kv * pool.kv_stride +
+                           (int64_t)layer * pool.layer_stride + (int64_t)g * pool.head_stride +
+                           (int64_t)(pos % pool.block_size) * pool.head_dim;
+  const char* src = (kv ? v_new : k_new) +
+                    (((int64_t)b * layers + layer) * pool.kv_heads + g) * pool.head_dim * elem;
+  char* dst = const_cast<char*>(pool.base) + dst_elem * elem;
+  reinterpret_cast<uint4*>(dst)[u] = reinterpret_cast<const uint4*>(src)[u];
+}
+
+// Multi-token append: one thread per 16-byte unit of every new row.  Rows
+// offsets[b] .. offsets[b+1]-1 of k_new / v_new ([total][kv_heads][head_dim])
+// belong to sequence b and go to positions starts[b], starts[b] + 1, ...
+__global__ __launch_bounds__(256) void append_tokens_kernel(PoolGeom pool, int layer, int elem,
+                                                            const char* __restrict__ k_new,
+                                                            const char* __restrict__ v_new,
+                                                            const int32_t* __restrict__ tables,
+                                                            int mb,
+                                                            const int32_t* __restrict__ starts,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int batch, int64_t total_rows) {
+  const int units = pool.head_dim * elem / 16;
+  const int64_t total = total_rows * pool.kv_heads * 2 * units;
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int u = (int)(i % units);
+  int64_t r = i / units;
+  const int kv = (int)(r & 1);
+  r >>= 1;
+  const int g = (int)(r % pool.kv_heads);
+  const int64_t row = r / pool.kv_heads;
+  // the sequence of this row: the largest b in [0, batch) with offsets[b] <= row
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (offsets[mid] <= row) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int start = starts[b];
+  if (start < 0) return;
+  const int t = start + (int)(row - offsets[b]);
+  const int phys = tables[(int64_t)b * mb + t / pool.block_size];
+  const int64_t dst_elem = (int64_t)phys * pool.block_stride + kv * pool.kv_stride +
+                           (int64_t)layer * pool.layer_stride + (int64_t)g * pool.head_stride +
+                           (int64_t)(t % pool.block_size) * pool.head_dim;
+  const char* src = (kv ? v_new : k_new) + (row * pool.kv_heads + g) * pool.head_dim * elem;
+  char* dst = const_cast<char*>(pool.base) + dst_elem * elem;
+  reinterpret_cast<uint4*>(dst)[u] = reinterpret_cast<const uint4*>(src)[u];
+}
+
 // Workgroup = 256 threads = (256 / units) tokens x units of one KV head.
 // grid = (ceil(max_len / tokens_per_iter), kv_heads, batch); each workgroup
 // walks kTokIters token tiles.
@@ -115,6 +188,35 @@ hipError_t launch_append(const kv_pool* pool, int layer, const void* k_new, cons
   hipLaunchKernelGGL(append_kernel, dim3((unsigned)blocks), dim3(256), 0, s, g, layer, elem,
                      static_cast<const char*>(k_new), static_cast<const char*>(v_new), tables, mb,
                      positions, batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_layers(const kv_pool* pool, const void* k_new, const void* v_new,
+                                const int32_t* tables, int mb, const int32_t* positions, int batch,
+                                hipStream_t s) {
+  const int elem = elem_size(pool->dtype);
+  const int units = pool->head_dim * elem / 16;
+  const int64_t total = (int64_t)batch * pool->layers * pool->kv_heads * 2 * units;
+  if (total == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(append_layers_kernel, dim3((unsigned)blocks), dim3(256), 0, s, geom_of(pool),
+                     pool->layers, elem, static_cast<const char*>(k_new),
+                     static_cast<const char*>(v_new), tables, mb, positions, batch);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_tokens(const kv_pool* pool, int layer, const void* k_new,
+                                const void* v_new, const int32_t* tables, int mb,
+                                const int32_t* starts, const int32_t* offsets, int batch,
+                                int64_t total_rows, hipStream_t s) {
+  const int elem = elem_size(pool->dtype);
+  const int units = pool->head_dim * elem / 16;
+  const int64_t total = total_rows * pool->kv_heads * 2 * units;
+  if (total == 0 || batch == 0) return hipSuccess;
+  const int64_t blocks = (total + 255) / 256;
+  hipLaunchKernelGGL(append_tokens_kernel, dim3((unsigned)blocks), dim3(256), 0, s, geom_of(pool),
+                     layer, elem, static_cast<const char*>(k_new), static_cast<const char*>(v_new),
+                     tables, mb, starts, offsets, batch, total_rows);
   return hipGetLastError();
 }
 

@@ -112,6 +112,13 @@ void decode_workspace_carve(void* ws, int batch, int kv_heads, int group,
 hipError_t launch_append(const kv_pool* pool, int layer, const void* k_new,
                          const void* v_new, const int32_t* tables, int mb,
                          const int32_t* positions, int batch, hipStream_t s);
+hipError_t launch_append_layers(const kv_pool* pool, const void* k_new, const void* v_new,
+                                const int32_t* tables, int mb, const int32_t* positions, int batch,
+                                hipStream_t s);
+hipError_t launch_append_tokens(const kv_pool* pool, int layer, const void* k_new,
+                                const void* v_new, const int32_t* tables, int mb,
+                                const int32_t* starts, const int32_t* offsets, int batch,
+                                int64_t total_rows, hipStream_t s);
 hipError_t launch_gather(void* k_out, void* v_out, uint8_t* mask,
                          const kv_pool* pool, int layer, const int32_t* tables,
                          int mb, const int32_t* lens, int batch, int max_len,

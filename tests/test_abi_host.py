@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     for n in names:
         assert hasattr(L, n), f"{n} missing from libpagedkv.so"
     assert set(names) == set(_lib.SIGNATURES), "binding signatures drift from the header"
@@ -166,6 +166,31 @@ def test_entry_points_validate_before_launch():
     assert L.paged_kv_gather(p, p, p, h, 5, p, 4, p, 4, 16, None) == _lib.ERR_INVALID_ARG
     assert L.paged_kv_gather(None, p, p, h, 0, p, 4, p, 4, 16, None) == _lib.ERR_INVALID_ARG
     assert L.paged_kv_gather(p, p, p, h, 0, p, 4, p, 4, 0, None) == 0
+    odd = ctypes.c_void_p(p.value + 8)                                  # not 16-byte aligned
+    assert dec(q=odd) == _lib.ERR_INVALID_ARG
+    assert dec(out=odd) == _lib.ERR_INVALID_ARG
+    assert fused(k=odd) == _lib.ERR_INVALID_ARG
+    assert L.kv_append(h, 0, odd, p, p, 4, p, 4, None) == _lib.ERR_INVALID_ARG
+    assert L.paged_kv_gather(p, odd, p, h, 0, p, 4, p, 4, 16, None) == _lib.ERR_INVALID_ARG
+    # all-layer append: kv_append_layers(pool, k, v, tables, mb, positions, batch, stream)
+    assert L.kv_append_layers(h, None, p, p, 4, p, 4, None) == _lib.ERR_INVALID_ARG
+    assert L.kv_append_layers(h, p, p, p, 0, p, 4, None) == _lib.ERR_INVALID_ARG
+    assert L.kv_append_layers(h, p, p, p, 4, p, -1, None) == _lib.ERR_INVALID_ARG
+    assert L.kv_append_layers(h, p, odd, p, 4, p, 4, None) == _lib.ERR_INVALID_ARG
+    assert L.kv_append_layers(h, None, None, None, 4, None, 0, None) == 0
+    # multi-token append: kv_append_tokens(pool, layer, k, v, tables, mb, starts,
+    #                                      offsets, batch, total, stream)
+    tok = lambda **kw: L.kv_append_tokens(  # noqa: E731
+        h, kw.get("layer", 0), kw.get("k", p), p, p, kw.get("mb", 4), p, kw.get("off", p),
+        kw.get("batch", 4), kw.get("total", 40), None)
+    assert tok(layer=2) == _lib.ERR_INVALID_ARG
+    assert tok(mb=0) == _lib.ERR_INVALID_ARG
+    assert tok(total=-1) == _lib.ERR_INVALID_ARG
+    assert tok(batch=-1) == _lib.ERR_INVALID_ARG
+    assert tok(off=None) == _lib.ERR_INVALID_ARG
+    assert tok(k=odd) == _lib.ERR_INVALID_ARG
+    assert tok(total=0, k=None, off=None) == 0
+    assert tok(batch=0, k=None, off=None) == 0
     assert L.paged_kv_resolve(p, p, 4, p, 4, 0, 16, None) == _lib.ERR_INVALID_ARG
     assert L.paged_kv_resolve(None, p, 4, p, 4, 16, 16, None) == _lib.ERR_INVALID_ARG
     L.kv_pool_destroy(h)

@@ -69,3 +69,21 @@ def test_bf16_rounding_is_rne():
     # 1 + 2^-8 is a tie between 1.0 and 1 + 2^-7: even mantissa wins (1.0).
     # 1 + 3*2^-8 is a tie between 1+2^-7 and 1+2^-6: even wins (1+2^-6).
     assert bf16_round_bits(x).tolist() == [0x3F80, 0x3F80, 0x3F82, 0xC020, 0x4049]
+
+
+def test_append_batch_well_formed():
+    from workloads import make_append_batch
+    starts = [0, 5, -1, 16, 0]
+    counts = [33, 4, 3, 0, 1]
+    a = make_append_batch(5, dtype="bf16", Hkv=2, D=64, BS=16, L=3, layer=1,
+                          starts=starts, counts=counts)
+    b = make_append_batch(5, dtype="bf16", Hkv=2, D=64, BS=16, L=3, layer=1,
+                          starts=starts, counts=counts)
+    assert a.pool.tobytes() == b.pool.tobytes() and a.k_rows.tobytes() == b.k_rows.tobytes()
+    assert a.token_offsets.tolist() == [0, 33, 37, 40, 40, 41]
+    assert a.k_rows.shape == (41, 2, 64) and a.k_layers.shape == (5, 3, 2, 64)
+    used = a.block_tables[a.block_tables >= 0]
+    assert len(used) == len(set(used.tolist())) and used.max() < a.NB
+    for s, n, row in zip(starts, counts, a.block_tables):
+        if s >= 0:   # every position the appends write has a block
+            assert (row[:math.ceil((s + max(n, 1)) / 16)] >= 0).all()

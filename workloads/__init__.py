@@ -9,8 +9,10 @@ arithmetic: no block-table resolution, no gather, no attention.
 
 from .synth import (  # noqa: F401
     CONFIG_NAMES,
+    AppendBatch,
     Workload,
     bf16_round_bits,
     config_spec,
+    make_append_batch,
     make_workload,
 )

@@ -263,3 +263,75 @@ def make_workload(index: int, *, with_pool: bool = True, seed_offset: int = 0,
         meta=dict(spec=spec, total_blocks=total_blocks, seed=1000 + index,
                   seed_offset=seed_offset),
     )
+
+
+@dataclass
+class AppendBatch:
+    """Inputs of the two multi-row appends (all layers of one token; several
+    tokens of one layer), with a pool whose background is random bits so
+    that any stray or missing write changes bytes a test compares."""
+
+    dtype: str
+    S: int
+    Hkv: int
+    D: int
+    BS: int
+    L: int
+    layer: int
+    NB: int
+    MB: int
+    pool: np.ndarray             # [NB, 2, L, Hkv, BS, D]
+    block_tables: np.ndarray     # int32 [S, MB], -1 where unused
+    start_positions: np.ndarray  # int32 [S], first new position (negative = skip)
+    token_offsets: np.ndarray    # int32 [S + 1], rows of sequence b: [off[b], off[b+1])
+    k_rows: np.ndarray           # [N, Hkv, D] new rows, N = token_offsets[-1]
+    v_rows: np.ndarray
+    k_layers: np.ndarray         # [S, L, Hkv, D] one token for every layer
+    v_layers: np.ndarray
+
+    @property
+    def total_rows(self) -> int:
+        return int(self.token_offsets[-1])
+
+
+def make_append_batch(seed: int, *, dtype: str, Hkv: int, D: int, BS: int, L: int, layer: int,
+                      starts, counts, spare_blocks: int = 3) -> AppendBatch:
+    """Sequence b gets counts[b] new tokens from position starts[b] on (the
+    layered rows are for position starts[b] alone).  Its table holds
+    ceil((starts[b] + max(counts[b], 1)) / BS) blocks drawn from one random
+    permutation of the pool; a negative start gets one block and is skipped
+    by the appends."""
+    starts = np.asarray(starts, dtype=np.int32)
+    counts = np.asarray(counts, dtype=np.int64)
+    S = len(starts)
+    ends = np.where(starts >= 0, starts.astype(np.int64) + np.maximum(counts, 1), 1)
+    need = (ends + BS - 1) // BS
+    mb = max(1, int(need.max()) if S else 1)
+    nb = int(need.sum()) + spare_blocks
+    ss = np.random.SeedSequence(seed)
+    s_tab, s_pool, s_rows, s_layers = ss.spawn(4)
+    perm = np.random.default_rng(s_tab).permutation(nb).astype(np.int32)
+    tables = np.full((S, mb), -1, dtype=np.int32)
+    off = 0
+    for b in range(S):
+        n = int(need[b])
+        tables[b, :n] = perm[off:off + n]
+        off += n
+    npdt = np.float32 if dtype == "f32" else np.uint16
+    shape = (nb, 2, L, Hkv, BS, D)
+    nbytes = int(np.prod(shape)) * np.dtype(npdt).itemsize
+    pool = np.frombuffer(np.random.default_rng(s_pool).bytes(nbytes), dtype=npdt)
+    pool = pool.reshape(shape).copy()
+    offsets = np.zeros(S + 1, dtype=np.int32)
+    offsets[1:] = np.cumsum(counts)
+    n_rows = int(offsets[-1])
+    rng_r = np.random.default_rng(s_rows)
+    k_rows = _normal_values(rng_r, (n_rows, Hkv, D), dtype)
+    v_rows = _normal_values(rng_r, (n_rows, Hkv, D), dtype)
+    rng_l = np.random.default_rng(s_layers)
+    k_layers = _normal_values(rng_l, (S, L, Hkv, D), dtype)
+    v_layers = _normal_values(rng_l, (S, L, Hkv, D), dtype)
+    return AppendBatch(dtype=dtype, S=S, Hkv=Hkv, D=D, BS=BS, L=L, layer=layer, NB=nb, MB=mb,
+                       pool=pool, block_tables=tables, start_positions=starts,
+                       token_offsets=offsets, k_rows=k_rows, v_rows=v_rows,
+                       k_layers=k_layers, v_layers=v_layers)
