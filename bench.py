@@ -138,6 +138,16 @@ def measure_appends(torch, pk, calls: int = 64) -> dict:
 
     p_ms = timed(prompt, calls)
     p_bytes = 2 * 2 * rows * Hkv * D * e + 4 * S * mb + 4 * S + 4 * (S + 1)
+    # the same bytes moved by a plain contiguous device copy (torch copy_), for scale
+    dst = [torch.empty_like(reps[0][0]) for _ in range(2)]
+
+    def plain_copy(i):
+        k, v = reps[i % 2]
+        dst[0].copy_(k)
+        dst[1].copy_(v)
+
+    c_ms = timed(plain_copy, calls)
+    del dst
 
     kl = torch.randn(S, L, Hkv, D, generator=gen).to(torch.bfloat16).cuda()
     vl = torch.randn(S, L, Hkv, D, generator=gen).to(torch.bfloat16).cuda()
@@ -159,7 +169,8 @@ def measure_appends(torch, pk, calls: int = 64) -> dict:
                         "block 16, bf16, 32-layer pool",
             "ms": round(p_ms, 5), "bytes": p_bytes,
             "GB_per_s": round(p_bytes / (p_ms * 1e-3) / 1e9, 1),
-            "frac": round(p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+            "frac": round(p_bytes / (p_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "plain_copy_same_bytes_GB_per_s": round(p_bytes / (c_ms * 1e-3) / 1e9, 1)},
         "all_layer_append": {
             "workload": "kv_append_layers, 64 sequences x 32 layers, 8 KV heads, head_dim 128, "
                         "bf16",

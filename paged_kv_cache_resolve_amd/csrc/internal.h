@@ -133,6 +133,8 @@ hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out
 // PAGEDKV_DECODE_WG_PER_CU environment variable overrides it, for launch-shape
 // sweeps), never more than `resident`.
 int decode_workgroups(int resident);
+// Compute units of the current device (0 if the runtime cannot tell).
+int device_cus();
 
 // Decode pass 1 variants and pass 2.  The *_supported predicates say which
 // shapes each pass-1 kernel handles.

@@ -65,6 +65,7 @@ hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out
 namespace {
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cus[kMaxDevices];   // CU count per device, 0 = not yet queried
+}  // namespace
 
 // CUs of the current device (0 if the runtime cannot tell), queried once.
 int device_cus() {
@@ -83,7 +84,6 @@ int device_cus() {
   }
   return cus;
 }
-}  // namespace
 
 int decode_workgroups(int resident) {
   static const int per_cu = [] {

@@ -35,6 +35,8 @@ SHAPES = [
     ("bf16", 4, 256, 16, 2),
     ("f32", 4, 64, 16, 3),
     ("f32", 2, 32, 8, 2),
+    ("bf16", 3, 96, 16, 2),     # 12 units per head row, 3 heads: no power of two
+    ("f32", 5, 20, 8, 2),       # 5 units per head row
 ]
 
 # Ragged counts: empty, single token, a whole block, block + 1, many blocks;
@@ -133,6 +135,27 @@ def test_append_tokens_prompt_llama8b_shape():
     S = 64
     a = make_append_batch(31, dtype="bf16", Hkv=8, D=128, BS=16, L=4, layer=2,
                           starts=[0] * S, counts=[512] * S)
+    dp = DevicePool(a)
+    pk.kv_append_tokens(dp.pool, a.layer, np_to_dev(a.k_rows, "bf16"),
+                        np_to_dev(a.v_rows, "bf16"), dp.tables,
+                        torch.from_numpy(a.start_positions).cuda(),
+                        torch.from_numpy(a.token_offsets).cuda())
+    torch.cuda.synchronize()
+    oracle.kv_append_tokens(a.pool, a.layer, a.block_tables, a.start_positions,
+                            a.token_offsets, a.k_rows, a.v_rows, in_place=True)
+    assert dp.pool_bytes() == a.pool.tobytes()
+
+
+@pytest.mark.parametrize("tokens", [64, 160])
+def test_append_tokens_mid_sizes(tokens):
+    """Launch sizes between the small cases and the 64 x 512 prompt, so that
+    every units-per-thread variant of the append kernel runs."""
+    say(f"kv_append_tokens 64 x {tokens}, Llama-8B KV geometry")
+    S = 64
+    rng = np.random.default_rng(tokens)
+    starts = rng.integers(0, 40, size=S)
+    a = make_append_batch(51 + tokens, dtype="bf16", Hkv=8, D=128, BS=16, L=2, layer=1,
+                          starts=starts, counts=rng.integers(tokens // 2, 2 * tokens, size=S))
     dp = DevicePool(a)
     pk.kv_append_tokens(dp.pool, a.layer, np_to_dev(a.k_rows, "bf16"),
                         np_to_dev(a.v_rows, "bf16"), dp.tables,
