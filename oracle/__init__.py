@@ -22,8 +22,12 @@ Parity status per function:
                                        brute force, closed forms, invariants)
   waste arithmetic                     pinned (the page's worked numbers)
   FreeBlockStack                       pinned (the page's LIFO semantics)
+  BlockManagerModel (manager.py)       pinned (the pages' waste figures and
+                                       bound, LIFO reuse, all-or-nothing
+                                       admission, conservation of blocks)
 """
 
+from .manager import BlockManagerModel  # noqa: F401
 from .paged import (  # noqa: F401
     FreeBlockStack,
     OutOfBlocks,

@@ -362,6 +362,104 @@ def check_free_stack():
     assert st.allocate() == 0 and st.allocate() == 2
 
 
+def check_block_manager_page_figures():
+    """[mini-infer] "The Problem" / "Memory Waste Analysis" with B = 16: a
+    42-token request holds 3 blocks (48 slots, 6 wasted); a 400-token one
+    holds 25 blocks and wastes nothing; one more token opens block 26 and the
+    waste reaches the page's maximum B - 1 = 15."""
+    m = oracle.BlockManagerModel(num_blocks=64, block_size=16, max_blocks_per_seq=32)
+    m.add_sequence(1)
+    m.add_sequence(2)
+    assert m.reserve([1, 2], [42, 400]) == [0, 0]
+    st = m.stats()
+    assert (len(m.tables[1]), len(m.tables[2])) == (3, 25)
+    assert (st["blocks_used"], st["tokens"], st["slots"], st["waste_slots"]) == (28, 442, 448, 6)
+    assert m.blocks_needed([2], [1]) == 1
+    assert m.reserve([2], [1]) == [400]
+    assert m.stats()["waste_slots"] == 6 + 15
+    assert m.stats()["blocks_free"] == 64 - 29
+
+
+def check_block_manager_lifo_reuse():
+    """The page's stack hands out N-1 first and reuses the last freed block
+    first; a finished sequence returns its blocks in logical order (block 0
+    first), so its last block is the next handed out.  Hand-derived."""
+    m = oracle.BlockManagerModel(num_blocks=8, block_size=16, max_blocks_per_seq=4)
+    for s in (1, 2, 3):
+        m.add_sequence(s)
+    m.reserve([1], [20])                  # 2 blocks: 7, 6
+    m.reserve([2], [1])                   # 5
+    assert m.tables[1] == [7, 6] and m.tables[2] == [5]
+    m.release(1)                          # pushes 7, then 6
+    m.reserve([3], [17])                  # pops 6, then 7
+    assert m.tables[3] == [6, 7]
+    tab, lens = m.block_tables([3, 2])
+    assert tab.tolist() == [[6, 7, -1, -1], [5, -1, -1, -1]] and lens.tolist() == [17, 1]
+    # one decode token for each: only a sequence whose blocks are all full needs one
+    m.add_sequence(4)
+    m.reserve([4], [16])                  # 4
+    assert m.blocks_needed([2, 3, 4], [1, 1, 1]) == 0 + 0 + 1
+    assert m.reserve([2, 3, 4], [1, 1, 1]) == [1, 17, 16]
+    assert m.tables[4] == [4, 3]
+
+
+def check_block_manager_admission():
+    """Admission ([kv-cache] section 3.1): a step runs only if the pool holds
+    the blocks it needs; otherwise the out-of-blocks error of the page's
+    allocator is raised and nothing changes (all or nothing)."""
+    m = oracle.BlockManagerModel(num_blocks=4, block_size=4, max_blocks_per_seq=8)
+    m.add_sequence(0)
+    m.add_sequence(1)
+    m.reserve([0], [12])                  # 3 of 4 blocks
+    before = (dict(m.lens), {k: list(v) for k, v in m.tables.items()}, len(m.stack))
+    assert m.blocks_needed([1, 0], [5, 1]) == 2 + 1
+    with pytest.raises(MemoryError):
+        m.reserve([1, 0], [5, 1])
+    assert (dict(m.lens), {k: list(v) for k, v in m.tables.items()}, len(m.stack)) == before
+    with pytest.raises(ValueError):       # wider than a block-table row
+        m.reserve([1], [33])
+    with pytest.raises(ValueError):       # a sequence twice in one step
+        m.reserve([1, 1], [1, 1])
+    assert m.reserve([1], [4]) == [0] and len(m.stack) == 0
+
+
+def check_block_manager_random_invariants():
+    """Seeded random traffic: blocks are conserved and never shared, each
+    sequence holds exactly the blocks its tokens fill, per-sequence waste
+    stays within [0, B - 1] and the total equals the pinned per-sequence
+    waste arithmetic."""
+    rng = np.random.default_rng(3)
+    B, NB = 16, 96
+    m = oracle.BlockManagerModel(num_blocks=NB, block_size=B, max_blocks_per_seq=12)
+    next_id = 0
+    for _ in range(600):
+        live = list(m.lens)
+        op = rng.random()
+        if op < 0.2 or not live:
+            m.add_sequence(next_id)
+            next_id += 1
+        elif op < 0.35:
+            m.release(live[int(rng.integers(len(live)))])
+        else:
+            k = int(rng.integers(1, len(live) + 1))
+            seqs = [live[int(i)] for i in rng.permutation(len(live))[:k]]
+            counts = [int(rng.integers(0, 20)) if rng.random() < 0.3 else 1 for _ in seqs]
+            try:
+                m.reserve(seqs, counts)
+            except (MemoryError, ValueError):
+                pass
+        held = [b for t in m.tables.values() for b in t]
+        free = [int(x) for x in m.stack._stack[:len(m.stack)]]
+        assert len(held) == len(set(held)) and not set(held) & set(free)
+        assert sorted(held + free) == list(range(NB))
+        for s, t in m.tables.items():
+            assert len(t) == math.ceil(m.lens[s] / B)
+            assert 0 <= len(t) * B - m.lens[s] <= B - 1
+        st = m.stats()
+        assert st["waste_slots"] == sum(oracle.paged_waste_slots(n, B) for n in m.lens.values())
+        assert st["blocks_free"] + st["blocks_used"] == NB
+
+
 def check_widen():
     assert oracle.widen(np.array([0x3F80, 0xC000, 0x0000, 0x3E80], np.uint16), "bf16").tolist() == [1.0, -2.0, 0.0, 0.25]
 
@@ -384,6 +482,10 @@ ALL_CHECKS = [
     ("multi_appends_equal_single_appends", check_multi_appends_equal_single_appends),
     ("waste_examples", check_waste_examples),
     ("free_stack", check_free_stack),
+    ("block_manager_page_figures", check_block_manager_page_figures),
+    ("block_manager_lifo_reuse", check_block_manager_lifo_reuse),
+    ("block_manager_admission", check_block_manager_admission),
+    ("block_manager_random_invariants", check_block_manager_random_invariants),
     ("widen", check_widen),
 ]
 
@@ -494,6 +596,57 @@ MUTANTS = [
     ("waste_floor", "paged_waste_slots", _mut_waste_floor),
     ("widen_low_half", "widen", _mut_widen_low_half),
 ]
+
+
+_Model = oracle.BlockManagerModel
+_orig_reserve = _Model.reserve
+
+
+def _mut_blocks_floor_plus_one(self, n):
+    return n // self.block_size + 1
+
+
+def _mut_release_last_first(self, seq):
+    for blk in reversed(self.tables.pop(seq)):
+        self.stack.free(blk)
+    del self.lens[seq]
+
+
+def _mut_reserve_partial(self, seqs, counts):
+    """allocates what it can before failing"""
+    seqs, counts = list(seqs), list(counts)
+    self._check_step(seqs, counts)
+    starts = []
+    for s, c in zip(seqs, counts):
+        while len(self.tables[s]) < self.blocks_for(self.lens[s] + c):
+            self.tables[s].append(self.stack.allocate())
+        starts.append(self.lens[s])
+        self.lens[s] += c
+    return starts
+
+
+def _mut_needed_ignores_full_tail(self, seqs, counts):
+    return sum(self.blocks_for(c) for c in counts)
+
+
+MANAGER_MUTANTS = [
+    ("manager_blocks_floor_plus_one", "blocks_for", _mut_blocks_floor_plus_one),
+    ("manager_release_last_first", "release", _mut_release_last_first),
+    ("manager_reserve_partial", "reserve", _mut_reserve_partial),
+    ("manager_needed_ignores_tail", "blocks_needed", _mut_needed_ignores_full_tail),
+]
+
+
+@pytest.mark.parametrize("name,attr,mutant", MANAGER_MUTANTS, ids=[m[0] for m in MANAGER_MUTANTS])
+def test_manager_mutants_are_caught(name, attr, mutant):
+    with mock.patch.object(_Model, attr, mutant):
+        failed = []
+        for cname, check in ALL_CHECKS:
+            try:
+                check()
+            except (AssertionError, Exception):  # noqa: BLE001 - any failure counts
+                failed.append(cname)
+        assert failed, f"mutant {name} passed every pin"
 
 
 @pytest.mark.parametrize("name,attr,mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
