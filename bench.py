@@ -180,6 +180,34 @@ def measure_appends(torch, pk, calls: int = 64) -> dict:
     }
 
 
+def measure_manager(torch, pk, w, steps: int = 2000) -> dict:
+    """Host cost of the block manager around one decode step of batch w:
+    admission + tail allocation for one token per sequence
+    (BlockManager.reserve) and the host block tables and lengths for the step
+    (BlockManager.block_tables), through the Python binding."""
+    bs = w.BS
+    need = int(((w.context_lens.astype(np.int64) + steps + bs - 1) // bs).sum())
+    pool = pk.KVPool(need, bs, 1, 1, 8, torch.bfloat16)   # tiny rows: only ids matter here
+    mb = int((int(w.context_lens.max()) + steps + bs - 1) // bs)
+    mgr = pk.BlockManager(pool, mb)
+    ids = list(range(w.S))
+    for i in ids:
+        mgr.add_sequence(i)
+    mgr.reserve(ids, (w.context_lens - 1).tolist())
+    ones = [1] * w.S
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mgr.reserve(ids, ones)
+        mgr.block_tables(ids)
+    dt = (time.perf_counter() - t0) / steps
+    st = mgr.stats()
+    mgr.close()
+    del pool
+    return {"us_per_step": round(dt * 1e6, 2), "batch": w.S, "steps": steps,
+            "waste_ratio_after": round(st["waste_ratio"], 5),
+            "waste_slots_after": st["waste_slots"]}
+
+
 def cpu_baseline(w, budget_tokens: int, min_seconds: float = 10.0):
     """The oracle, as it stands, on a bounded sample of the same batch: whole
     sequences in a seeded order until `budget_tokens` cached tokens, run
@@ -397,6 +425,9 @@ def main(argv=None) -> int:
             result["appends"] = measure_appends(torch, pk)
         except torch.cuda.OutOfMemoryError:
             result["appends"] = None
+
+    if not args.no_appends:
+        result["host_block_manager"] = measure_manager(torch, pk, w0)
 
     if args.copy_calibration:
         n = args.copy_calibration << 20

@@ -111,6 +111,77 @@ int kv_pool_free_block(kv_pool_t* pool, int32_t block_id);
 /* Number of free blocks, or a negative status. */
 int kv_pool_num_free(const kv_pool_t* pool);
 
+/* ---- Host block manager (host memory only; never touches the GPU) ----
+ *
+ * Tracks which physical blocks each sequence holds and how many tokens it
+ * has, drawing blocks from and returning them to the pool's free stack:
+ *   - blocks are added one at a time as a sequence grows, so only its last
+ *     block can be partly filled ([kv-cache] section 2, "Zero-Waste
+ *     Allocation"; [mini-infer] "Memory Waste Analysis");
+ *   - a step is admitted only if the pool holds every block it needs
+ *     ([kv-cache] section 3.1, "Cache Block Pool"); otherwise nothing changes;
+ *   - a finished sequence returns its blocks in logical order, so its last
+ *     block is the next one the stack hands out.
+ * Sequences are named by caller-chosen int64 ids.  Not thread-safe: calls on
+ * one manager, and on its pool's free stack, must not overlap.  Destroying
+ * the pool detaches its managers: their later calls return
+ * PAGEDKV_ERR_INVALID_ARG, and kv_manager_destroy only frees the manager. */
+typedef struct kv_block_manager kv_block_manager_t;
+
+typedef struct {
+  int64_t sequences;     /* live sequences */
+  int64_t blocks_total;  /* pool blocks */
+  int64_t blocks_free;   /* on the pool's free stack */
+  int64_t blocks_used;   /* held by this manager's sequences */
+  int64_t tokens;        /* tokens held */
+  int64_t slots;         /* blocks_used * block_size */
+  int64_t waste_slots;   /* slots - tokens: at most block_size - 1 per sequence */
+  double waste_ratio;    /* waste_slots / tokens (0 when no tokens) */
+} kv_manager_stats_t;
+
+/* max_blocks_per_seq: width of the block-table rows the manager writes; a
+ * sequence may not grow past it. */
+int kv_manager_create(kv_block_manager_t** out, kv_pool_t* pool, int max_blocks_per_seq);
+
+/* Releases every live sequence's blocks to the pool, then frees the
+ * manager.  NULL is accepted. */
+int kv_manager_destroy(kv_block_manager_t* mgr);
+
+/* Register an empty sequence (no blocks).  An id already live is
+ * PAGEDKV_ERR_INVALID_ARG. */
+int kv_manager_add_sequence(kv_block_manager_t* mgr, int64_t seq_id);
+
+/* The admission figure of a step: free blocks needed to grow sequence
+ * seq_ids[i] by counts[i] tokens for every i (a decode step: counts all 1;
+ * a prompt or a chunk of one: its length).  Returns the count (>= 0) or a
+ * negative status: unknown id, an id twice, a negative count or growth past
+ * max_blocks_per_seq blocks is PAGEDKV_ERR_INVALID_ARG. */
+int64_t kv_manager_blocks_needed(const kv_block_manager_t* mgr, int n, const int64_t* seq_ids,
+                                 const int32_t* counts);
+
+/* Admit and apply a step: allocate the blocks kv_manager_blocks_needed
+ * counts (sequences in the order given, each one's blocks in logical order),
+ * grow every sequence, and write its first new position (its token count
+ * before the step) to start_positions[i] (may be NULL).  If the pool has
+ * too few free blocks, returns PAGEDKV_ERR_OUT_OF_BLOCKS and changes
+ * nothing; argument errors as for kv_manager_blocks_needed. */
+int kv_manager_reserve(kv_block_manager_t* mgr, int n, const int64_t* seq_ids,
+                       const int32_t* counts, int32_t* start_positions);
+
+/* Finish a sequence: its blocks go back to the pool's free stack in logical
+ * order and the id is forgotten. */
+int kv_manager_release(kv_block_manager_t* mgr, int64_t seq_id);
+
+/* Host block tables for a batch: tables[i][j] (row-major [n][max_blocks_per_seq],
+ * -1 past the sequence's blocks) and context_lens[i] = its token count.  Ready
+ * to be copied to the device for kv_append* and paged_attention_decode*. */
+int kv_manager_block_tables(const kv_block_manager_t* mgr, int n, const int64_t* seq_ids,
+                            int32_t* tables, int32_t* context_lens);
+
+/* Blocks and tokens held, and the internal-fragmentation waste
+ * ([mini-infer] "Memory Waste Analysis"). */
+int kv_manager_stats(const kv_block_manager_t* mgr, kv_manager_stats_t* out);
+
 /* Append one token per sequence into its tail block
  * ([kv-cache] section 2: blocks are filled per block as generation
  * proceeds; [mini-infer] "The Solution": a block stores K and V of B

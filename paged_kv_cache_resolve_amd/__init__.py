@@ -12,12 +12,17 @@ streams.
     paged_attention_decode_append(out, q, pool, layer, block_tables, context_lens, scale,
                                   k_new, v_new, positions)   # both of the above in one call
     k_all, v_all, mask = paged_kv_gather(pool, layer, block_tables, context_lens, max_len)
+
+    mgr = BlockManager(pool, max_blocks_per_seq)   # host block manager (C++)
+    mgr.add_sequence(7); starts = mgr.reserve([7], [prompt_len])
+    tables, lens = mgr.block_tables([7])            # host int32 arrays
 """
 
 from __future__ import annotations
 
 import ctypes
 
+import numpy as np
 import torch
 
 from . import _lib
@@ -26,7 +31,7 @@ from ._lib import OutOfBlocksError, PagedKVError  # noqa: F401
 _L = _lib.load()
 
 __all__ = [
-    "KVPool", "kv_pool_create", "kv_append", "kv_append_layers", "kv_append_tokens",
+    "KVPool", "kv_pool_create", "BlockManager", "kv_append", "kv_append_layers", "kv_append_tokens",
     "paged_kv_gather", "paged_attention_decode",
     "paged_attention_decode_append", "DecodePlan",
     "paged_attention_workspace_bytes", "paged_kv_resolve", "PagedKVError", "OutOfBlocksError",
@@ -126,6 +131,78 @@ class KVPool:
         if h is not None and h.value and _L is not None:
             _L.kv_pool_destroy(h)
             self._handle = ctypes.c_void_p()
+
+
+class BlockManager:
+    """Host block manager over a pool's free-block stack (libpagedkv's C++
+    manager): admission of a step, tail-block allocation as sequences grow,
+    release of a finished sequence's blocks, and waste statistics.  Host
+    memory only.  Sequence ids are caller-chosen integers."""
+
+    def __init__(self, pool: KVPool, max_blocks_per_seq: int):
+        self.pool = pool                      # keeps the pool alive
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+        self._handle = ctypes.c_void_p()
+        _check(_L.kv_manager_create(ctypes.byref(self._handle), pool.handle,
+                                    self.max_blocks_per_seq), "kv_manager_create")
+
+    @staticmethod
+    def _ids(seq_ids):
+        return np.ascontiguousarray(np.asarray(seq_ids, dtype=np.int64).reshape(-1))
+
+    def add_sequence(self, seq_id: int) -> None:
+        _check(_L.kv_manager_add_sequence(self._handle, int(seq_id)), "kv_manager_add_sequence")
+
+    def blocks_needed(self, seq_ids, counts) -> int:
+        ids = self._ids(seq_ids)
+        cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32).reshape(-1))
+        if cnt.shape != ids.shape:
+            raise ValueError("seq_ids and counts differ in length")
+        n = _L.kv_manager_blocks_needed(self._handle, len(ids), ids.ctypes.data, cnt.ctypes.data)
+        _check(int(min(n, 0)), "kv_manager_blocks_needed")
+        return int(n)
+
+    def reserve(self, seq_ids, counts) -> np.ndarray:
+        """Admit a step (grow seq_ids[i] by counts[i] tokens) and return each
+        sequence's first new position; OutOfBlocksError leaves all unchanged."""
+        ids = self._ids(seq_ids)
+        cnt = np.ascontiguousarray(np.asarray(counts, dtype=np.int32).reshape(-1))
+        if cnt.shape != ids.shape:
+            raise ValueError("seq_ids and counts differ in length")
+        starts = np.empty(len(ids), dtype=np.int32)
+        _check(_L.kv_manager_reserve(self._handle, len(ids), ids.ctypes.data, cnt.ctypes.data,
+                                     starts.ctypes.data), "kv_manager_reserve")
+        return starts
+
+    def release(self, seq_id: int) -> None:
+        _check(_L.kv_manager_release(self._handle, int(seq_id)), "kv_manager_release")
+
+    def block_tables(self, seq_ids) -> tuple[np.ndarray, np.ndarray]:
+        """Host int32 [n, max_blocks_per_seq] tables (-1 padded) and [n] lengths."""
+        ids = self._ids(seq_ids)
+        tables = np.empty((len(ids), self.max_blocks_per_seq), dtype=np.int32)
+        lens = np.empty(len(ids), dtype=np.int32)
+        _check(_L.kv_manager_block_tables(self._handle, len(ids), ids.ctypes.data,
+                                          tables.ctypes.data, lens.ctypes.data),
+               "kv_manager_block_tables")
+        return tables, lens
+
+    def stats(self) -> dict:
+        st = _lib.ManagerStats()
+        _check(_L.kv_manager_stats(self._handle, ctypes.byref(st)), "kv_manager_stats")
+        return {name: getattr(st, name) for name, _ in st._fields_}
+
+    def close(self) -> None:
+        """Return every live sequence's blocks to the pool and free the
+        manager (also done when the object is collected)."""
+        h = getattr(self, "_handle", None)
+        # at interpreter exit the module globals may already be cleared
+        if h is not None and h.value and _L is not None:
+            _L.kv_manager_destroy(h)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        self.close()
 
 
 def kv_pool_create(num_blocks: int, block_size: int = 16, layers: int = 24, kv_heads: int = 2,

@@ -25,6 +25,16 @@ _c_size = ctypes.c_size_t
 _vp = ctypes.c_void_p
 _i32p = ctypes.POINTER(ctypes.c_int32)
 
+
+
+class ManagerStats(ctypes.Structure):
+    """kv_manager_stats_t"""
+    _fields_ = [("sequences", ctypes.c_int64), ("blocks_total", ctypes.c_int64),
+                ("blocks_free", ctypes.c_int64), ("blocks_used", ctypes.c_int64),
+                ("tokens", ctypes.c_int64), ("slots", ctypes.c_int64),
+                ("waste_slots", ctypes.c_int64), ("waste_ratio", ctypes.c_double)]
+
+
 # name -> (restype, argtypes)
 SIGNATURES = {
     "kv_pool_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int, _c_int, _c_int]),
@@ -38,6 +48,14 @@ SIGNATURES = {
     "kv_pool_alloc_block": (_c_int, [_vp, _i32p]),
     "kv_pool_free_block": (_c_int, [_vp, ctypes.c_int32]),
     "kv_pool_num_free": (_c_int, [_vp]),
+    "kv_manager_create": (_c_int, [ctypes.POINTER(_vp), _vp, _c_int]),
+    "kv_manager_destroy": (_c_int, [_vp]),
+    "kv_manager_add_sequence": (_c_int, [_vp, ctypes.c_int64]),
+    "kv_manager_blocks_needed": (ctypes.c_int64, [_vp, _c_int, _vp, _vp]),
+    "kv_manager_reserve": (_c_int, [_vp, _c_int, _vp, _vp, _vp]),
+    "kv_manager_release": (_c_int, [_vp, ctypes.c_int64]),
+    "kv_manager_block_tables": (_c_int, [_vp, _c_int, _vp, _vp, _vp]),
+    "kv_manager_stats": (_c_int, [_vp, ctypes.POINTER(ManagerStats)]),
     "kv_append": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp]),
     "kv_append_layers": (_c_int, [_vp, _vp, _vp, _vp, _c_int, _vp, _c_int, _vp]),
     "kv_append_tokens": (_c_int, [_vp, _c_int, _vp, _vp, _vp, _c_int, _vp, _vp, _c_int, _c_int,

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(HERE, "libpagedkv.so")
 SOURCES = [
     "api.cpp",
     "launch_cache.cpp",
+    "block_manager.cpp",
     "copy_kernels.hip",
     "decode_mfma.hip",
     "decode_generic.hip",

@@ -92,6 +92,8 @@ int kv_pool_create(kv_pool_t** out, int num_blocks, int block_size, int layers, 
 }
 
 int kv_pool_destroy(kv_pool_t* pool) {
+  if (pool)
+    for (kv_block_manager* m : pool->managers) kv_manager_detach(m);
   delete pool;
   return PAGEDKV_OK;
 }

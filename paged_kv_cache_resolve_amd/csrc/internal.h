@@ -20,7 +20,11 @@ struct kv_pool {
   size_t bytes;
   std::vector<int32_t> free_stack;   // top = back()
   std::vector<uint8_t> is_free;
+  std::vector<kv_block_manager*> managers;   // detached when the pool is destroyed
 };
+
+// Called by kv_pool_destroy for every manager still attached to the pool.
+void kv_manager_detach(kv_block_manager* m);
 
 namespace pagedkv {
 
