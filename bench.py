@@ -54,6 +54,7 @@ WORKLOADS = {
     "llama8b_decode_bf16": 2,
     "long_context_bf16": 3,
     "high_concurrency_bf16": 4,
+    "llama8b_decode_f32": 5,
 }
 
 

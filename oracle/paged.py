@@ -14,7 +14,7 @@ Sources (three web pages on paged KV caches):
 Storage conventions: a pool is a numpy array of shape
 ``[num_blocks, 2, layers, kv_heads, block_size, head_dim]`` (K at index 0 of
 the second axis, V at index 1), holding float32 values or bfloat16 bit
-patterns as uint16.  Copies (gather, append) move raw storage; attention
+patterns as uint16 (fp16 as numpy float16).  Copies (gather, append) move raw storage; attention
 widens to float64 first.
 
 Readings taken where the pages leave a step open:
@@ -40,12 +40,15 @@ import numpy as np
 
 def widen(x: np.ndarray, dtype: str) -> np.ndarray:
     """Raw storage -> float64.  bfloat16 is the upper half of a float32, so
-    widening is exact: shift the 16 stored bits into the high half."""
+    widening is exact: shift the 16 stored bits into the high half.  IEEE
+    half precision (numpy float16) widens exactly by conversion."""
     if dtype == "f32":
         return np.asarray(x, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
         hi = np.asarray(x, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return hi.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(x, dtype=np.float16).astype(np.float64)
     raise ValueError(dtype)
 
 

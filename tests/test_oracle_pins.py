@@ -58,6 +58,10 @@ def _random_paged_case(rng, *, S, Hq, Hkv, D, BS, L, layer, max_T, dtype, poison
         store = np.float32
         nan = np.float32(np.nan)
         draw = lambda shape: rng.standard_normal(shape).astype(np.float32)  # noqa: E731
+    elif dtype == "f16":
+        store = np.float16
+        nan = np.float16(np.nan)
+        draw = lambda shape: rng.standard_normal(shape).astype(np.float16)  # noqa: E731
     else:
         store = np.uint16
         nan = np.uint16(0x7FC0)
@@ -79,7 +83,20 @@ def _random_paged_case(rng, *, S, Hq, Hkv, D, BS, L, layer, max_T, dtype, poison
 
 
 def _to_f64(x, dtype):
+    if dtype == "f16":   # through torch's half type, not numpy's
+        return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float64).numpy()
     return x.astype(np.float64) if dtype == "f32" else _bf16_to_f64_via_torch(x)
+
+
+def _half_value_from_bits(u: int) -> float:
+    """IEEE 754 binary16 from its definition: sign, 5-bit exponent with bias
+    15, 10-bit fraction; exponent 0 is subnormal (no implicit 1)."""
+    sign = -1.0 if u >> 15 else 1.0
+    e = (u >> 10) & 0x1F
+    f = u & 0x3FF
+    if e == 0:
+        return sign * f * 2.0 ** -24
+    return sign * (1024 + f) * 2.0 ** (e - 25)
 
 
 def _sdpa_reference(q, K, V, scale):
@@ -460,6 +477,20 @@ def check_block_manager_random_invariants():
         assert st["blocks_free"] + st["blocks_used"] == NB
 
 
+def check_widen_f16():
+    """Every finite binary16 pattern widens to the value its bits define;
+    a few by hand: 1, -2, 0.25, the largest finite 65504, the smallest
+    subnormal 2^-24 and -2^-14."""
+    hand = np.array([0x3C00, 0xC000, 0x3400, 0x7BFF, 0x0001, 0x8400], np.uint16)
+    assert oracle.widen(hand.view(np.float16), "f16").tolist() == \
+        [1.0, -2.0, 0.25, 65504.0, 2.0 ** -24, -2.0 ** -14]
+    bits = np.arange(1 << 16, dtype=np.uint32)
+    finite = bits[((bits >> 10) & 0x1F) != 0x1F].astype(np.uint16)
+    got = oracle.widen(finite.view(np.float16), "f16")
+    want = np.array([_half_value_from_bits(int(u)) for u in finite])
+    assert got.tobytes() == want.tobytes()
+
+
 def check_widen():
     assert oracle.widen(np.array([0x3F80, 0xC000, 0x0000, 0x3E80], np.uint16), "bf16").tolist() == [1.0, -2.0, 0.0, 0.25]
 
@@ -471,6 +502,8 @@ ALL_CHECKS = [
     ("contiguous_equivalence_bf16", lambda: check_contiguous_equivalence("bf16")),
     ("attention_vs_sdpa_f32", lambda: check_attention_vs_sdpa("f32")),
     ("attention_vs_sdpa_bf16", lambda: check_attention_vs_sdpa("bf16")),
+    ("attention_vs_sdpa_f16", lambda: check_attention_vs_sdpa("f16")),
+    ("contiguous_equivalence_f16", lambda: check_contiguous_equivalence("f16")),
     ("bruteforce_tiny", check_bruteforce_tiny),
     ("closed_forms", check_closed_forms),
     ("invariants", check_invariants),
@@ -487,6 +520,7 @@ ALL_CHECKS = [
     ("block_manager_admission", check_block_manager_admission),
     ("block_manager_random_invariants", check_block_manager_random_invariants),
     ("widen", check_widen),
+    ("widen_f16", check_widen_f16),
 ]
 
 
@@ -502,6 +536,7 @@ def test_pin(name, check):
 _orig_l2p = P.logical_to_physical
 _orig_attend = P.attend
 _orig_gather_seq = P.gather_sequence
+_orig_widen = P.widen
 
 
 def _mut_l2p_swapped(table_row, t, bs):
@@ -574,6 +609,12 @@ def _mut_waste_floor(n, bs):
     return (n // bs) * bs - n + bs - 1 if n % bs else 0
 
 
+def _mut_widen_f16_as_bf16(x, dtype):
+    if dtype == "f16":
+        return _orig_widen(np.asarray(x).view(np.uint16), "bf16")
+    return _orig_widen(x, dtype)
+
+
 def _mut_widen_low_half(x, dtype):
     if dtype == "bf16":
         return np.asarray(x, np.uint16).astype(np.float64)
@@ -595,6 +636,7 @@ MUTANTS = [
     ("append_layers_first_only", "kv_append_layers", _mut_append_layers_first_only),
     ("waste_floor", "paged_waste_slots", _mut_waste_floor),
     ("widen_low_half", "widen", _mut_widen_low_half),
+    ("widen_f16_as_bf16", "widen", _mut_widen_f16_as_bf16),
 ]
 
 

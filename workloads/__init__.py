@@ -15,4 +15,5 @@ from .synth import (  # noqa: F401
     config_spec,
     make_append_batch,
     make_workload,
+    storage_dtype,
 )

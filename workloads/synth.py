@@ -1,11 +1,12 @@
-"""Seeded synthetic inputs for the five paged-decode workloads.
+"""Seeded synthetic inputs for the paged-decode workloads.
 
 Workload i draws from ``numpy.random.default_rng`` streams spawned from
 ``SeedSequence(1000 + i)``: one child stream each for context lengths, block
 tables, pool values, queries and the new tokens' keys and values.  bf16
 values are float32 draws from N(0, 1) rounded to bfloat16 with
 round-to-nearest-even and kept as raw uint16 bit patterns, so that every
-consumer sees exactly the same bits.
+consumer sees exactly the same bits; fp16 values are the same draws converted
+to numpy float16 (also round-to-nearest-even).
 
 Pool layout (page 3, mini-infer, "Python Implementation: Physical Block
 Pool"): ``[num_blocks, 2 (K/V), layers, kv_heads, block_size, head_dim]``.
@@ -35,6 +36,7 @@ CONFIG_NAMES = {
     2: "llama8b_decode_bf16",
     3: "long_context_bf16",
     4: "high_concurrency_bf16",
+    5: "llama8b_decode_f32",
 }
 
 # Sequences' context lengths count the token appended in this step: the new
@@ -50,6 +52,9 @@ _SPECS = {
             lens=("uniform", 32768, 131072), NB="1.1x", tables="perm"),
     4: dict(dtype="bf16", S=256, Hq=64, Hkv=8, D=128, BS=16, L=1, layer=0,
             lens=("bimodal", 0.7, (16, 512), (4096, 16384)), NB="1.1x", tables="perm"),
+    # the Llama-8B-shaped layer of workload 2 with an fp32 cache
+    5: dict(dtype="f32", S=64, Hq=32, Hkv=8, D=128, BS=16, L=1, layer=0,
+            lens=("lognormal", 2048.0, 0.5, 128, 8192), NB="1.1x", tables="perm"),
 }
 
 _CHURN_STEPS = 20000
@@ -108,7 +113,7 @@ class Workload:
 
     @property
     def np_dtype(self):
-        return np.float32 if self.dtype == "f32" else np.uint16
+        return {"f32": np.float32, "f16": np.float16}.get(self.dtype, np.uint16)
 
     def kv_bytes(self) -> int:
         e = 4 if self.dtype == "f32" else 2
@@ -188,13 +193,24 @@ def _tables_after_churn(rng, lens, bs, nb, mb) -> np.ndarray:
 
 
 def _normal_values(rng: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """float32 draws; bf16 as RNE-rounded bit patterns; fp16 as numpy float16
+    (numpy's float32 -> float16 conversion rounds to nearest even)."""
     x = rng.standard_normal(size=shape, dtype=np.float32)
-    return x if dtype == "f32" else bf16_round_bits(x)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16)
+    return bf16_round_bits(x)
+
+
+def storage_dtype(dtype: str):
+    """numpy array type of a pool dtype's raw storage."""
+    return {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[dtype]
 
 
 def _fill_pool(seed_seq: np.random.SeedSequence, nb, L, layer, hkv, bs, d, dtype,
                threads: int | None) -> np.ndarray:
-    npdt = np.float32 if dtype == "f32" else np.uint16
+    npdt = storage_dtype(dtype)
     pool = np.zeros((nb, 2, L, hkv, bs, d), dtype=npdt)
     nchunks = (nb + _POOL_CHUNK_BLOCKS - 1) // _POOL_CHUNK_BLOCKS
     children = seed_seq.spawn(max(nchunks, 1))
@@ -317,7 +333,7 @@ def make_append_batch(seed: int, *, dtype: str, Hkv: int, D: int, BS: int, L: in
         n = int(need[b])
         tables[b, :n] = perm[off:off + n]
         off += n
-    npdt = np.float32 if dtype == "f32" else np.uint16
+    npdt = storage_dtype(dtype)
     shape = (nb, 2, L, Hkv, BS, D)
     nbytes = int(np.prod(shape)) * np.dtype(npdt).itemsize
     pool = np.frombuffer(np.random.default_rng(s_pool).bytes(nbytes), dtype=npdt)
