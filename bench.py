@@ -55,6 +55,7 @@ WORKLOADS = {
     "long_context_bf16": 3,
     "high_concurrency_bf16": 4,
     "llama8b_decode_f32": 5,
+    "llama8b_decode_f16": 6,
 }
 
 
@@ -287,10 +288,10 @@ def main(argv=None) -> int:
           f"BS={w0.BS} sum(T)={int(w0.context_lens.sum())} replicas={reps}", file=sys.stderr,
           flush=True)
 
-    tdt = torch.float32 if w0.dtype == "f32" else torch.bfloat16
+    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w0.dtype]
 
     def dev(x):
-        if w0.dtype == "f32":
+        if w0.dtype in ("f32", "f16"):
             return torch.from_numpy(np.ascontiguousarray(x)).cuda()
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
 
@@ -366,7 +367,7 @@ def main(argv=None) -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w0.dtype == "bf16" else "f32",
+        "dtype": w0.dtype,
         "data": "synthetic (seeded N(0,1) K/V/q, seeded context lengths and block tables)",
         "config": {
             "workload": args.workload,

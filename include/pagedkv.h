@@ -64,7 +64,8 @@ extern "C" {
 /* Element types of the pool (and of q / out / new tokens / gather output). */
 typedef enum {
   PAGEDKV_F32 = 0,
-  PAGEDKV_BF16 = 1
+  PAGEDKV_BF16 = 1,
+  PAGEDKV_F16 = 2    /* IEEE binary16 */
 } pagedkv_dtype_t;
 
 /* Opaque host handle describing a pool.  It records the geometry and the

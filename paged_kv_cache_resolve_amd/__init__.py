@@ -38,7 +38,7 @@ __all__ = [
     "library",
 ]
 
-_DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16}
+_DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.float16: _lib.F16}
 
 
 def library() -> ctypes.CDLL:

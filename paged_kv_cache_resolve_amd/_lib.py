@@ -19,6 +19,7 @@ ERR_HIP = -5
 
 F32 = 0
 BF16 = 1
+F16 = 2
 
 _c_int = ctypes.c_int
 _c_size = ctypes.c_size_t

@@ -12,7 +12,9 @@ using namespace pagedkv;
 
 namespace {
 
-bool valid_dtype(pagedkv_dtype_t t) { return t == PAGEDKV_F32 || t == PAGEDKV_BF16; }
+bool valid_dtype(pagedkv_dtype_t t) {
+  return t == PAGEDKV_F32 || t == PAGEDKV_BF16 || t == PAGEDKV_F16;
+}
 
 size_t pool_bytes_checked(int nb, int bs, int layers, int hkv, int d, pagedkv_dtype_t t) {
   if (nb < 1 || bs < 1 || layers < 1 || hkv < 1 || d < 1 || !valid_dtype(t)) return 0;

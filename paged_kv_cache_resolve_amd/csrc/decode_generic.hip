@@ -1,4 +1,4 @@
-// Paged-attention decode, pass 1, general shapes (fp32 or bf16 pools, any
+// Paged-attention decode, pass 1, general shapes (fp32, bf16 or fp16 pools, any
 // block size, head_dim a multiple of 4 up to 256, up to 16 query heads per KV
 // head), plain VALU arithmetic.
 //
@@ -26,16 +26,19 @@ namespace {
 constexpr int kGenDimsPerLane = 4;   // head_dim <= 256
 constexpr int kKBatch = 16;          // 4-element K pieces per lane in flight
 
+// Storage types: float (fp32), uint16_t (bf16 bit patterns), _Float16 (fp16).
 template <typename TS> __device__ __forceinline__ float to_f32(TS x);
 template <> __device__ __forceinline__ float to_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t x) {
   return __uint_as_float((uint32_t)x << 16);
 }
+template <> __device__ __forceinline__ float to_f32<_Float16>(_Float16 x) { return (float)x; }
 template <typename TS> __device__ __forceinline__ TS from_f32(float x);
 template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <> __device__ __forceinline__ uint16_t from_f32<uint16_t>(float x) {
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) { return (_Float16)x; }
 
 // Four consecutive K elements as floats (16-byte or 8-byte load).  K and V
 // are streamed once, so their loads are non-temporal.
@@ -50,7 +53,21 @@ __device__ __forceinline__ float4 load4(const uint16_t* p) {
   return make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u),
                      __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xffff0000u));
 }
+// fp16 from its 16 bits.  The halves are taken out of each loaded dword with
+// integer shifts: bit-casting the loaded vector's elements straight to half
+// pairs made this compiler load one dword and use it for both pairs.
+__device__ __forceinline__ float half_bits(uint32_t bits) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+__device__ __forceinline__ float4 load4(const _Float16* p) {
+  const u32x2_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p));
+  return make_float4(half_bits(v.x & 0xffffu), half_bits(v.x >> 16), half_bits(v.y & 0xffffu),
+                     half_bits(v.y >> 16));
+}
 __device__ __forceinline__ float load1(const float* p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ float load1(const _Float16* p) {
+  return half_bits(__builtin_nontemporal_load(reinterpret_cast<const uint16_t*>(p)));
+}
 __device__ __forceinline__ float load1(const uint16_t* p) {
   return __uint_as_float((uint32_t)__builtin_nontemporal_load(p) << 16);
 }
@@ -254,9 +271,11 @@ hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
   const size_t lds = sizeof(int32_t) * pre_words +
                      sizeof(float) * (size_t)p.group * (p.pool.head_dim + 64);
   const bool f32 = p.dtype == PAGEDKV_F32;
+  const bool f16 = p.dtype == PAGEDKV_F16;
   const int dpl = p.pool.head_dim <= 64 ? 1 : p.pool.head_dim <= 128 ? 2 : 4;
   const void* fn = f32 ? reinterpret_cast<const void*>(&decode_generic_kernel<float, 4>)
-                       : reinterpret_cast<const void*>(&decode_generic_kernel<uint16_t, 4>);
+                   : f16 ? reinterpret_cast<const void*>(&decode_generic_kernel<_Float16, 4>)
+                         : reinterpret_cast<const void*>(&decode_generic_kernel<uint16_t, 4>);
   int wgs = 0;
   hipError_t e = resident_workgroups(fn, 64, lds, &wgs);
   if (e != hipSuccess) return e;
@@ -281,6 +300,10 @@ hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
     if (dpl == 1) hipLaunchKernelGGL((decode_generic_kernel<float, 1>), grid, block, lds, s, p);
     else if (dpl == 2) hipLaunchKernelGGL((decode_generic_kernel<float, 2>), grid, block, lds, s, p);
     else hipLaunchKernelGGL((decode_generic_kernel<float, 4>), grid, block, lds, s, p);
+  } else if (f16) {
+    if (dpl == 1) hipLaunchKernelGGL((decode_generic_kernel<_Float16, 1>), grid, block, lds, s, p);
+    else if (dpl == 2) hipLaunchKernelGGL((decode_generic_kernel<_Float16, 2>), grid, block, lds, s, p);
+    else hipLaunchKernelGGL((decode_generic_kernel<_Float16, 4>), grid, block, lds, s, p);
   } else {
     if (dpl == 1) hipLaunchKernelGGL((decode_generic_kernel<uint16_t, 1>), grid, block, lds, s, p);
     else if (dpl == 2) hipLaunchKernelGGL((decode_generic_kernel<uint16_t, 2>), grid, block, lds, s, p);

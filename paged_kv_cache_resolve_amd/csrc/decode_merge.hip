@@ -24,9 +24,10 @@ constexpr int kDimsPerLane = 4;   // head_dim <= 256
 
 template <typename TS> __device__ __forceinline__ TS out_cast(float x);
 template <> __device__ __forceinline__ float out_cast<float>(float x) { return x; }
-template <> __device__ __forceinline__ uint16_t out_cast<uint16_t>(float x) {
+template <> __device__ __forceinline__ uint16_t out_cast<uint16_t>(float x) {   // bf16
   return __builtin_bit_cast(uint16_t, (__bf16)x);
 }
+template <> __device__ __forceinline__ _Float16 out_cast<_Float16>(float x) { return (_Float16)x; }
 
 // One wavefront per (sequence b, query head h).  Every lane reads the same
 // (m_k, l_k) of each partial and its own dims of o_k, eight partials per
@@ -141,6 +142,8 @@ hipError_t launch_decode_merge(const DecodeParams& p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   if (p.dtype == PAGEDKV_F32)
     hipLaunchKernelGGL(decode_merge_kernel<float>, dim3((unsigned)blocks), dim3(64), 0, s, p);
+  else if (p.dtype == PAGEDKV_F16)
+    hipLaunchKernelGGL(decode_merge_kernel<_Float16>, dim3((unsigned)blocks), dim3(64), 0, s, p);
   else
     hipLaunchKernelGGL(decode_merge_kernel<uint16_t>, dim3((unsigned)blocks), dim3(64), 0, s, p);
   return hipGetLastError();

@@ -1,4 +1,4 @@
-// Paged-attention decode for bf16 pools: MFMA tiles on gfx950, one kernel.
+// Paged-attention decode for bf16 and fp16 pools: MFMA tiles on gfx950, one kernel.
 //
 // What is computed ("vllmini: Building a Minimalist PagedAttention and KV
 // Cache Engine", section "The CUDA Block Kernel"; "KV Cache and Attention
@@ -21,7 +21,7 @@
 //        used, the rest zero), giving score(token 4*(lane/16)+r, head lane%16);
 //      - online softmax in fp32 in the exp2 domain (the accumulator is
 //        rescaled branch-free; the factor is 1 unless a running max grew);
-//      - the probabilities, rounded to bf16, already sit in the B-operand
+//      - the probabilities, rounded to the pool type, already sit in the B-operand
 //        layout of v_mfma_f32_16x16x16_bf16 (k = token); V rows are loaded
 //        fully coalesced (lane = token 4*(lane/16)+r, dims VD*(lane%16)..)
 //        and transposed to the A operand with v_perm_b32.  The accumulator
@@ -43,6 +43,9 @@ namespace pagedkv {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
@@ -54,8 +57,8 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kTilesPerStep = PAGEDKV_TILES_PER_STEP;   // 16-token MFMA tiles per chunk
 
 template <int D> struct VRow;
-template <> struct VRow<128> { using type = uint4; };   // 8 bf16 per lane
-template <> struct VRow<64> { using type = uint2; };    // 4 bf16 per lane
+template <> struct VRow<128> { using type = uint4; };   // 8 elements per lane
+template <> struct VRow<64> { using type = uint2; };    // 4 elements per lane
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -65,8 +68,9 @@ __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlan
 // Llama-shaped and long-context workloads.
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_nt __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ bf16x8_t stream_load(const bf16x8_t* p) {
-  return __builtin_nontemporal_load(p);
+template <typename X8>
+__device__ __forceinline__ X8 stream_load8(const char* p) {
+  return __builtin_bit_cast(X8, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
 }
 __device__ __forceinline__ void stream_load(uint4& d, const char* p) {
   d = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
@@ -79,24 +83,58 @@ __device__ __forceinline__ void stream_load(uint2& d, const char* p) {
 // constant address space lets uniform indices become scalar loads.
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 __device__ __forceinline__ uint32_t dword_of(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
 
-// Round two floats to bf16 (nearest even) and pack: lo = a, hi = b.
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-  bf16x2_t v;
-  v[0] = (__bf16)a;
-  v[1] = (__bf16)b;
-  return __builtin_bit_cast(uint32_t, v);
-}
-__device__ __forceinline__ uint16_t to_bf16(float a) { return __builtin_bit_cast(uint16_t, (__bf16)a); }
-__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+// Element operations of the two 16-bit pool types: the MFMA forms, rounding
+// of two floats to a packed pair (nearest even; lo = a, hi = b) and widening
+// of either half of a pair.  Probabilities are multiplied by 2^kPScaleLog2
+// before rounding: fp16 would lose small weights to its subnormal range, and
+// the output and the normaliser carry the same factor, so it cancels (bf16
+// has fp32's exponent range and needs none).
+struct Bf16Ops {
+  using x8 = bf16x8_t;
+  static constexpr float kPScaleLog2 = 0.f;
+  static __device__ __forceinline__ f32x4_t mma32(x8 a, x8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mma16(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                     __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    bf16x2_t v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) { return __uint_as_float(x << 16); }
+  static __device__ __forceinline__ float hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+};
+
+struct F16Ops {
+  using x8 = f16x8_t;
+  static constexpr float kPScaleLog2 = 15.f;   // p <= 2^15 < 65504
+  static __device__ __forceinline__ f32x4_t mma32(x8 a, x8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mma16(uint2 a, uint2 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                 __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    f16x2_t v;
+    v[0] = (_Float16)a;
+    v[1] = (_Float16)b;
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float lo(uint32_t x) { return (float)__builtin_bit_cast(f16x2_t, x)[0]; }
+  static __device__ __forceinline__ float hi(uint32_t x) { return (float)__builtin_bit_cast(f16x2_t, x)[1]; }
+};
 
 // Combine a value with the lane 16 (resp. 32) apart, on the VALU.
 __device__ __forceinline__ float max_x16(float x) {
@@ -117,9 +155,9 @@ __device__ __forceinline__ float sum_x32(float x) {
 }
 
 // K and V registers of one step: TILES tiles of 16 tokens.
-template <int D, int TILES>
+template <typename E, int D, int TILES>
 struct ChunkBuf {
-  bf16x8_t k[TILES][D / 32];
+  typename E::x8 k[TILES][D / 32];
   typename VRow<D>::type v[TILES][4];
 };
 
@@ -156,8 +194,10 @@ struct Cursor {
 // With APPEND, the row of a sequence's appended token is read from k_new /
 // v_new instead of the pool (a per-lane address choice; the pool row is
 // written by the merge pass).
-template <int D, int TILES, bool APPEND>
+template <typename E, int D, int TILES, bool APPEND>
 struct Stream {
+  using x8 = typename E::x8;
+  using Buf = ChunkBuf<E, D, TILES>;
   static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
   static constexpr int VD = D / 16;   // V dims per lane
   static constexpr int NW = VD / 2;   // dwords per lane per V row
@@ -167,7 +207,7 @@ struct Stream {
   const int g;              // KV head served by this wavefront
   const int64_t unit;       // head group (chunk range) of this wavefront
 
-  bf16x8_t qop[NK];
+  x8 qop[NK];
   f32x4_t acc[VD];
   float m, l;
 
@@ -191,7 +231,7 @@ struct Stream {
                            ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + min(n, G - 1)) * D +
                            8 * quad;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) qop[i] = *reinterpret_cast<const bf16x8_t*>(qrow + 32 * i);
+    for (int i = 0; i < NK; ++i) qop[i] = *reinterpret_cast<const x8*>(qrow + 32 * i);
   }
 
   // Physical blocks of chunk c's tiles: scalar loads of block-table
@@ -224,7 +264,7 @@ struct Stream {
            2 * ((int64_t)c.b * p.pool.kv_heads + g) * D;
   }
 
-  __device__ __forceinline__ void issue_k(ChunkBuf<D, TILES>& cb, const Cursor& c,
+  __device__ __forceinline__ void issue_k(Buf& cb, const Cursor& c,
                                           const int* ph) const {
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
@@ -234,10 +274,10 @@ struct Stream {
         if (tok == c.pos) kl = new_row(c, 0) + 2 * 8 * quad;
       }
 #pragma unroll
-      for (int i = 0; i < NK; ++i) cb.k[t][i] = stream_load(reinterpret_cast<const bf16x8_t*>(kl + 64 * i));
+      for (int i = 0; i < NK; ++i) cb.k[t][i] = stream_load8<x8>(kl + 64 * i);
     }
   }
-  __device__ __forceinline__ void issue_v(ChunkBuf<D, TILES>& cb, const Cursor& c,
+  __device__ __forceinline__ void issue_v(Buf& cb, const Cursor& c,
                                           const int* ph) const {
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
@@ -255,22 +295,22 @@ struct Stream {
     }
   }
 
-  __device__ __forceinline__ void qk(const ChunkBuf<D, TILES>& cb, f32x4_t* s) const {
+  __device__ __forceinline__ void qk(const Buf& cb, f32x4_t* s) const {
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < NK; ++i)
-        s[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cb.k[t][i], qop[i], s[t], 0, 0, 0);
+        s[t] = E::mma32(cb.k[t][i], qop[i], s[t]);
     }
   }
 
-  // Scores -> bf16 probabilities (already in the B-operand layout of the PV
+  // Scores -> probabilities in the pool type (already in the B-operand layout of the PV
   // product), then the weighted V sum; updates m, l, acc.  TAIL masks tokens
   // at or past T; masked V rows are zeroed, not weighted by zero, so unused
   // pool slots never reach the sum.
   template <bool TAIL>
-  __device__ __forceinline__ void attend(const f32x4_t* s, ChunkBuf<D, TILES>& cb, const Cursor& c) {
+  __device__ __forceinline__ void attend(const f32x4_t* s, Buf& cb, const Cursor& c) {
     float sv[TILES][4];
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
@@ -294,11 +334,12 @@ struct Stream {
       m = mn;
     }
     uint32_t pw[TILES][2];
+    const float mp = m - E::kPScaleLog2;
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-      pw[t][0] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[t][0] - m), __builtin_amdgcn_exp2f(sv[t][1] - m));
-      pw[t][1] = pack_bf16x2(__builtin_amdgcn_exp2f(sv[t][2] - m), __builtin_amdgcn_exp2f(sv[t][3] - m));
-      l += (bf16_lo(pw[t][0]) + bf16_hi(pw[t][0])) + (bf16_lo(pw[t][1]) + bf16_hi(pw[t][1]));
+      pw[t][0] = E::pack2(__builtin_amdgcn_exp2f(sv[t][0] - mp), __builtin_amdgcn_exp2f(sv[t][1] - mp));
+      pw[t][1] = E::pack2(__builtin_amdgcn_exp2f(sv[t][2] - mp), __builtin_amdgcn_exp2f(sv[t][3] - mp));
+      l += (E::lo(pw[t][0]) + E::hi(pw[t][0])) + (E::lo(pw[t][1]) + E::hi(pw[t][1]));
     }
     if (TAIL) {
 #pragma unroll
@@ -308,8 +349,8 @@ struct Stream {
           if (c.j * (16 * TILES) + 16 * t + 4 * quad + r >= c.T) zero_row<D>(cb.v[t][r]);
     }
     if constexpr (TILES == 1) {
-      // k = 4 tokens per lane: v_mfma_f32_16x16x16_bf16
-      const s16x4_t pop = __builtin_bit_cast(s16x4_t, make_uint2(pw[0][0], pw[0][1]));
+      // k = 4 tokens per lane: the 16x16x16 MFMA
+      const uint2 pop = make_uint2(pw[0][0], pw[0][1]);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const uint32_t v0 = dword_of(cb.v[0][0], w), v1 = dword_of(cb.v[0][1], w);
@@ -318,16 +359,13 @@ struct Stream {
                                     __builtin_amdgcn_perm(v3, v2, 0x05040100u));
         const uint2 od = make_uint2(__builtin_amdgcn_perm(v1, v0, 0x07060302u),
                                     __builtin_amdgcn_perm(v3, v2, 0x07060302u));
-        acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, ev), pop,
-                                                               acc[2 * w], 0, 0, 0);
-        acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, od),
-                                                                   pop, acc[2 * w + 1], 0, 0, 0);
+        acc[2 * w] = E::mma16(ev, pop, acc[2 * w]);
+        acc[2 * w + 1] = E::mma16(od, pop, acc[2 * w + 1]);
       }
     } else {
       // k = 8 tokens per lane (4 of each tile, in the order the lane holds
-      // its scores): v_mfma_f32_16x16x32_bf16
-      const bf16x8_t pop =
-          __builtin_bit_cast(bf16x8_t, make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
+      // its scores): the 16x16x32 MFMA
+      const x8 pop = __builtin_bit_cast(x8, make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         uint32_t ev[4], od[4];
@@ -340,17 +378,15 @@ struct Stream {
           od[2 * t] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
           od[2 * t + 1] = __builtin_amdgcn_perm(v3, v2, 0x07060302u);
         }
-        acc[2 * w] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, make_uint4(ev[0], ev[1], ev[2], ev[3])), pop, acc[2 * w],
-            0, 0, 0);
-        acc[2 * w + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8_t, make_uint4(od[0], od[1], od[2], od[3])), pop,
-            acc[2 * w + 1], 0, 0, 0);
+        acc[2 * w] = E::mma32(__builtin_bit_cast(x8, make_uint4(ev[0], ev[1], ev[2], ev[3])), pop,
+                              acc[2 * w]);
+        acc[2 * w + 1] = E::mma32(__builtin_bit_cast(x8, make_uint4(od[0], od[1], od[2], od[3])),
+                                  pop, acc[2 * w + 1]);
       }
     }
   }
 
-  __device__ __forceinline__ void attend_chunk(const f32x4_t* s, ChunkBuf<D, TILES>& cb,
+  __device__ __forceinline__ void attend_chunk(const f32x4_t* s, Buf& cb,
                                                const Cursor& c) {
     if (c.j == c.nb - 1 && (c.T % (16 * TILES)) != 0)
       attend<true>(s, cb, c);
@@ -373,16 +409,16 @@ struct Stream {
         uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          d4[r] = make_uint4(pack_bf16x2(acc[0][r] * inv, acc[1][r] * inv),
-                             pack_bf16x2(acc[2][r] * inv, acc[3][r] * inv),
-                             pack_bf16x2(acc[4][r] * inv, acc[5][r] * inv),
-                             pack_bf16x2(acc[6][r] * inv, acc[7][r] * inv));
+          d4[r] = make_uint4(E::pack2(acc[0][r] * inv, acc[1][r] * inv),
+                             E::pack2(acc[2][r] * inv, acc[3][r] * inv),
+                             E::pack2(acc[4][r] * inv, acc[5][r] * inv),
+                             E::pack2(acc[6][r] * inv, acc[7][r] * inv));
       } else {
         uint2* d2 = reinterpret_cast<uint2*>(dst);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          d2[r] = make_uint2(pack_bf16x2(acc[0][r] * inv, acc[1][r] * inv),
-                             pack_bf16x2(acc[2][r] * inv, acc[3][r] * inv));
+          d2[r] = make_uint2(E::pack2(acc[0][r] * inv, acc[1][r] * inv),
+                             E::pack2(acc[2][r] * inv, acc[3][r] * inv));
       }
     } else {
       const int64_t slot = partial_slot(c.b, g, unit, p.pool.kv_heads);
@@ -401,7 +437,7 @@ struct Stream {
   }
 };
 
-template <int D, int TILES, bool APPEND>
+template <typename E, int D, int TILES, bool APPEND>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ int32_t prefix[];
   __shared__ int32_t scan[kThreads];
@@ -428,10 +464,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   cur.load_seq(prefix, lens, poss);
   cur.j = uni((int)(c0 - prefix[cur.b]));
 
-  Stream<D, TILES, APPEND> st(p, lane, g, unit);
+  Stream<E, D, TILES, APPEND> st(p, lane, g, unit);
   st.reset();
   st.load_q(cur);
-  ChunkBuf<D, TILES> cb;
+  ChunkBuf<E, D, TILES> cb;
   int ph[TILES], ph_nx[TILES], ph_n2[TILES];
   st.fetch_phys(cur, ph);
   st.issue_k(cb, cur, ph);
@@ -485,17 +521,28 @@ size_t mfma_lds_bytes(int batch) { return sizeof(int32_t) * (size_t)(batch + 1);
 }  // namespace
 
 bool mfma_supported(const kv_pool* pool, int group) {
-  return pool->dtype == PAGEDKV_BF16 && (pool->head_dim == 64 || pool->head_dim == 128) &&
+  return (pool->dtype == PAGEDKV_BF16 || pool->dtype == PAGEDKV_F16) &&
+         (pool->head_dim == 64 || pool->head_dim == 128) &&
          pool->block_size % 16 == 0 && group >= 1 && group <= kMaxGroup;
 }
 
 int mfma_chunk_tokens() { return 16 * kTilesPerStep; }
 
 namespace {
-template <int D, bool APPEND>
+template <typename E, int D, bool APPEND>
 void launch_one(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((decode_mfma_kernel<D, kTilesPerStep, APPEND>), dim3(wgs), dim3(kThreads), lds,
-                     s, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<E, D, kTilesPerStep, APPEND>), dim3(wgs), dim3(kThreads),
+                     lds, s, p);
+}
+
+template <typename E>
+void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
+  const bool append = p.positions != nullptr;
+  if (p.pool.head_dim == 128) {
+    if (append) launch_one<E, 128, true>(p, wgs, lds, s); else launch_one<E, 128, false>(p, wgs, lds, s);
+  } else {
+    if (append) launch_one<E, 64, true>(p, wgs, lds, s); else launch_one<E, 64, false>(p, wgs, lds, s);
+  }
 }
 }  // namespace
 
@@ -503,8 +550,8 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   const size_t lds = mfma_lds_bytes(p.batch);
   // every instantiation has the same resources: size the grid by one
   const void* fn = p.pool.head_dim == 128
-                       ? reinterpret_cast<const void*>(&decode_mfma_kernel<128, kTilesPerStep, false>)
-                       : reinterpret_cast<const void*>(&decode_mfma_kernel<64, kTilesPerStep, false>);
+      ? reinterpret_cast<const void*>(&decode_mfma_kernel<Bf16Ops, 128, kTilesPerStep, false>)
+      : reinterpret_cast<const void*>(&decode_mfma_kernel<Bf16Ops, 64, kTilesPerStep, false>);
   int wgs = 0;
   hipError_t e = resident_workgroups(fn, kThreads, lds, &wgs);
   if (e != hipSuccess) return e;
@@ -524,12 +571,10 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
     p.units = (int)(useful < 1 ? 1 : useful);
     wgs = (p.units * p.pool.kv_heads + kWaves - 1) / kWaves;
   }
-  const bool append = p.positions != nullptr;
-  if (p.pool.head_dim == 128) {
-    if (append) launch_one<128, true>(p, wgs, lds, s); else launch_one<128, false>(p, wgs, lds, s);
-  } else {
-    if (append) launch_one<64, true>(p, wgs, lds, s); else launch_one<64, false>(p, wgs, lds, s);
-  }
+  if (p.dtype == PAGEDKV_F16)
+    launch_typed<F16Ops>(p, wgs, lds, s);
+  else
+    launch_typed<Bf16Ops>(p, wgs, lds, s);
   return hipGetLastError();
 }
 

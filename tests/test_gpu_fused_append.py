@@ -19,14 +19,13 @@ import oracle
 import paged_kv_cache_resolve_amd as pk
 from workloads import make_workload
 
-from gpu_helpers import DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say
+from gpu_helpers import NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say
 
 pytestmark = [
     pytest.mark.gpu,
     pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU"),
 ]
 
-NAN_BITS = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0)}
 
 
 def poison_append_slots(w, positions):
@@ -93,6 +92,8 @@ SHAPES = [
     ("bf16", 16, 1, 128, 16),
     ("bf16", 8, 2, 64, 8),
     ("f32", 8, 2, 64, 16),
+    ("f16", 8, 2, 128, 16),
+    ("f16", 8, 2, 64, 8),
 ]
 
 
@@ -117,8 +118,8 @@ def test_fused_position_cases(dtype, Hq, Hkv, D, BS):
     pk.kv_append(two.pool, w.layer, two.k_new, two.v_new, two.tables, pos)
     out2 = two.decode()
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
-                       out2.view(torch.int16) if out2.dtype == torch.bfloat16 else out2), \
+    assert torch.equal(out.view(torch.int16) if out.element_size() == 2 else out,
+                       out2.view(torch.int16) if out2.element_size() == 2 else out2), \
         "fused output differs from append + decode"
     assert not dev_to_np(out)[8].any(), "empty sequence must give a zero row"
 

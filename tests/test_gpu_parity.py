@@ -15,7 +15,7 @@ import oracle
 import paged_kv_cache_resolve_amd as pk
 from workloads import make_workload
 
-from gpu_helpers import (DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say,
+from gpu_helpers import (NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say,
                          t_dtype)
 
 pytestmark = [
@@ -23,7 +23,6 @@ pytestmark = [
     pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU"),
 ]
 
-NAN_BITS = {"f32": np.float32(np.nan), "bf16": np.uint16(0x7FC0)}
 
 
 def poison(w):
@@ -218,6 +217,11 @@ EDGE_CASES = [
     ("bf16", 6, 2, 96, 16),     # generic bf16 (head_dim 96)
     ("f32", 4, 4, 64, 16),      # generic fp32, MHA
     ("f32", 32, 8, 128, 16),    # generic fp32, G = 4
+    ("f16", 8, 2, 128, 16),     # MFMA fp16, G = 4
+    ("f16", 14, 2, 64, 32),     # MFMA fp16, G = 7
+    ("f16", 16, 1, 128, 16),    # MFMA fp16, G = 16
+    ("f16", 8, 2, 64, 8),       # generic fp16 (block size 8)
+    ("f16", 6, 2, 96, 16),      # generic fp16 (head_dim 96)
 ]
 
 
@@ -234,7 +238,7 @@ def test_decode_edge_lengths_with_poison(dtype, Hq, Hkv, D, BS):
     assert not dev_to_np(out)[zero_rows].any(), "empty sequences must give zero rows"
 
 
-@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("f32", 64, 16)])
+@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("f32", 64, 16), ("f16", 128, 16)])
 def test_decode_block_permutation_invariance(dtype, D, BS):
     say(f"decode permutation invariance {dtype}")
     w = custom(dtype, 9, 8, 2, D, BS, [300, 1, 17, 0, 900, 64, 33, 2048, 5], nb_slack=40)
@@ -279,12 +283,13 @@ def test_decode_rejects_mismatched_dtype():
                                   dw.tables, dw.lens, 0.125)
 
 
-def test_output_dtype_rounding_bf16():
-    """bf16 outputs are the fp32 result rounded to nearest even: the GPU
-    output must be one of the two bf16 neighbours of the fp64 oracle value
-    (the fp32 accumulation error is far below the bf16 spacing here)."""
-    say("decode bf16 rounding")
-    w = custom("bf16", 2, 4, 4, 64, 16, [1, 1])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_output_dtype_rounding(dtype):
+    """16-bit outputs are the fp32 result rounded to nearest even.  With one
+    cached token the softmax weight is exactly 1, so the output must be the
+    single V row, bit for bit (for fp16 also through the probability scale)."""
+    say(f"decode {dtype} rounding")
+    w = custom(dtype, 2, 4, 4, 64, 16, [1, 1])
     dw = DeviceWorkload(w)
     out = dev_to_np(dw.decode())
     # T = 1: the output is exactly the single V row (weight 1), so bits match

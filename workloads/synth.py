@@ -37,6 +37,7 @@ CONFIG_NAMES = {
     3: "long_context_bf16",
     4: "high_concurrency_bf16",
     5: "llama8b_decode_f32",
+    6: "llama8b_decode_f16",
 }
 
 # Sequences' context lengths count the token appended in this step: the new
@@ -54,6 +55,9 @@ _SPECS = {
             lens=("bimodal", 0.7, (16, 512), (4096, 16384)), NB="1.1x", tables="perm"),
     # the Llama-8B-shaped layer of workload 2 with an fp32 cache
     5: dict(dtype="f32", S=64, Hq=32, Hkv=8, D=128, BS=16, L=1, layer=0,
+            lens=("lognormal", 2048.0, 0.5, 128, 8192), NB="1.1x", tables="perm"),
+    # ... and with an fp16 cache
+    6: dict(dtype="f16", S=64, Hq=32, Hkv=8, D=128, BS=16, L=1, layer=0,
             lens=("lognormal", 2048.0, 0.5, 128, 8192), NB="1.1x", tables="perm"),
 }
 
