@@ -123,12 +123,12 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
 #pragma unroll
     for (int h = 0; h < kMaxGroup; ++h) s[h] = 0.f;
     for (int d0 = 0; d0 < D; d0 += 4 * kKBatch) {
+      // Unconditional loads (a lane past T reads row 0 of the pool, a piece
+      // past D re-reads the row's last piece; both are discarded below), so
+      // that the whole batch is in flight before the first use.
       float4 kk[kKBatch];
 #pragma unroll
-      for (int u = 0; u < kKBatch; ++u) {
-        const int d = d0 + 4 * u;
-        kk[u] = valid && d < D ? load4(pool + row + d) : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
+      for (int u = 0; u < kKBatch; ++u) kk[u] = load4(pool + row + min(d0 + 4 * u, D - 4));
 #pragma unroll
       for (int u = 0; u < kKBatch; ++u) {
         const int d = d0 + 4 * u;
@@ -172,10 +172,7 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
                           (uint32_t)__builtin_amdgcn_readlane((int)row_lo, t);
         const TS* vrow = pool + r + p.pool.kv_stride;
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          const int d = lane + 64 * i;
-          v[u][i] = d < D ? load1(vrow + d) : 0.f;
-        }
+        for (int i = 0; i < DPL; ++i) v[u][i] = load1(vrow + min(lane + 64 * i, D - 1));
       }
 #pragma unroll
       for (int u = 0; u < VB; ++u) {

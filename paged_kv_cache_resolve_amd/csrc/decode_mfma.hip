@@ -196,6 +196,9 @@ struct Cursor {
 // written by the merge pass).
 template <typename E, int D, int TILES, bool APPEND>
 struct Stream {
+  static constexpr int kTiles = TILES;
+  static constexpr int kChunk = 16 * TILES;   // tokens per chunk
+  static constexpr bool kAppend = APPEND;
   using x8 = typename E::x8;
   using Buf = ChunkBuf<E, D, TILES>;
   static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
@@ -437,13 +440,221 @@ struct Stream {
   }
 };
 
-template <typename E, int D, int TILES, bool APPEND>
+// fp32 pools: v_mfma_f32_16x16x4_f32 (full fp32 products), one 16-token
+// tile per chunk, so that a chunk moves as many bytes as a bf16 one.
+//  * QK: the sum over head_dim is taken in the order (i, c): at step (i, c)
+//    lane (token n, quad) feeds K[n][16*i + 4*quad + c] and lane (head n,
+//    quad) feeds q[n][16*i + 4*quad + c].  Load i of a lane is then the
+//    float4 at dim 16*i + 4*quad of its row, and the four quads of a row
+//    read 64 contiguous bytes per instruction.  Four accumulators (one per
+//    c) keep the dependent MFMA chains short.
+//  * PV: step r (0..3) takes tokens 4*quad + r.  Its B operand is the lane's
+//    own probability of token 4*quad + r (the score layout, so no data moves
+//    between lanes) and its A operand holds V dims 4*n + e + 64*h of those
+//    tokens for output block (h, e): each lane reads float4s at dims
+//    4*n + 64*h of its four rows.  Block (h, e) accumulates out^T rows i ->
+//    dim 64*h + 4*i + e, so lane (head n, quad) ends with dims
+//    64*h + 16*quad + 4*r + e: 16 contiguous dims per h.
+//  * Probabilities stay in fp32.
+template <int D, bool APPEND>
+struct StreamF32 {
+  static constexpr int kTiles = 1;
+  static constexpr int kChunk = 16;
+  static constexpr bool kAppend = APPEND;
+  static constexpr int KQ = D / 4;    // K floats per lane per tile
+  static constexpr int NH = D / 64;   // float4 V loads per row per lane
+  static constexpr int NB = D / 16;   // output blocks (h, e)
+  struct Buf {
+    float4 k[KQ / 4];
+    float4 v[4][NH];
+  };
+
+  const DecodeParams& p;
+  const int lane, n, quad;
+  const int g;
+  const int64_t unit;
+
+  float qop[KQ];
+  f32x4_t acc[NB];
+  float m, l;
+
+  __device__ StreamF32(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
+      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), unit(unit_) {}
+
+  __device__ __forceinline__ void reset() {
+#pragma unroll
+    for (int c = 0; c < NB; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    m = -INFINITY;
+    l = 0.f;
+  }
+
+  // Columns n >= G repeat head G-1 (see the 16-bit stream).
+  __device__ __forceinline__ void load_q(const Cursor& c) {
+    const int G = p.group;
+    const float4* qrow = reinterpret_cast<const float4*>(
+        static_cast<const float*>(p.q) +
+        ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + min(n, G - 1)) * D + 4 * quad);
+#pragma unroll
+    for (int i = 0; i < KQ / 4; ++i) {
+      const float4 v = qrow[4 * i];   // dims 16*i + 4*quad .. + 3
+      qop[4 * i] = v.x;
+      qop[4 * i + 1] = v.y;
+      qop[4 * i + 2] = v.z;
+      qop[4 * i + 3] = v.w;
+    }
+  }
+
+  __device__ __forceinline__ void fetch_phys(const Cursor& c, int* ph) const {
+    const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
+    ph[0] = uni(trow[(c.j * 16) / p.pool.block_size]);
+  }
+
+  __device__ __forceinline__ const char* tile_base(const Cursor& c, const int* ph) const {
+    const int tok = c.j * 16;
+    return p.pool.base + 4 * ((int64_t)p.layer * p.pool.layer_stride +
+                              (int64_t)g * p.pool.head_stride +
+                              (int64_t)ph[0] * p.pool.block_stride +
+                              (int64_t)(tok % p.pool.block_size) * D);
+  }
+
+  __device__ __forceinline__ const char* new_row(const Cursor& c, int kv) const {
+    return static_cast<const char*>(kv ? p.v_new : p.k_new) +
+           4 * ((int64_t)c.b * p.pool.kv_heads + g) * D;
+  }
+
+  __device__ __forceinline__ void issue_k(Buf& cb, const Cursor& c, const int* ph) const {
+    const char* kl = tile_base(c, ph) + (uint32_t)(4 * (n * D + 4 * quad));
+    if constexpr (APPEND) {
+      if (c.j * 16 + n == c.pos) kl = new_row(c, 0) + 4 * 4 * quad;
+    }
+#pragma unroll
+    for (int i = 0; i < KQ / 4; ++i) {
+      uint4 u;
+      stream_load(u, kl + 64 * i);
+      cb.k[i] = __builtin_bit_cast(float4, u);
+    }
+  }
+
+  __device__ __forceinline__ void issue_v(Buf& cb, const Cursor& c, const int* ph) const {
+    const char* vl = tile_base(c, ph) + 4 * p.pool.kv_stride + (uint32_t)(4 * (4 * quad * D + 4 * n));
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const char* row = vl + 4 * r * D;
+      if constexpr (APPEND) {
+        if (c.j * 16 + 4 * quad + r == c.pos) row = new_row(c, 1) + 4 * 4 * n;
+      }
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        uint4 u;
+        stream_load(u, row + 4 * 64 * h);
+        cb.v[r][h] = __builtin_bit_cast(float4, u);
+      }
+    }
+  }
+
+  __device__ __forceinline__ void qk(const Buf& cb, f32x4_t* s) const {
+    f32x4_t a[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) a[w] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KQ / 4; ++i) {
+      a[0] = __builtin_amdgcn_mfma_f32_16x16x4f32(cb.k[i].x, qop[4 * i], a[0], 0, 0, 0);
+      a[1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cb.k[i].y, qop[4 * i + 1], a[1], 0, 0, 0);
+      a[2] = __builtin_amdgcn_mfma_f32_16x16x4f32(cb.k[i].z, qop[4 * i + 2], a[2], 0, 0, 0);
+      a[3] = __builtin_amdgcn_mfma_f32_16x16x4f32(cb.k[i].w, qop[4 * i + 3], a[3], 0, 0, 0);
+    }
+    s[0] = (a[0] + a[1]) + (a[2] + a[3]);
+  }
+
+  template <bool TAIL>
+  __device__ __forceinline__ void attend(const f32x4_t* s, Buf& cb, const Cursor& c) {
+    float sv[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      sv[r] = s[0][r] * p.scale_log2;
+      if (TAIL && c.j * 16 + 4 * quad + r >= c.T) sv[r] = -INFINITY;
+    }
+    float bmax = fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]));
+    bmax = max_x32(max_x16(bmax));
+    {
+      const float mn = fmaxf(m, bmax);
+      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+      for (int i = 0; i < NB; ++i) acc[i] *= alpha;
+      l *= alpha;
+      m = mn;
+    }
+    float pr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pr[r] = __builtin_amdgcn_exp2f(sv[r] - m);
+    l += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    if (TAIL) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (c.j * 16 + 4 * quad + r >= c.T)
+#pragma unroll
+          for (int h = 0; h < NH; ++h) cb.v[r][h] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        acc[4 * h + 0] = __builtin_amdgcn_mfma_f32_16x16x4f32(cb.v[r][h].x, pr[r], acc[4 * h + 0], 0, 0, 0);
+        acc[4 * h + 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(cb.v[r][h].y, pr[r], acc[4 * h + 1], 0, 0, 0);
+        acc[4 * h + 2] = __builtin_amdgcn_mfma_f32_16x16x4f32(cb.v[r][h].z, pr[r], acc[4 * h + 2], 0, 0, 0);
+        acc[4 * h + 3] = __builtin_amdgcn_mfma_f32_16x16x4f32(cb.v[r][h].w, pr[r], acc[4 * h + 3], 0, 0, 0);
+      }
+  }
+
+  __device__ __forceinline__ void attend_chunk(const f32x4_t* s, Buf& cb, const Cursor& c) {
+    if (c.j == c.nb - 1 && (c.T % 16) != 0)
+      attend<true>(s, cb, c);
+    else
+      attend<false>(s, cb, c);
+  }
+
+  __device__ void flush(const Cursor& c, bool whole) {
+    const int G = p.group;
+    const float lt = sum_x32(sum_x16(l));
+    if (n >= G) return;
+    // lane holds dim 64*h + 16*quad + 4*r + e of head n as acc[4*h + e][r]
+    if (whole) {
+      const float inv = 1.0f / lt;
+      float* dst = static_cast<float*>(p.out) +
+                   ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + n) * D + 16 * quad;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<float4*>(dst + 64 * h + 4 * r) =
+              make_float4(acc[4 * h][r] * inv, acc[4 * h + 1][r] * inv, acc[4 * h + 2][r] * inv,
+                          acc[4 * h + 3][r] * inv);
+    } else {
+      const int64_t slot = partial_slot(c.b, g, unit, p.pool.kv_heads);
+      float* o = p.ws_o + (slot * G + n) * D + 16 * quad;
+#pragma unroll
+      for (int h = 0; h < NH; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *reinterpret_cast<float4*>(o + 64 * h + 4 * r) =
+              make_float4(acc[4 * h][r], acc[4 * h + 1][r], acc[4 * h + 2][r], acc[4 * h + 3][r]);
+      if (quad == 0) {
+        p.ws_ml[(slot * G + n) * 2 + 0] = m;
+        p.ws_ml[(slot * G + n) * 2 + 1] = lt;
+      }
+    }
+  }
+};
+
+// One persistent kernel for every stream type S (16-bit or fp32 elements).
+template <typename S>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ int32_t prefix[];
   __shared__ int32_t scan[kThreads];
   const int H = p.pool.kv_heads;
 
-  block_chunk_prefix<kThreads>(p.context_lens, p.batch, 16 * TILES, prefix, scan);
+  constexpr int TILES = S::kTiles;
+  block_chunk_prefix<kThreads>(p.context_lens, p.batch, S::kChunk, prefix, scan);
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= p.batch; i += kThreads) p.ws_prefix[i] = prefix[i];
 
@@ -458,16 +669,16 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int rem = (int)(wave_begin(unit + 1, C, Ue) - c0);   // >= 1
 
   const const_i32_ptr lens = (const_i32_ptr)p.context_lens;
-  const const_i32_ptr poss = APPEND ? (const_i32_ptr)p.positions : nullptr;
+  const const_i32_ptr poss = S::kAppend ? (const_i32_ptr)p.positions : nullptr;
   Cursor cur;
   cur.b = uni(seq_of_chunk(prefix, p.batch, c0));
   cur.load_seq(prefix, lens, poss);
   cur.j = uni((int)(c0 - prefix[cur.b]));
 
-  Stream<E, D, TILES, APPEND> st(p, lane, g, unit);
+  S st(p, lane, g, unit);
   st.reset();
   st.load_q(cur);
-  ChunkBuf<E, D, TILES> cb;
+  typename S::Buf cb;
   int ph[TILES], ph_nx[TILES], ph_n2[TILES];
   st.fetch_phys(cur, ph);
   st.issue_k(cb, cur, ph);
@@ -521,27 +732,39 @@ size_t mfma_lds_bytes(int batch) { return sizeof(int32_t) * (size_t)(batch + 1);
 }  // namespace
 
 bool mfma_supported(const kv_pool* pool, int group) {
-  return (pool->dtype == PAGEDKV_BF16 || pool->dtype == PAGEDKV_F16) &&
-         (pool->head_dim == 64 || pool->head_dim == 128) &&
+  return (pool->head_dim == 64 || pool->head_dim == 128) &&
          pool->block_size % 16 == 0 && group >= 1 && group <= kMaxGroup;
 }
 
 int mfma_chunk_tokens() { return 16 * kTilesPerStep; }
 
 namespace {
-template <typename E, int D, bool APPEND>
+template <typename S>
 void launch_one(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL((decode_mfma_kernel<E, D, kTilesPerStep, APPEND>), dim3(wgs), dim3(kThreads),
-                     lds, s, p);
+  hipLaunchKernelGGL((decode_mfma_kernel<S>), dim3(wgs), dim3(kThreads), lds, s, p);
 }
 
 template <typename E>
 void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
   const bool append = p.positions != nullptr;
+  constexpr int T = kTilesPerStep;
   if (p.pool.head_dim == 128) {
-    if (append) launch_one<E, 128, true>(p, wgs, lds, s); else launch_one<E, 128, false>(p, wgs, lds, s);
+    if (append) launch_one<Stream<E, 128, T, true>>(p, wgs, lds, s);
+    else launch_one<Stream<E, 128, T, false>>(p, wgs, lds, s);
   } else {
-    if (append) launch_one<E, 64, true>(p, wgs, lds, s); else launch_one<E, 64, false>(p, wgs, lds, s);
+    if (append) launch_one<Stream<E, 64, T, true>>(p, wgs, lds, s);
+    else launch_one<Stream<E, 64, T, false>>(p, wgs, lds, s);
+  }
+}
+
+void launch_f32(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
+  const bool append = p.positions != nullptr;
+  if (p.pool.head_dim == 128) {
+    if (append) launch_one<StreamF32<128, true>>(p, wgs, lds, s);
+    else launch_one<StreamF32<128, false>>(p, wgs, lds, s);
+  } else {
+    if (append) launch_one<StreamF32<64, true>>(p, wgs, lds, s);
+    else launch_one<StreamF32<64, false>>(p, wgs, lds, s);
   }
 }
 }  // namespace
@@ -550,8 +773,9 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   const size_t lds = mfma_lds_bytes(p.batch);
   // every instantiation has the same resources: size the grid by one
   const void* fn = p.pool.head_dim == 128
-      ? reinterpret_cast<const void*>(&decode_mfma_kernel<Bf16Ops, 128, kTilesPerStep, false>)
-      : reinterpret_cast<const void*>(&decode_mfma_kernel<Bf16Ops, 64, kTilesPerStep, false>);
+      ? reinterpret_cast<const void*>(&decode_mfma_kernel<Stream<Bf16Ops, 128, kTilesPerStep, false>>)
+      : reinterpret_cast<const void*>(&decode_mfma_kernel<Stream<Bf16Ops, 64, kTilesPerStep, false>>);
+  const int chunk = p.dtype == PAGEDKV_F32 ? 16 : 16 * kTilesPerStep;
   int wgs = 0;
   hipError_t e = resident_workgroups(fn, kThreads, lds, &wgs);
   if (e != hipSuccess) return e;
@@ -565,13 +789,15 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   if (p.min_chunks < 1) p.min_chunks = 2;
   // no more units than the largest possible chunk count can keep busy
   const int64_t max_chunks = (int64_t)p.batch *
-      (((int64_t)p.max_blocks_per_seq * p.pool.block_size + 16 * kTilesPerStep - 1) / (16 * kTilesPerStep));
+      (((int64_t)p.max_blocks_per_seq * p.pool.block_size + chunk - 1) / chunk);
   const int64_t useful = (max_chunks + p.min_chunks - 1) / p.min_chunks;
   if (useful < p.units) {
     p.units = (int)(useful < 1 ? 1 : useful);
     wgs = (p.units * p.pool.kv_heads + kWaves - 1) / kWaves;
   }
-  if (p.dtype == PAGEDKV_F16)
+  if (p.dtype == PAGEDKV_F32)
+    launch_f32(p, wgs, lds, s);
+  else if (p.dtype == PAGEDKV_F16)
     launch_typed<F16Ops>(p, wgs, lds, s);
   else
     launch_typed<Bf16Ops>(p, wgs, lds, s);

@@ -92,6 +92,8 @@ SHAPES = [
     ("bf16", 16, 1, 128, 16),
     ("bf16", 8, 2, 64, 8),
     ("f32", 8, 2, 64, 16),
+    ("f32", 8, 2, 128, 16),
+    ("f32", 8, 2, 64, 8),
     ("f16", 8, 2, 128, 16),
     ("f16", 8, 2, 64, 8),
 ]

@@ -215,8 +215,11 @@ EDGE_CASES = [
     ("bf16", 4, 4, 128, 64),    # MFMA, G = 1
     ("bf16", 8, 2, 64, 8),      # generic bf16 (block size 8)
     ("bf16", 6, 2, 96, 16),     # generic bf16 (head_dim 96)
-    ("f32", 4, 4, 64, 16),      # generic fp32, MHA
-    ("f32", 32, 8, 128, 16),    # generic fp32, G = 4
+    ("f32", 4, 4, 64, 16),      # MFMA fp32, MHA
+    ("f32", 32, 8, 128, 16),    # MFMA fp32, G = 4
+    ("f32", 14, 2, 128, 32),    # MFMA fp32, G = 7
+    ("f32", 8, 2, 64, 8),       # generic fp32 (block size 8)
+    ("f32", 6, 2, 96, 16),      # generic fp32 (head_dim 96)
     ("f16", 8, 2, 128, 16),     # MFMA fp16, G = 4
     ("f16", 14, 2, 64, 32),     # MFMA fp16, G = 7
     ("f16", 16, 1, 128, 16),    # MFMA fp16, G = 16
