@@ -20,6 +20,9 @@ Parity status per function:
                                        to per-layer / per-token kv_append)
   attend, paged_attention_decode       pinned (torch SDPA in float64,
                                        brute force, closed forms, invariants)
+  dense_masked_decode                  pinned (equal to the paged decode on
+                                       the gathered batch; brute force with
+                                       random masks; masked rows ignored)
   waste arithmetic                     pinned (the page's worked numbers)
   FreeBlockStack                       pinned (the page's LIFO semantics)
   BlockManagerModel (manager.py)       pinned (the pages' waste figures and
@@ -32,6 +35,7 @@ from .paged import (  # noqa: F401
     FreeBlockStack,
     OutOfBlocks,
     attend,
+    dense_masked_decode,
     gather_sequence,
     kv_append,
     kv_append_layers,

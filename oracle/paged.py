@@ -267,6 +267,28 @@ def paged_attention_decode(pool: np.ndarray, dtype: str, layer: int,
     return out
 
 
+def dense_masked_decode(k: np.ndarray, v: np.ndarray, mask: np.ndarray, q: np.ndarray,
+                        dtype: str, scale: float, seqs=None) -> np.ndarray:
+    """Attention over gathered, padded K/V: k and v are [S, max_len, Hkv, D]
+    as the batched gather returns them, mask [S, max_len] marks the cached
+    tokens; every position whose mask is 0 is left out of the softmax.
+    Returns [S, Hq, D] float64 (rows of sequences not in ``seqs`` stay zero;
+    a sequence with no unmasked position gives zeros).
+
+    [mini-infer] "Zero-Copy Batched Attention Gather": the gathered batch is
+    the input of the attention for all active sequences at once; the mask
+    tells the cached tokens from the padding.
+    """
+    S, Hq, D = q.shape
+    scale64 = float(np.float32(scale))
+    out = np.zeros((S, Hq, D), dtype=np.float64)
+    for b in (range(S) if seqs is None else seqs):
+        keep = np.nonzero(np.asarray(mask[b]) != 0)[0]
+        out[b] = attend(widen(q[b], dtype), widen(k[b][keep], dtype), widen(v[b][keep], dtype),
+                        scale64)
+    return out
+
+
 # ----------------------------------------------------------------------------
 # Memory waste ([mini-infer] "The Problem" and "Memory Waste Analysis")
 # ----------------------------------------------------------------------------

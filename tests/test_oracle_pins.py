@@ -477,6 +477,50 @@ def check_block_manager_random_invariants():
         assert st["blocks_free"] + st["blocks_used"] == NB
 
 
+def check_dense_masked_decode():
+    """The gather-then-dense path of [mini-infer] v0.2.0 gives the paged
+    decode's result: gathered K/V with the gather's mask through the dense
+    decode equal, bit for bit, the paged decode (both take the same rows to
+    the same attention); with random non-prefix masks the dense decode
+    equals per-element loops over the unmasked rows; and the values of
+    masked rows do not matter."""
+    rng = np.random.default_rng(21)
+    for dtype in ("f32", "bf16", "f16"):
+        c = _random_paged_case(rng, S=5, Hq=6, Hkv=2, D=8, BS=4, L=2, layer=1, max_T=19,
+                               dtype=dtype)
+        max_len = int(c["lens"].max())
+        k, v, mask = oracle.paged_kv_gather(c["pool"], 1, c["tables"], c["lens"], max_len)
+        dense = oracle.dense_masked_decode(k, v, mask, c["q"], dtype, 0.37)
+        paged = oracle.paged_attention_decode(c["pool"], dtype, 1, c["tables"], c["lens"],
+                                              c["q"], 0.37)
+        assert dense.tobytes() == paged.tobytes()
+    S, L, Hq, Hkv, D = 3, 7, 4, 2, 2
+    k = rng.integers(-3, 4, size=(S, L, Hkv, D)).astype(np.float32)
+    v = rng.integers(-3, 4, size=(S, L, Hkv, D)).astype(np.float32)
+    q = rng.integers(-2, 3, size=(S, Hq, D)).astype(np.float32)
+    mask = (rng.random((S, L)) < 0.5).astype(np.uint8)
+    mask[0] = 0                                   # nothing cached: zero row
+    mask[1, 3] = 1
+    got = oracle.dense_masked_decode(k, v, mask, q, "f32", 0.5)
+    for b in range(S):
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            ts = [t for t in range(L) if mask[b, t]]
+            if not ts:
+                assert not got[b, h].any()
+                continue
+            sc = [0.5 * sum(float(q[b, h, d]) * float(k[b, t, g, d]) for d in range(D)) for t in ts]
+            mx = max(sc)
+            w = [math.exp(x - mx) for x in sc]
+            for d in range(D):
+                want = sum(wi * float(v[b, t, g, d]) for wi, t in zip(w, ts)) / sum(w)
+                assert abs(got[b, h, d] - want) < 1e-12
+    k2, v2 = k.copy(), v.copy()
+    k2[mask == 0] = 1e3
+    v2[mask == 0] = -1e3
+    assert oracle.dense_masked_decode(k2, v2, mask, q, "f32", 0.5).tobytes() == got.tobytes()
+
+
 def check_widen_f16():
     """Every finite binary16 pattern widens to the value its bits define;
     a few by hand: 1, -2, 0.25, the largest finite 65504, the smallest
@@ -521,6 +565,7 @@ ALL_CHECKS = [
     ("block_manager_random_invariants", check_block_manager_random_invariants),
     ("widen", check_widen),
     ("widen_f16", check_widen_f16),
+    ("dense_masked_decode", check_dense_masked_decode),
 ]
 
 
@@ -537,6 +582,7 @@ _orig_l2p = P.logical_to_physical
 _orig_attend = P.attend
 _orig_gather_seq = P.gather_sequence
 _orig_widen = P.widen
+_orig_dense = P.dense_masked_decode
 
 
 def _mut_l2p_swapped(table_row, t, bs):
@@ -615,6 +661,10 @@ def _mut_widen_f16_as_bf16(x, dtype):
     return _orig_widen(x, dtype)
 
 
+def _mut_dense_ignores_mask(k, v, mask, q, dtype, scale, seqs=None):
+    return _orig_dense(k, v, np.ones_like(mask), q, dtype, scale, seqs)
+
+
 def _mut_widen_low_half(x, dtype):
     if dtype == "bf16":
         return np.asarray(x, np.uint16).astype(np.float64)
@@ -637,6 +687,7 @@ MUTANTS = [
     ("waste_floor", "paged_waste_slots", _mut_waste_floor),
     ("widen_low_half", "widen", _mut_widen_low_half),
     ("widen_f16_as_bf16", "widen", _mut_widen_f16_as_bf16),
+    ("dense_ignores_mask", "dense_masked_decode", _mut_dense_ignores_mask),
 ]
 
 
