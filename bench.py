@@ -418,6 +418,28 @@ def main(argv=None) -> int:
             gb = gather_bytes(w, max_len)
             result["gather"] = {"ms": round(gms, 4), "bytes": gb,
                                 "GB_per_s": round(gb / (gms * 1e-3) / 1e9, 1)}
+            if w.dtype != "f32":
+                # the rest of the gather-then-attend path: dense decode over
+                # the padded batch (every max_len row, padding included)
+                dout = torch.empty_like(r["q"])
+                pk.dense_attention_decode(dout, r["q"], outs[0], outs[1], outs[2], w.scale)
+                for a, b in gev:
+                    a.record(stream)
+                    pk.dense_attention_decode(dout, r["q"], outs[0], outs[1], outs[2], w.scale)
+                    b.record(stream)
+                torch.cuda.synchronize()
+                dms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
+                e = 2
+                db = (2 * w.S * max_len * w.Hkv * w.D * e + w.S * max_len
+                      + 2 * w.S * w.Hq * w.D * e)
+                result["gather_then_dense"] = {
+                    "dense_ms": round(dms, 4), "dense_bytes": db,
+                    "dense_GB_per_s": round(db / (dms * 1e-3) / 1e9, 1),
+                    "total_ms": round(gms + dms, 4),
+                    "total_bytes": gb + db,
+                    "paged_step_ms": round(dec_avg_ms, 4),
+                    "total_over_paged": round((gms + dms) / dec_avg_ms, 2),
+                }
             del outs
         except torch.cuda.OutOfMemoryError:
             result["gather"] = None

@@ -296,6 +296,28 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new,
                                   int num_q_heads, float scale, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* Bytes of device workspace dense_attention_decode needs (0 for invalid
+ * arguments). */
+size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads, int head_dim);
+
+/* Decode over gathered, padded K/V: the attention that follows
+ * paged_kv_gather in [mini-infer] "Zero-Copy Batched Attention Gather"
+ * (the v0.2.0 path), kept to compare with the paged decode, which reads the
+ * pool in place.
+ *   out, q : device, [batch][num_q_heads][head_dim], dtype.
+ *   k, v   : device, [batch][max_len][kv_heads][head_dim], dtype (the gather's
+ *            outputs; values must be finite).
+ *   mask   : device, [batch][max_len] uint8; token t of sequence b takes part
+ *            iff mask[b][t] != 0.  A sequence with no such token gives zeros.
+ * Every one of the max_len rows is read, padding included.  Same arithmetic
+ * and tolerances as paged_attention_decode.  bf16 and fp16, head_dim 64 or
+ * 128, up to 16 query heads per KV head; otherwise PAGEDKV_ERR_UNSUPPORTED.
+ * workspace as for paged_attention_decode (256-byte aligned). */
+int dense_attention_decode(void* out, const void* q, const void* k, const void* v,
+                           const uint8_t* mask, int batch, int max_len, int kv_heads,
+                           int head_dim, int num_q_heads, pagedkv_dtype_t dtype, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
 /* Block-table resolution on its own ([vllmini] "PagedAttention Metaphor":
  * logical offsets resolved to physical page offsets on the fly).
  *   slots : device, [batch][max_len] int64; slots[b][t] =

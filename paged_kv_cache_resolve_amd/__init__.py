@@ -33,7 +33,7 @@ _L = _lib.load()
 __all__ = [
     "KVPool", "kv_pool_create", "BlockManager", "kv_append", "kv_append_layers", "kv_append_tokens",
     "paged_kv_gather", "paged_attention_decode",
-    "paged_attention_decode_append", "DecodePlan",
+    "paged_attention_decode_append", "DecodePlan", "dense_attention_decode",
     "paged_attention_workspace_bytes", "paged_kv_resolve", "PagedKVError", "OutOfBlocksError",
     "library",
 ]
@@ -305,11 +305,11 @@ def paged_attention_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int) 
 _WORKSPACES: dict = {}
 
 
-def _workspace(pool: KVPool, nbytes: int, stream: int) -> torch.Tensor:
-    key = (pool.device.index, stream)
+def _workspace(device: torch.device, nbytes: int, stream: int) -> torch.Tensor:
+    key = (device.index, stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=pool.device)
+        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
 
@@ -327,7 +327,7 @@ def _decode_args(out, q, pool, block_tables, context_lens, workspace):
     need = paged_attention_workspace_bytes(pool, batch, hq)
     stream = _stream(pool.device)
     if workspace is None:
-        workspace = _workspace(pool, need, stream)
+        workspace = _workspace(pool.device, need, stream)
     wp = _dev_tensor(workspace, "workspace", pool.device, torch.uint8)
     return batch, hq, qp, op, tp, mb, lp, wp, workspace.numel(), stream
 
@@ -386,7 +386,7 @@ class DecodePlan:
                                                                      context_lens, workspace)
         self.pool = pool
         self._keep = (out, q, block_tables, context_lens, k_new, v_new, positions,
-                      workspace if workspace is not None else _workspace(pool, wn, stream))
+                      workspace if workspace is not None else _workspace(pool.device, wn, stream))
         self._device = pool.device
         # the shared per-stream workspace may only be used on its own stream
         self._stream = None if workspace is not None else stream
@@ -413,6 +413,40 @@ class DecodePlan:
             raise RuntimeError("DecodePlan built on another stream; pass a workspace to share it")
         _check(self._fn(*self._args, stream), self._what)
         return self._keep[0]
+
+
+def dense_attention_decode(out: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           mask: torch.Tensor, scale: float, workspace=None) -> torch.Tensor:
+    """Decode over gathered, padded K/V (what paged_kv_gather returns): k and
+    v [batch, max_len, kv_heads, head_dim], mask uint8 [batch, max_len]
+    (token t of sequence b attended iff mask[b, t] != 0).  Every max_len row
+    is read.  bf16 and fp16."""
+    if q.dim() != 3 or k.dim() != 4:
+        raise ValueError("q must be [batch, num_q_heads, head_dim], k [batch, max_len, kv_heads, head_dim]")
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if not q.is_cuda:
+        raise ValueError("q must be a GPU tensor")
+    device = torch.device("cuda", q.get_device())
+    batch, hq, d = (int(x) for x in q.shape)
+    _, max_len, hkv, _ = (int(x) for x in k.shape)
+    shape = (batch, max_len, hkv, d)
+    qp = _dev_tensor(q, "q", device, q.dtype)
+    op = _dev_tensor(out, "out", device, q.dtype, q.shape)
+    kp = _dev_tensor(k, "k", device, q.dtype, shape)
+    vp = _dev_tensor(v, "v", device, q.dtype, shape)
+    mp = _dev_tensor(mask, "mask", device, torch.uint8, (batch, max_len))
+    need = _L.dense_attention_workspace_bytes(batch, hkv, hq, d)
+    if need == 0:
+        raise ValueError("num_q_heads must be a multiple of kv_heads")
+    stream = _stream(device)
+    if workspace is None:
+        workspace = _workspace(device, need, stream)
+    wp = _dev_tensor(workspace, "workspace", device, torch.uint8)
+    _check(_L.dense_attention_decode(op, qp, kp, vp, mp, batch, max_len, hkv, d, hq,
+                                     _DTYPES[q.dtype], ctypes.c_float(scale), wp,
+                                     workspace.numel(), stream), "dense_attention_decode")
+    return out
 
 
 def paged_kv_resolve(block_tables: torch.Tensor, context_lens: torch.Tensor, block_size: int,

@@ -69,6 +69,9 @@ SIGNATURES = {
     "paged_attention_decode_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int,
                                                _vp, _c_int, _c_int, ctypes.c_float, _vp, _c_size,
                                                _vp]),
+    "dense_attention_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
+    "dense_attention_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
+                                        _c_int, _c_int, ctypes.c_float, _vp, _c_size, _vp]),
     "paged_kv_resolve": (_c_int, [_vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp]),
     "pagedkv_status_string": (ctypes.c_char_p, [_c_int]),
 }

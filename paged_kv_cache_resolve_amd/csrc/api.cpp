@@ -290,6 +290,57 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
                      positions);
 }
 
+size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads, int head_dim) {
+  if (batch < 0 || kv_heads < 1 || num_q_heads < 1 || num_q_heads % kv_heads != 0 || head_dim < 1)
+    return 0;
+  return decode_workspace_bytes(batch, kv_heads, num_q_heads / kv_heads, head_dim);
+}
+
+int dense_attention_decode(void* out, const void* q, const void* k, const void* v,
+                           const uint8_t* mask, int batch, int max_len, int kv_heads,
+                           int head_dim, int num_q_heads, pagedkv_dtype_t dtype, float scale,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (batch < 0 || max_len < 0 || kv_heads < 1 || num_q_heads < 1 ||
+      num_q_heads % kv_heads != 0 || !isfinite(scale) || !valid_dtype(dtype) || head_dim < 1)
+    return PAGEDKV_ERR_INVALID_ARG;
+  if (batch == 0) return PAGEDKV_OK;
+  if (!out || !q || (max_len > 0 && (!k || !v || !mask))) return PAGEDKV_ERR_INVALID_ARG;
+  if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return PAGEDKV_ERR_INVALID_ARG;
+  const int group = num_q_heads / kv_heads;
+  if ((dtype != PAGEDKV_BF16 && dtype != PAGEDKV_F16) || (head_dim != 64 && head_dim != 128) ||
+      group > kMaxGroup || batch > kMaxBatchLds)
+    return PAGEDKV_ERR_UNSUPPORTED;
+  if ((int64_t)batch * ((max_len + 31) / 32) > INT32_MAX) return PAGEDKV_ERR_UNSUPPORTED;
+  const size_t need = decode_workspace_bytes(batch, kv_heads, group, head_dim);
+  if (!workspace || workspace_bytes < need) return PAGEDKV_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PAGEDKV_ERR_WORKSPACE;
+
+  DecodeParams p;
+  memset(&p, 0, sizeof(p));
+  // only the head geometry of the "pool" is used; K/V come from k and v
+  p.pool.kv_heads = kv_heads;
+  p.pool.head_dim = head_dim;
+  p.pool.block_size = 16;
+  p.max_blocks_per_seq = max_len > 0 ? (max_len + 15) / 16 : 1;
+  p.q = q;
+  p.out = out;
+  decode_workspace_carve(workspace, batch, kv_heads, group, head_dim, &p.ws_prefix, &p.ws_ml,
+                         &p.ws_o);
+  p.batch = batch;
+  p.num_q_heads = num_q_heads;
+  p.group = group;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  p.dtype = dtype;
+  p.k_dense = k ? k : q;   // max_len == 0: never read
+  p.v_dense = v ? v : q;
+  p.mask = mask;
+  p.dense_len = max_len;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_decode_mfma(p, s) != hipSuccess) return PAGEDKV_ERR_HIP;
+  return hip_status(launch_decode_merge(p, s));
+}
+
 int paged_kv_resolve(int64_t* slots, const int32_t* block_tables, int max_blocks_per_seq,
                      const int32_t* context_lens, int batch, int block_size, int max_len,
                      void* stream) {

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       if (k0 + u >= K) break;
+      if (mv[u] == -INFINITY) continue;   // a partial with every token masked (dense decode)
       const float Mn = fmaxf(M, mv[u]);
       const float sc = __builtin_amdgcn_exp2f(M - Mn);
       const float w = __builtin_amdgcn_exp2f(mv[u] - Mn);
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
       M = Mn;
     }
   }
-  const float inv = 1.0f / L;
+  const float inv = L > 0.f ? 1.0f / L : 0.f;   // nothing attended: zeros
 #pragma unroll
   for (int i = 0; i < kDimsPerLane; ++i) {
     const int d = lane + 64 * i;

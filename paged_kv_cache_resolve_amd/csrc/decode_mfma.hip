@@ -157,6 +157,7 @@ __device__ __forceinline__ float sum_x32(float x) {
 // K and V registers of one step: TILES tiles of 16 tokens.
 template <typename E, int D, int TILES>
 struct ChunkBuf {
+  uint32_t mk[TILES];   // dense batches: the mask bytes of the lane's 4 score tokens per tile (loaded with V)
   typename E::x8 k[TILES][D / 32];
   typename VRow<D>::type v[TILES][4];
 };
@@ -170,11 +171,12 @@ template <> __device__ __forceinline__ void zero_row<64>(uint2& v) { v = make_ui
 // else -1).  All fields are wave-uniform.
 struct Cursor {
   int b, j, nb, T, pos;
+  int dense_T;   // length of every sequence of a dense batch (lens is null then)
 
   __device__ __forceinline__ void load_seq(const int32_t* prefix, const_i32_ptr lens,
                                            const_i32_ptr positions) {
     nb = uni(prefix[b + 1] - prefix[b]);
-    T = uni(lens[b]);
+    T = lens ? uni(lens[b]) : dense_T;
     pos = positions ? uni(positions[b]) : -1;
   }
 
@@ -194,11 +196,16 @@ struct Cursor {
 // With APPEND, the row of a sequence's appended token is read from k_new /
 // v_new instead of the pool (a per-lane address choice; the pool row is
 // written by the merge pass).
-template <typename E, int D, int TILES, bool APPEND>
+// With DENSE, K and V are the contiguous, padded [batch][max_len][kv_heads]
+// [head_dim] tensors a batched gather produces, every sequence is max_len
+// long, and a token takes part only where its mask byte is non-zero (the
+// gather-then-attend path, for comparison with the paged one).
+template <typename E, int D, int TILES, bool APPEND, bool DENSE = false>
 struct Stream {
   static constexpr int kTiles = TILES;
   static constexpr int kChunk = 16 * TILES;   // tokens per chunk
   static constexpr bool kAppend = APPEND;
+  static constexpr bool kDense = DENSE;
   using x8 = typename E::x8;
   using Buf = ChunkBuf<E, D, TILES>;
   static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
@@ -242,6 +249,11 @@ struct Stream {
   // be partly empty) reuses tile 0's block: its loads stay inside the pool
   // and all of its tokens are masked.
   __device__ __forceinline__ void fetch_phys(const Cursor& c, int* ph) const {
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) ph[t] = 0;
+      return;
+    }
     const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
     const int tok0 = c.j * (16 * TILES);
     ph[0] = uni(trow[tok0 / p.pool.block_size]);
@@ -267,8 +279,27 @@ struct Stream {
            2 * ((int64_t)c.b * p.pool.kv_heads + g) * D;
   }
 
+  // Dense batches: byte address of token tok's row of head g (tokens past
+  // the end re-read the last row; they are masked).
+  __device__ __forceinline__ const char* dense_row(const void* base, const Cursor& c,
+                                                   int tok) const {
+    const int tc = min(tok, c.T - 1);
+    return static_cast<const char*>(base) +
+           2 * ((((int64_t)c.b * p.dense_len + tc) * p.pool.kv_heads + g) * D);
+  }
+
   __device__ __forceinline__ void issue_k(Buf& cb, const Cursor& c,
                                           const int* ph) const {
+    if constexpr (DENSE) {
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        const int tok0 = c.j * (16 * TILES) + 16 * t;
+        const char* kl = dense_row(p.k_dense, c, tok0 + n) + 2 * 8 * quad;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) cb.k[t][i] = stream_load8<x8>(kl + 64 * i);
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const char* kl = tile_base(c, ph, t) + (uint32_t)(2 * (n * D + 8 * quad));
@@ -282,6 +313,24 @@ struct Stream {
   }
   __device__ __forceinline__ void issue_v(Buf& cb, const Cursor& c,
                                           const int* ph) const {
+    if constexpr (DENSE) {
+      // The mask bytes of the lane's score tokens travel with V: the next
+      // chunk's V (and mask) is issued only after this chunk's softmax,
+      // while its K is issued before it.
+      const uint8_t* mrow = p.mask + (int64_t)c.b * p.dense_len;
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        uint32_t bits = 0;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int tok = c.j * (16 * TILES) + 16 * t + 4 * quad + r;
+          stream_load(cb.v[t][r], dense_row(p.v_dense, c, tok) + 2 * VD * n);
+          bits |= (uint32_t)mrow[min(tok, c.T - 1)] << (8 * r);
+        }
+        cb.mk[t] = bits;
+      }
+      return;
+    }
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       const char* vl = tile_base(c, ph, t) + 2 * p.pool.kv_stride +
@@ -321,30 +370,36 @@ struct Stream {
       for (int r = 0; r < 4; ++r) {
         sv[t][r] = s[t][r] * p.scale_log2;
         if (TAIL && c.j * (16 * TILES) + 16 * t + 4 * quad + r >= c.T) sv[t][r] = -INFINITY;
+        if (DENSE && ((cb.mk[t] >> (8 * r)) & 0xffu) == 0) sv[t][r] = -INFINITY;
       }
     float bmax = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
 #pragma unroll
     for (int t = 1; t < TILES; ++t)
       bmax = fmaxf(bmax, fmaxf(fmaxf(sv[t][0], sv[t][1]), fmaxf(sv[t][2], sv[t][3])));
     bmax = max_x32(max_x16(bmax));
+    // A dense batch can present chunks with every token masked: while the
+    // running max is still -inf, exponents are taken against 0 instead
+    // (acc and l are zero then, and the weights of masked tokens are 0).
+    float mref;
     {
       // branch-free rescale (alpha = 1 when no running max grows)
       const float mn = fmaxf(m, bmax);
-      const float alpha = __builtin_amdgcn_exp2f(m - mn);
+      mref = DENSE && mn == -INFINITY ? 0.f : mn;
+      const float alpha = __builtin_amdgcn_exp2f(m - mref);
 #pragma unroll
       for (int i = 0; i < VD; ++i) acc[i] *= alpha;
       l *= alpha;
       m = mn;
     }
     uint32_t pw[TILES][2];
-    const float mp = m - E::kPScaleLog2;
+    const float mp = mref - E::kPScaleLog2;
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       pw[t][0] = E::pack2(__builtin_amdgcn_exp2f(sv[t][0] - mp), __builtin_amdgcn_exp2f(sv[t][1] - mp));
       pw[t][1] = E::pack2(__builtin_amdgcn_exp2f(sv[t][2] - mp), __builtin_amdgcn_exp2f(sv[t][3] - mp));
       l += (E::lo(pw[t][0]) + E::hi(pw[t][0])) + (E::lo(pw[t][1]) + E::hi(pw[t][1]));
     }
-    if (TAIL) {
+    if (TAIL && !DENSE) {   // dense rows past the end repeat a real row; their weight is 0
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
 #pragma unroll
@@ -391,7 +446,7 @@ struct Stream {
 
   __device__ __forceinline__ void attend_chunk(const f32x4_t* s, Buf& cb,
                                                const Cursor& c) {
-    if (c.j == c.nb - 1 && (c.T % (16 * TILES)) != 0)
+    if (DENSE || (c.j == c.nb - 1 && (c.T % (16 * TILES)) != 0))
       attend<true>(s, cb, c);
     else
       attend<false>(s, cb, c);
@@ -405,7 +460,7 @@ struct Stream {
     if (n >= G) return;
     // lane holds dims 4*VD*quad + VD*r + i of head n as acc[i][r]
     if (whole) {
-      const float inv = 1.0f / lt;
+      const float inv = DENSE && lt == 0.f ? 0.f : 1.0f / lt;   // dense: all masked -> zeros
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
                       ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + n) * D + 4 * VD * quad;
       if constexpr (VD == 8) {
@@ -461,6 +516,7 @@ struct StreamF32 {
   static constexpr int kTiles = 1;
   static constexpr int kChunk = 16;
   static constexpr bool kAppend = APPEND;
+  static constexpr bool kDense = false;
   static constexpr int KQ = D / 4;    // K floats per lane per tile
   static constexpr int NH = D / 64;   // float4 V loads per row per lane
   static constexpr int NB = D / 16;   // output blocks (h, e)
@@ -654,7 +710,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int H = p.pool.kv_heads;
 
   constexpr int TILES = S::kTiles;
-  block_chunk_prefix<kThreads>(p.context_lens, p.batch, S::kChunk, prefix, scan);
+  if constexpr (S::kDense) {   // every sequence is dense_len tokens long
+    const int nc = chunks_of(p.dense_len, S::kChunk);
+    for (int i = threadIdx.x; i <= p.batch; i += kThreads) prefix[i] = i * nc;
+    __syncthreads();
+  } else {
+    block_chunk_prefix<kThreads>(p.context_lens, p.batch, S::kChunk, prefix, scan);
+  }
   if (blockIdx.x == 0)
     for (int i = threadIdx.x; i <= p.batch; i += kThreads) p.ws_prefix[i] = prefix[i];
 
@@ -668,9 +730,10 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   const int64_t c0 = wave_begin(unit, C, Ue);
   const int rem = (int)(wave_begin(unit + 1, C, Ue) - c0);   // >= 1
 
-  const const_i32_ptr lens = (const_i32_ptr)p.context_lens;
+  const const_i32_ptr lens = S::kDense ? nullptr : (const_i32_ptr)p.context_lens;
   const const_i32_ptr poss = S::kAppend ? (const_i32_ptr)p.positions : nullptr;
   Cursor cur;
+  cur.dense_T = p.dense_len;
   cur.b = uni(seq_of_chunk(prefix, p.batch, c0));
   cur.load_seq(prefix, lens, poss);
   cur.j = uni((int)(c0 - prefix[cur.b]));
@@ -748,6 +811,11 @@ template <typename E>
 void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
   const bool append = p.positions != nullptr;
   constexpr int T = kTilesPerStep;
+  if (p.k_dense) {
+    if (p.pool.head_dim == 128) launch_one<Stream<E, 128, T, false, true>>(p, wgs, lds, s);
+    else launch_one<Stream<E, 64, T, false, true>>(p, wgs, lds, s);
+    return;
+  }
   if (p.pool.head_dim == 128) {
     if (append) launch_one<Stream<E, 128, T, true>>(p, wgs, lds, s);
     else launch_one<Stream<E, 128, T, false>>(p, wgs, lds, s);

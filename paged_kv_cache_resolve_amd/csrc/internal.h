@@ -99,6 +99,12 @@ struct DecodeParams {
   const void* k_new;
   const void* v_new;
   const int32_t* positions;
+  // Dense decode (null for the paged forms): K and V as [batch][dense_len]
+  // [kv_heads][head_dim], token t of sequence b attended where mask[b][t] != 0.
+  const void* k_dense;
+  const void* v_dense;
+  const uint8_t* mask;
+  int dense_len;
 };
 
 constexpr int kMaxWaves = 8192;          // upper bound on wavefronts (256 CUs x 32)

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 24, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), f"{n} missing from libpagedkv.so"
     assert set(names) == set(_lib.SIGNATURES), "binding signatures drift from the header"
@@ -191,6 +191,22 @@ def test_entry_points_validate_before_launch():
     assert tok(k=odd) == _lib.ERR_INVALID_ARG
     assert tok(total=0, k=None, off=None) == 0
     assert tok(batch=0, k=None, off=None) == 0
+    # dense decode: (out, q, k, v, mask, batch, max_len, kv_heads, head_dim, hq, dtype, scale, ws, wsb, stream)
+    dws = L.dense_attention_workspace_bytes(4, 2, 8, 128)
+    assert dws > 0 and L.dense_attention_workspace_bytes(4, 2, 7, 128) == 0
+    dd = lambda **kw: L.dense_attention_decode(  # noqa: E731
+        kw.get("out", p), p, kw.get("k", p), p, kw.get("mask", p), kw.get("batch", 4),
+        kw.get("max_len", 40), 2, kw.get("d", 128), kw.get("hq", 8), kw.get("dtype", _lib.BF16),
+        ctypes.c_float(0.1), kw.get("ws", p), kw.get("wsb", dws), None)
+    assert dd(hq=7) == _lib.ERR_INVALID_ARG
+    assert dd(mask=None) == _lib.ERR_INVALID_ARG
+    assert dd(k=odd) == _lib.ERR_INVALID_ARG
+    assert dd(max_len=-1) == _lib.ERR_INVALID_ARG
+    assert dd(dtype=_lib.F32) == _lib.ERR_UNSUPPORTED
+    assert dd(d=96) == _lib.ERR_UNSUPPORTED
+    assert dd(hq=2 * 17) == _lib.ERR_UNSUPPORTED
+    assert dd(wsb=dws - 1) == _lib.ERR_WORKSPACE
+    assert dd(batch=0, out=None) == 0
     assert L.paged_kv_resolve(p, p, 4, p, 4, 0, 16, None) == _lib.ERR_INVALID_ARG
     assert L.paged_kv_resolve(None, p, 4, p, 4, 16, 16, None) == _lib.ERR_INVALID_ARG
     L.kv_pool_destroy(h)
