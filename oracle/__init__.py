@@ -49,5 +49,6 @@ from .paged import (  # noqa: F401
     paged_waste_ratio,
     paged_waste_slots,
     resolve_slots,
+    validate_decode_inputs,
     widen,
 )

@@ -249,6 +249,34 @@ def attend(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndar
     return out
 
 
+def validate_decode_inputs(num_blocks: int, block_size: int, block_tables: np.ndarray,
+                           context_lens: np.ndarray, num_q_heads: int, num_kv_heads: int) -> None:
+    """The preconditions of a decode: query heads a multiple of KV heads,
+    0 <= T_b <= max_blocks_per_seq * B, every used table entry a block of the
+    pool, and no physical block used by two (sequence, logical block) pairs
+    (so no two tokens share a slot).  Raises ValueError.
+
+    [vllmini] "PagedAttention Metaphor" (each logical block maps to its own
+    physical block); [mini-infer] "The Solution" (the table maps a request's
+    logical blocks to physical block ids of the pool).
+    """
+    if num_kv_heads < 1 or num_q_heads % num_kv_heads != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    S, MB = block_tables.shape
+    owner = {}
+    for b in range(S):
+        T = int(context_lens[b])
+        if T < 0 or T > MB * block_size:
+            raise ValueError(f"sequence {b}: length {T} outside [0, {MB * block_size}]")
+        for j in range(math.ceil(T / block_size)):
+            blk = int(block_tables[b, j])
+            if not 0 <= blk < num_blocks:
+                raise ValueError(f"sequence {b}: block {blk} outside the pool")
+            if blk in owner:
+                raise ValueError(f"block {blk} used by {owner[blk]} and {(b, j)}")
+            owner[blk] = (b, j)
+
+
 def paged_attention_decode(pool: np.ndarray, dtype: str, layer: int,
                            block_tables: np.ndarray, context_lens: np.ndarray,
                            q: np.ndarray, scale: float, seqs=None) -> np.ndarray:
@@ -259,6 +287,8 @@ def paged_attention_decode(pool: np.ndarray, dtype: str, layer: int,
     GPU receives.  Sources: see :func:`gather_sequence` and :func:`attend`.
     """
     S, Hq, D = q.shape
+    validate_decode_inputs(pool.shape[0], pool.shape[4], block_tables, context_lens, Hq,
+                           pool.shape[3])
     scale64 = float(np.float32(scale))
     out = np.zeros((S, Hq, D), dtype=np.float64)
     for b in (range(S) if seqs is None else seqs):

@@ -34,7 +34,8 @@ __all__ = [
     "KVPool", "kv_pool_create", "BlockManager", "kv_append", "kv_append_layers", "kv_append_tokens",
     "paged_kv_gather", "paged_attention_decode",
     "paged_attention_decode_append", "DecodePlan", "dense_attention_decode",
-    "paged_attention_workspace_bytes", "paged_kv_resolve", "PagedKVError", "OutOfBlocksError",
+    "paged_attention_workspace_bytes", "paged_kv_resolve", "validate_decode_inputs",
+    "PagedKVError", "OutOfBlocksError",
     "library",
 ]
 
@@ -203,6 +204,40 @@ class BlockManager:
 
     def __del__(self):
         self.close()
+
+
+def validate_decode_inputs(num_blocks: int, block_size: int, block_tables: torch.Tensor,
+                           context_lens: torch.Tensor, positions: torch.Tensor | None = None) -> None:
+    """Check the device-resident inputs the library trusts (it cannot read
+    them without a synchronisation): 0 <= T_b <= max_blocks_per_seq *
+    block_size, every used table entry a block of the pool, no physical
+    block used twice, and for an append every non-negative position inside
+    the table with its block present.  Copies the arrays to the host (a
+    synchronisation); meant for tests and debugging.  Raises ValueError."""
+    tables = block_tables.detach().cpu().numpy()
+    lens = context_lens.detach().cpu().numpy().astype(np.int64)
+    if tables.ndim != 2 or lens.shape != (tables.shape[0],):
+        raise ValueError("block_tables must be [batch, max_blocks_per_seq], context_lens [batch]")
+    mb = tables.shape[1]
+    if (lens < 0).any() or (lens > mb * block_size).any():
+        raise ValueError("a context length lies outside [0, max_blocks_per_seq * block_size]")
+    used = (lens + block_size - 1) // block_size
+    cols = np.arange(mb)[None, :] < used[:, None]
+    ids = tables[cols]
+    if ((ids < 0) | (ids >= num_blocks)).any():
+        raise ValueError("a used block-table entry lies outside the pool")
+    if len(np.unique(ids)) != len(ids):
+        raise ValueError("a physical block is used by two logical blocks")
+    if positions is not None:
+        pos = positions.detach().cpu().numpy().astype(np.int64)
+        if pos.shape != lens.shape:
+            raise ValueError("positions must be [batch]")
+        live = pos >= 0
+        if (pos[live] >= mb * block_size).any():
+            raise ValueError("a position lies past the block table")
+        blk = tables[np.nonzero(live)[0], pos[live] // block_size]
+        if ((blk < 0) | (blk >= num_blocks)).any():
+            raise ValueError("the block of an appended position is missing")
 
 
 def kv_pool_create(num_blocks: int, block_size: int = 16, layers: int = 24, kv_heads: int = 2,

@@ -63,6 +63,8 @@ class DeviceWorkload:
         self.tables = torch.from_numpy(w.block_tables).to(device)
         self.lens = torch.from_numpy(w.context_lens).to(device)
         self.positions = torch.from_numpy(w.positions).to(device)
+        # the preconditions the library trusts, checked on the host copy
+        pk.validate_decode_inputs(w.NB, w.BS, self.tables, self.lens)
         self.q = np_to_dev(w.q, w.dtype, device)
         self.k_new = np_to_dev(w.k_new, w.dtype, device)
         self.v_new = np_to_dev(w.v_new, w.dtype, device)

@@ -219,3 +219,23 @@ def test_binding_refuses_host_tensors():
     data = torch.zeros((4, 2, 1, 2, 16, 64), dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pk.KVPool(4, 16, 1, 2, 64, torch.bfloat16, data=data)
+
+
+def test_validate_decode_inputs_host_helper():
+    import torch
+    t = torch.tensor([[3, 1, -7], [0, 2, 99]], dtype=torch.int32)
+    pk.validate_decode_inputs(4, 4, t, torch.tensor([8, 6], dtype=torch.int32))
+    pk.validate_decode_inputs(4, 4, t, torch.tensor([8, 6], dtype=torch.int32),
+                              positions=torch.tensor([7, -1], dtype=torch.int32))
+    bad = [
+        (t, [13, 6], None),                                               # past the table
+        (torch.tensor([[3, 4, 0], [0, 2, 0]], dtype=torch.int32), [8, 6], None),   # block 4 of 4
+        (torch.tensor([[3, 1, 0], [1, 2, 0]], dtype=torch.int32), [8, 6], None),   # shared block
+        (t, [-1, 6], None),
+        (t, [8, 6], [12, -1]),                                            # block of 12 is -7
+        (t, [8, 6], [7, 12]),                                             # 12 // 4 = 3: past the row
+    ]
+    for tab, lens, pos in bad:
+        with pytest.raises(ValueError):
+            pk.validate_decode_inputs(4, 4, tab, torch.tensor(lens, dtype=torch.int32),
+                                      None if pos is None else torch.tensor(pos, dtype=torch.int32))

@@ -521,6 +521,25 @@ def check_dense_masked_decode():
     assert oracle.dense_masked_decode(k2, v2, mask, q, "f32", 0.5).tobytes() == got.tobytes()
 
 
+def check_validate_decode_inputs():
+    """The oracle refuses inputs outside the decode's preconditions: a length
+    past the table, a block outside the pool, a block shared by two logical
+    blocks, query heads not a multiple of KV heads; well-formed inputs and
+    padding entries (never read) pass."""
+    tables = np.array([[3, 1, -7], [0, 2, 99]], np.int32)   # padding past ceil(T/B) ignored
+    oracle.validate_decode_inputs(4, 4, tables, np.array([8, 6]), 8, 2)
+    bad = [
+        (np.array([[3, 1, -7], [0, 2, 99]], np.int32), np.array([13, 6]), 8, 2),   # 13 > 3*4
+        (np.array([[3, 4, -7], [0, 2, 99]], np.int32), np.array([8, 6]), 8, 2),    # block 4 of 4
+        (np.array([[3, 1, -7], [1, 2, 99]], np.int32), np.array([8, 6]), 8, 2),    # 1 twice
+        (np.array([[3, 1, -7], [0, 2, 99]], np.int32), np.array([8, 6]), 6, 4),    # 6 % 4
+        (np.array([[3, 1, -7], [0, 2, 99]], np.int32), np.array([-1, 6]), 8, 2),   # negative
+    ]
+    for t, lens, hq, hkv in bad:
+        with pytest.raises(ValueError):
+            oracle.validate_decode_inputs(4, 4, t, lens, hq, hkv)
+
+
 def check_widen_f16():
     """Every finite binary16 pattern widens to the value its bits define;
     a few by hand: 1, -2, 0.25, the largest finite 65504, the smallest
@@ -566,6 +585,7 @@ ALL_CHECKS = [
     ("widen", check_widen),
     ("widen_f16", check_widen_f16),
     ("dense_masked_decode", check_dense_masked_decode),
+    ("validate_decode_inputs", check_validate_decode_inputs),
 ]
 
 
