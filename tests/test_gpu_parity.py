@@ -13,6 +13,7 @@ import torch
 
 import oracle
 import paged_kv_cache_resolve_amd as pk
+from paged_kv_cache_resolve_amd import _lib
 from workloads import make_workload
 
 from gpu_helpers import (NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say,
@@ -225,6 +226,11 @@ EDGE_CASES = [
     ("f16", 16, 1, 128, 16),    # MFMA fp16, G = 16
     ("f16", 8, 2, 64, 8),       # generic fp16 (block size 8)
     ("f16", 6, 2, 96, 16),      # generic fp16 (head_dim 96)
+    ("bf16", 8, 2, 64, 1),      # generic, one token per block
+    ("bf16", 8, 2, 128, 128),   # MFMA, 128-token blocks
+    ("bf16", 8, 2, 256, 16),    # generic, head_dim 256
+    ("f32", 4, 1, 256, 32),     # generic fp32, head_dim 256
+    ("f32", 16, 1, 64, 64),     # MFMA fp32, G = 16
 ]
 
 
@@ -299,3 +305,25 @@ def test_output_dtype_rounding(dtype):
     for b in range(2):
         K, V = oracle.gather_sequence(w.pool, 0, w.block_tables[b], 1)
         assert out[b].tobytes() == np.ascontiguousarray(V[0]).tobytes()
+
+
+def test_decode_largest_batch_and_one_past_it():
+    """16384 sequences (the most whose chunk prefix fits in LDS) with short
+    and empty contexts; one more is refused before any launch."""
+    say("decode 16384 sequences")
+    rng = np.random.default_rng(16384)
+    lens = rng.integers(0, 40, size=16384)
+    w = custom("bf16", 16384, 8, 2, 64, 16, lens)
+    dw = DeviceWorkload(w)
+    out = dw.decode()
+    torch.cuda.synchronize()
+    seqs = sorted(set(rng.choice(16384, size=100, replace=False).tolist()) | {0, 16383})
+    assert_attention_close(out, _oracle_decode(w, seqs=seqs), "bf16", rows=seqs, what="16384")
+    zero = [i for i in range(16384) if lens[i] == 0][:50]
+    assert not dev_to_np(out)[zero].any()
+    q = torch.zeros(16385, 8, 64, dtype=torch.bfloat16, device="cuda")
+    tables = torch.zeros(16385, 1, dtype=torch.int32, device="cuda")
+    ctx = torch.zeros(16385, dtype=torch.int32, device="cuda")
+    with pytest.raises(pk.PagedKVError) as e:
+        pk.paged_attention_decode(torch.empty_like(q), q, dw.pool, 0, tables, ctx, 0.125)
+    assert e.value.status == _lib.ERR_UNSUPPORTED
