@@ -270,8 +270,8 @@ def cpu_baseline(w, budget_tokens: int, min_seconds: float = 10.0):
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_decode_bf16", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=0, help="input replicas (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")

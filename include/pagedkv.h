@@ -85,7 +85,8 @@ size_t kv_pool_bytes(int num_blocks, int block_size, int layers, int kv_heads,
  * the free-block stack in ascending order, so the first allocation returns
  * num_blocks - 1 ([mini-infer] "Python Implementation: Physical Block Pool":
  * the free list is a stack popped from its end).
- * Requirements: all sizes >= 1, head_dim a multiple of 8 (bf16) or 4 (fp32).
+ * Requirements: all sizes >= 1, head_dim a multiple of 8 (bf16, fp16) or 4
+ * (fp32), so that a row is a whole number of 16-byte units.
  * On success *out receives a handle to release with kv_pool_destroy. */
 int kv_pool_create(kv_pool_t** out, int num_blocks, int block_size, int layers,
                    int kv_heads, int head_dim, pagedkv_dtype_t dtype,
@@ -261,10 +262,14 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  *                  256-byte aligned; contents need no initialisation.  Calls
  *                  that share a workspace must not overlap.
  * out[b][h] = sum_t softmax_t(scale * q[b][h] . K_t) V_t over t < T_b,
- * computed with fp32 accumulation; bf16 outputs are rounded to nearest
- * even.  T_b = 0 gives a zero row.  Work is split evenly over all
+ * computed with fp32 accumulation; bf16 and fp16 outputs are rounded to
+ * nearest even.  T_b = 0 gives a zero row.  Work is split evenly over all
  * wavefronts the GPU holds at once; a sequence split across wavefronts is
- * merged by a second kernel on the same stream (log-sum-exp weights). */
+ * merged by a second kernel on the same stream (log-sum-exp weights).
+ * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
+ * (bf16, fp16, fp32); a VALU kernel for head_dim up to 256 in steps of 4 and
+ * any block size.  At most 16 query heads per KV head and 16384 sequences per
+ * call; otherwise PAGEDKV_ERR_UNSUPPORTED. */
 int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
                            int layer, const int32_t* block_tables,
                            int max_blocks_per_seq, const int32_t* context_lens,
@@ -283,10 +288,10 @@ int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
  * position at or past T_b is written but not attended, as in the two-call
  * form).  Arguments are those of the two calls; k_new, v_new and positions
  * must all be non-null when batch > 0.
- * For bf16 pools with head_dim 64 or 128 and block_size a multiple of 16 the
- * decode kernel reads each new K/V row from k_new / v_new instead of the
- * pool and the merge kernel stores them into the pool afterwards, which
- * saves the separate append launch; other shapes run the two launches. */
+ * Where the MFMA kernel runs (head_dim 64 or 128, block_size a multiple of
+ * 16) it reads each new K/V row from k_new / v_new instead of the pool and
+ * the merge kernel stores them into the pool afterwards, which saves the
+ * separate append launch; other shapes run the two launches. */
 int paged_attention_decode_append(void* out, const void* q, const void* k_new,
                                   const void* v_new, const int32_t* positions,
                                   kv_pool_t* pool, int layer,
