@@ -327,3 +327,53 @@ def test_decode_largest_batch_and_one_past_it():
     with pytest.raises(pk.PagedKVError) as e:
         pk.paged_attention_decode(torch.empty_like(q), q, dw.pool, 0, tables, ctx, 0.125)
     assert e.value.status == _lib.ERR_UNSUPPORTED
+
+
+def _rne_16(x32: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to bf16 / fp16 bits, nearest even, written out
+    with integer arithmetic (bf16) or numpy's IEEE conversion (fp16)."""
+    if dtype == "f16":
+        return x32.astype(np.float16).view(np.uint16)
+    u = x32.view(np.uint32).astype(np.uint64)
+    lower = u >> 16
+    rest = u & 0xFFFF
+    up = (rest > 0x8000) | ((rest == 0x8000) & (lower & 1 == 1))
+    return (lower + up).astype(np.uint16)
+
+
+@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("bf16", 64, 8), ("f16", 128, 16),
+                                        ("f16", 64, 8)])
+def test_output_rounding_is_nearest_even(dtype, D, BS):
+    """Two cached tokens with identical K rows get weights of exactly 1/2,
+    so the fp32 result is the midpoint of their V values.  V pairs are
+    neighbouring representable values, so every midpoint lies exactly
+    halfway between two outputs: round-to-nearest-even and truncation give
+    different bits, and the output must be the even one."""
+    say(f"output rounding {dtype} D={D} BS={BS}")
+    w = custom(dtype, 3, 8, 2, D, BS, [2, 2, 2])
+    rng = np.random.default_rng(D + BS)
+    for b in range(w.S):
+        blk = w.block_tables[b, 0]
+        for g in range(w.Hkv):
+            w.pool[blk, 0, 0, g, 1, :] = w.pool[blk, 0, 0, g, 0, :]       # K1 = K0
+            if dtype == "f16":
+                lo = (rng.standard_normal(D) * 4).astype(np.float16)
+                hi = np.nextafter(lo, np.float16(np.inf) * np.sign(lo + np.float16(1e-3)))
+            else:
+                bits = w.pool[blk, 1, 0, g, 0, :].astype(np.uint32)
+                lo = bits.astype(np.uint16)
+                hi = (bits + 1).astype(np.uint16)                          # next bf16 away from 0
+            w.pool[blk, 1, 0, g, 0, :] = lo
+            w.pool[blk, 1, 0, g, 1, :] = hi
+    out = dev_to_np(DeviceWorkload(w).decode())
+    G = 4
+    for b in range(w.S):
+        blk = w.block_tables[b, 0]
+        for h in range(8):
+            v0 = oracle.widen(w.pool[blk, 1, 0, h // G, 0, :], dtype)
+            v1 = oracle.widen(w.pool[blk, 1, 0, h // G, 1, :], dtype)
+            mid = ((v0 + v1) / 2).astype(np.float32)                     # exact in fp32
+            assert (mid.astype(np.float64) == (v0 + v1) / 2).all()
+            want = _rne_16(mid, dtype)
+            got = out[b, h].view(np.uint16)
+            assert got.tobytes() == want.tobytes(), (b, h)
