@@ -368,6 +368,47 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     dec_ms = [a.elapsed_time(b) for a, b in ev]
 
+    # The same step replayed from a HIP graph: 32 consecutive steps (what one
+    # iteration of a 32-layer model enqueues) captured once, replayed.  Each
+    # plan gets its own workspace, since a capture uses its own stream.
+    graph_ms = None
+    try:
+        gplans = []
+        for r in reps_dev:
+            w = r["w"]
+            wsb = pk.paged_attention_workspace_bytes(r["pool"], w.S, w.Hq)
+            gplans.append(pk.DecodePlan(
+                r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"], w.scale,
+                r["k"], r["v"], r["pos"],
+                workspace=torch.empty(wsb, dtype=torch.uint8, device="cuda")))
+        n_graph = 32
+
+        def graph_body():
+            for i in range(n_graph):
+                gplans[i % len(gplans)].run()
+
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            graph_body()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            graph_body()
+        graph.replay()
+        torch.cuda.synchronize()
+        g0, g1 = ev_pair()
+        g0.record(stream)
+        for _ in range(5):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = g0.elapsed_time(g1) / (5 * n_graph)
+        del graph, gplans
+    except RuntimeError as exc:   # capture unavailable: report it, keep the rest
+        print(f"[bench] graph replay skipped: {exc}", file=sys.stderr, flush=True)
+
     step_bytes = np.mean([decode_bytes(r["w"]) + append_bytes(r["w"]) for r in reps_dev])
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = step_bytes / (dec_avg_ms * 1e-3) / 1e9
@@ -399,6 +440,7 @@ def main(argv=None) -> int:
         "tokens_per_s": round(tokens_per_s, 1),
         "gpu_ms_per_step": round(gpu_ms_per_step, 5),
         "call_ms": round(dec_avg_ms, 5),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "calls_timed": n_dec,
         "call_ms_per_call_events_p10_p50_p90": [
             round(float(np.percentile(dec_ms, q)), 5) for q in (10, 50, 90)],
