@@ -1,16 +1,19 @@
-// Bit-exact copy kernels: KV append into the tail block, batched paged-KV
-// gather into contiguous tensors, and the stand-alone block-table resolver.
+// Bit-exact copy kernels: KV appends (one token, one token for every layer,
+// several tokens of a prompt), batched paged-KV gather into contiguous
+// tensors, and the stand-alone block-table resolver.
 //
 //   append  -- "KV Cache and Attention Mechanisms", section 2 (blocks are
-//              filled one token at a time as generation proceeds);
-//              "Paged KV-Cache Memory Management", section "The Solution".
+//              filled one token at a time as generation proceeds; a prompt
+//              fills whole blocks and only the last is partly filled);
+//              "Paged KV-Cache Memory Management", section "The Solution"
+//              (a block holds its tokens' K and V for all layers).
 //   gather  -- "Paged KV-Cache Memory Management", section "Zero-Copy
 //              Batched Attention Gather".
 //   resolve -- "vllmini", section "PagedAttention Metaphor".
 //
 // All copies move 16-byte units (a pool row of head_dim elements is a
-// whole number of units: head_dim is a multiple of 8 for bf16 and of 4 for
-// fp32), so every load and store is a dwordx4.
+// whole number of units: head_dim is a multiple of 8 for bf16 and fp16 and
+// of 4 for fp32), so every load and store is a dwordx4.
 
 #include "internal.h"
 

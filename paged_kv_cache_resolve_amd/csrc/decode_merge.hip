@@ -6,7 +6,9 @@
 // With M = max_k m_k and w_k = exp2(m_k - M):
 //     out = (sum_k w_k o_k) / (sum_k w_k l_k),
 // the softmax-weighted V sum over the whole context, accumulated here with
-// an online (running-max) update.  Empty sequences (T_b = 0) get zero rows.
+// an online (running-max) update.  Empty sequences (T_b = 0) get zero rows,
+// and so does a (sequence, head) with nothing attended (a dense batch whose
+// mask is all zero): partials with m_k = -inf are skipped.
 //
 // For a fused append, this pass also stores each sequence's new K/V rows
 // into the pool: pass 1 read them from the k_new / v_new inputs, so the pool

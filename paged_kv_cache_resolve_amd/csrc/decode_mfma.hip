@@ -1,4 +1,10 @@
-// Paged-attention decode for bf16 and fp16 pools: MFMA tiles on gfx950, one kernel.
+// Paged-attention decode, pass 1, on MFMA tiles (gfx950): one persistent
+// kernel body (decode_mfma_kernel<S>) over three stream types S.
+//   Stream<E, D, 2, ...>  bf16 / fp16 pools (E = Bf16Ops, F16Ops), 32-token
+//                         chunks of two 16x16 tiles; its DENSE form reads
+//                         the padded [batch][max_len][kv_heads][head_dim]
+//                         tensors a batched gather writes, under a mask;
+//   StreamF32<D, ...>     fp32 pools, 16-token chunks (described at the type).
 //
 // What is computed ("vllmini: Building a Minimalist PagedAttention and KV
 // Cache Engine", section "The CUDA Block Kernel"; "KV Cache and Attention
@@ -7,32 +13,34 @@
 // physical blocks of the pool, and scaled q.K scores, a max-subtracted
 // softmax and the weighted sum of V rows are formed.
 //
-// Mapping onto CDNA4.
+// Mapping onto CDNA4 (16-bit stream; the fp32 stream differs in the operand
+// layouts only).
 //  * Work split (internal.h, decode_split.h): the kv_heads wavefronts of a
-//    head group take the same contiguous, equal-sized range of 16-token
-//    chunks of the sequences laid end to end, one KV head each, and stream
-//    through it without stopping at sequence boundaries.  All G query heads
-//    of a KV head are computed from the same K/V bytes, so each byte is read
-//    from HBM once, and the group reads each block's heads side by side.
+//    head group take the same contiguous, equal-sized range of chunks of the
+//    sequences laid end to end, one KV head each, and stream through it
+//    without stopping at sequence boundaries.  All G query heads of a KV head
+//    are computed from the same K/V bytes, so each byte is read from HBM
+//    once, and the group reads each block's heads side by side.
 //  * Per chunk:
-//      - the K tile [16 tokens x D] is loaded straight into the A-operand
-//        layout of v_mfma_f32_16x16x32_bf16 (row = token = lane % 16, eight
+//      - the K tiles [16 tokens x D] are loaded straight into the A-operand
+//        layout of the 16x16x32 MFMA (row = token = lane % 16, eight
 //        consecutive dims per lane) and multiplied by Q^T (16 head columns, G
-//        used, the rest zero), giving score(token 4*(lane/16)+r, head lane%16);
+//        used), giving score(token 4*(lane/16)+r, head lane%16);
 //      - online softmax in fp32 in the exp2 domain (the accumulator is
 //        rescaled branch-free; the factor is 1 unless a running max grew);
-//      - the probabilities, rounded to the pool type, already sit in the B-operand
-//        layout of v_mfma_f32_16x16x16_bf16 (k = token); V rows are loaded
-//        fully coalesced (lane = token 4*(lane/16)+r, dims VD*(lane%16)..)
-//        and transposed to the A operand with v_perm_b32.  The accumulator
-//        holds out^T: lane = head lane%16, 4*VD contiguous dims;
-//      - the next chunk's K and V (and, at a pair boundary, the next pair's
-//        q) are in flight while this chunk is computed; the block-table entry
-//        of the chunk after that is already being fetched by a scalar load.
-//  * When a pair ends inside the wavefront's range the normalised output is
-//    written directly; a pair cut by a range edge leaves a partial (running
-//    max, sum, unnormalised output) in the workspace, and the merge kernel
-//    (decode_merge.hip) combines the partials of every such pair.
+//      - the probabilities, rounded to the pool type, already sit in the
+//        B-operand layout of the PV MFMA (k = token); V rows are loaded fully
+//        coalesced (lane = token 4*(lane/16)+r, dims VD*(lane%16)..) and
+//        transposed to the A operand with v_perm_b32.  The accumulator holds
+//        out^T: lane = head lane%16, 4*VD contiguous dims;
+//      - the next chunk's K and V (and, at a sequence boundary, the next
+//        sequence's q) are in flight while this chunk is computed; the
+//        block-table entry of the chunk after that is already being fetched
+//        by a scalar load.
+//  * When a (sequence, KV head) ends inside the wavefront's range the
+//    normalised output is written directly; one cut by a range edge leaves a
+//    partial (running max, sum, unnormalised output) in the workspace, and
+//    the merge kernel (decode_merge.hip) combines the partials.
 
 #include <math.h>
 
@@ -231,10 +239,10 @@ struct Stream {
     l = 0.f;
   }
 
-  // q of the pair's G heads in the B-operand layout.  MFMA columns n >= G
-  // carry a copy of head G-1: every column goes through its own softmax and
-  // accumulator and only columns n < G are ever written, so the copies cost
-  // nothing and need neither a branch nor masking.
+  // q of the sequence's G query heads of this KV head in the B-operand
+  // layout.  MFMA columns n >= G carry a copy of head G-1: every column goes
+  // through its own softmax and accumulator and only columns n < G are ever
+  // written, so the copies cost nothing and need neither a branch nor masking.
   __device__ __forceinline__ void load_q(const Cursor& c) {
     const int G = p.group;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
