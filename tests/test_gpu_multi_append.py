@@ -37,6 +37,8 @@ SHAPES = [
     ("f32", 2, 32, 8, 2),
     ("bf16", 3, 96, 16, 2),     # 12 units per head row, 3 heads: no power of two
     ("f32", 5, 20, 8, 2),       # 5 units per head row
+    ("f16", 8, 128, 16, 3),
+    ("f16", 2, 64, 32, 2),
 ]
 
 # Ragged counts: empty, single token, a whole block, block + 1, many blocks;

@@ -98,7 +98,8 @@ def test_gather_workloads(idx):
 
 
 @pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("bf16", 64, 32), ("f32", 64, 16),
-                                        ("bf16", 32, 8), ("f32", 128, 1)])
+                                        ("bf16", 32, 8), ("f32", 128, 1), ("f16", 128, 16),
+                                        ("f16", 64, 4)])
 def test_gather_shapes_and_padding(dtype, D, BS):
     say(f"gather {dtype} D={D} BS={BS}")
     w = poison(custom(dtype, 6, 4, 2, D, BS, [0, 1, BS - 1 if BS > 1 else 1, BS, BS + 1, 3 * BS + 5],
@@ -110,10 +111,13 @@ def test_gather_shapes_and_padding(dtype, D, BS):
 # append
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("idx", [0, 1])
-def test_append_whole_pool(idx):
-    say(f"append workload {idx}")
-    w = make_workload(idx)
+@pytest.mark.parametrize("idx,dtype", [(0, None), (1, None), (1, "f16"), (2, "f16")])
+def test_append_whole_pool(idx, dtype):
+    say(f"append workload {idx} {dtype or ''}")
+    over = {"dtype": dtype} if dtype else {}
+    if idx == 2:
+        over["S"] = 8
+    w = make_workload(idx, **over)
     dw = DeviceWorkload(w)
     pk.kv_append(dw.pool, w.layer, dw.k_new, dw.v_new, dw.tables, dw.positions)
     ref = oracle.kv_append(w.pool, w.layer, w.block_tables, w.positions, w.k_new, w.v_new)
