@@ -126,22 +126,24 @@ def test_fused_position_cases(dtype, Hq, Hkv, D, BS):
     assert not dev_to_np(out)[8].any(), "empty sequence must give a zero row"
 
 
-def test_fused_step_full_size_llama8b():
-    """The benchmarked configuration: full batch, sampled rows checked, the
-    whole pool bit-exact against the oracle's append."""
-    say("fused append+decode workload 2 full size")
-    w = make_workload(2)
+@pytest.mark.parametrize("idx", [2, 3])
+def test_fused_step_full_size(idx):
+    """The benchmarked configurations (the Llama-shaped layer and the long
+    contexts) at full size, through the benchmarked call: sampled rows
+    checked, the whole pool bit-exact against the oracle's append."""
+    say(f"fused append+decode workload {idx} full size")
+    w = make_workload(idx)
     positions = w.positions.copy()
     poison_append_slots(w, positions)
     dw = DeviceWorkload(w)
     out = run_fused(dw, positions)
     ref_pool = oracle.kv_append(w.pool, w.layer, w.block_tables, positions, w.k_new, w.v_new)
     rng = np.random.default_rng(202)
-    seqs = sorted(set(rng.choice(w.S, size=12, replace=False).tolist())
+    seqs = sorted(set(rng.choice(w.S, size=min(12, w.S // 2), replace=False).tolist())
                   | {int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))})
     ref = oracle.paged_attention_decode(ref_pool, w.dtype, w.layer, w.block_tables,
                                         w.context_lens, w.q, w.scale, seqs=seqs)
-    assert_attention_close(out, ref, w.dtype, rows=seqs, what="fused w2 full")
+    assert_attention_close(out, ref, w.dtype, rows=seqs, what=f"fused w{idx} full")
     assert dev_to_np(dw.pool.data).tobytes() == ref_pool.tobytes()
     # a second step over the same inputs reads the appended rows from the pool
     # (now holding the same values), so the output must not change
