@@ -266,9 +266,9 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * nearest even.  T_b = 0 gives a zero row.  Work is split evenly over all
  * wavefronts the GPU holds at once; a sequence split across wavefronts is
  * merged by a second kernel on the same stream (log-sum-exp weights).
- * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
- * (bf16, fp16, fp32); a VALU kernel for head_dim up to 256 in steps of 4 and
- * any block size.  At most 16 query heads per KV head and 16384 sequences per
+ * Kernels: MFMA for block_size a multiple of 16 and head_dim 64 or 128
+ * (bf16, fp16, fp32) or 96 (bf16, fp16); a VALU kernel for head_dim up to 256
+ * in steps of 4 and any block size.  At most 16 query heads per KV head and 16384 sequences per
  * call; otherwise PAGEDKV_ERR_UNSUPPORTED. */
 int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
                            int layer, const int32_t* block_tables,
@@ -288,8 +288,8 @@ int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
  * position at or past T_b is written but not attended, as in the two-call
  * form).  Arguments are those of the two calls; k_new, v_new and positions
  * must all be non-null when batch > 0.
- * Where the MFMA kernel runs (head_dim 64 or 128, block_size a multiple of
- * 16) it reads each new K/V row from k_new / v_new instead of the pool and
+ * Where the MFMA kernel runs (see paged_attention_decode) it reads each new
+ * K/V row from k_new / v_new instead of the pool and
  * the merge kernel stores them into the pool afterwards, which saves the
  * separate append launch; other shapes run the two launches. */
 int paged_attention_decode_append(void* out, const void* q, const void* k_new,
@@ -315,8 +315,8 @@ size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads,
  *   mask   : device, [batch][max_len] uint8; token t of sequence b takes part
  *            iff mask[b][t] != 0.  A sequence with no such token gives zeros.
  * Every one of the max_len rows is read, padding included.  Same arithmetic
- * and tolerances as paged_attention_decode.  bf16 and fp16, head_dim 64 or
- * 128, up to 16 query heads per KV head; otherwise PAGEDKV_ERR_UNSUPPORTED.
+ * and tolerances as paged_attention_decode.  bf16 and fp16, head_dim 64, 96
+ * or 128, up to 16 query heads per KV head; otherwise PAGEDKV_ERR_UNSUPPORTED.
  * workspace as for paged_attention_decode (256-byte aligned). */
 int dense_attention_decode(void* out, const void* q, const void* k, const void* v,
                            const uint8_t* mask, int batch, int max_len, int kv_heads,

@@ -308,7 +308,8 @@ int dense_attention_decode(void* out, const void* q, const void* k, const void* 
   if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v))
     return PAGEDKV_ERR_INVALID_ARG;
   const int group = num_q_heads / kv_heads;
-  if ((dtype != PAGEDKV_BF16 && dtype != PAGEDKV_F16) || (head_dim != 64 && head_dim != 128) ||
+  if ((dtype != PAGEDKV_BF16 && dtype != PAGEDKV_F16) ||
+      (head_dim != 64 && head_dim != 96 && head_dim != 128) ||
       group > kMaxGroup || batch > kMaxBatchLds)
     return PAGEDKV_ERR_UNSUPPORTED;
   if ((int64_t)batch * ((max_len + 31) / 32) > INT32_MAX) return PAGEDKV_ERR_UNSUPPORTED;

@@ -66,6 +66,7 @@ constexpr int kTilesPerStep = PAGEDKV_TILES_PER_STEP;   // 16-token MFMA tiles p
 
 template <int D> struct VRow;
 template <> struct VRow<128> { using type = uint4; };   // 8 elements per lane
+template <> struct VRow<96> { using type = uint3; };    // 6 elements per lane
 template <> struct VRow<64> { using type = uint2; };    // 4 elements per lane
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
@@ -83,6 +84,12 @@ __device__ __forceinline__ X8 stream_load8(const char* p) {
 __device__ __forceinline__ void stream_load(uint4& d, const char* p) {
   d = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p)));
 }
+// 12-byte rows (head_dim 96) are only 4-byte aligned
+typedef unsigned int u32x3_nt __attribute__((ext_vector_type(3), aligned(4)));
+__device__ __forceinline__ void stream_load(uint3& d, const char* p) {
+  const u32x3_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x3_nt*>(p));
+  d = make_uint3(v.x, v.y, v.z);
+}
 __device__ __forceinline__ void stream_load(uint2& d, const char* p) {
   d = __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p)));
 }
@@ -94,6 +101,9 @@ typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 
 __device__ __forceinline__ uint32_t dword_of(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+__device__ __forceinline__ uint32_t dword_of(const uint3& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : v.z;
 }
 __device__ __forceinline__ uint32_t dword_of(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
 
@@ -172,6 +182,7 @@ struct ChunkBuf {
 
 template <int D> __device__ __forceinline__ void zero_row(typename VRow<D>::type& v);
 template <> __device__ __forceinline__ void zero_row<128>(uint4& v) { v = make_uint4(0, 0, 0, 0); }
+template <> __device__ __forceinline__ void zero_row<96>(uint3& v) { v = make_uint3(0, 0, 0); }
 template <> __device__ __forceinline__ void zero_row<64>(uint2& v) { v = make_uint2(0, 0); }
 
 // Position in the chunk space of one KV head: chunk j of sequence b, which
@@ -479,6 +490,14 @@ struct Stream {
                              E::pack2(acc[2][r] * inv, acc[3][r] * inv),
                              E::pack2(acc[4][r] * inv, acc[5][r] * inv),
                              E::pack2(acc[6][r] * inv, acc[7][r] * inv));
+      } else if constexpr (VD == 6) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {   // 12 bytes per r: three dword stores
+          uint32_t* d1 = reinterpret_cast<uint32_t*>(dst + VD * r);
+          d1[0] = E::pack2(acc[0][r] * inv, acc[1][r] * inv);
+          d1[1] = E::pack2(acc[2][r] * inv, acc[3][r] * inv);
+          d1[2] = E::pack2(acc[4][r] * inv, acc[5][r] * inv);
+        }
       } else {
         uint2* d2 = reinterpret_cast<uint2*>(dst);
 #pragma unroll
@@ -488,13 +507,23 @@ struct Stream {
       }
     } else {
       const int64_t slot = partial_slot(c.b, g, unit, p.pool.kv_heads);
-      float4* o = reinterpret_cast<float4*>(p.ws_o + (slot * G + n) * D + 4 * VD * quad);
+      float* of = p.ws_o + (slot * G + n) * D + 4 * VD * quad;
+      if constexpr (VD % 4 == 0) {
+        float4* o = reinterpret_cast<float4*>(of);
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+        for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int h = 0; h < VD / 4; ++h)
-          o[r * (VD / 4) + h] = make_float4(acc[4 * h][r], acc[4 * h + 1][r], acc[4 * h + 2][r],
-                                            acc[4 * h + 3][r]);
+          for (int h = 0; h < VD / 4; ++h)
+            o[r * (VD / 4) + h] = make_float4(acc[4 * h][r], acc[4 * h + 1][r], acc[4 * h + 2][r],
+                                              acc[4 * h + 3][r]);
+      } else {
+        float2* o = reinterpret_cast<float2*>(of);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int h = 0; h < VD / 2; ++h)
+            o[r * (VD / 2) + h] = make_float2(acc[2 * h][r], acc[2 * h + 1][r]);
+      }
       if (quad == 0) {
         p.ws_ml[(slot * G + n) * 2 + 0] = m;
         p.ws_ml[(slot * G + n) * 2 + 1] = lt;
@@ -803,8 +832,9 @@ size_t mfma_lds_bytes(int batch) { return sizeof(int32_t) * (size_t)(batch + 1);
 }  // namespace
 
 bool mfma_supported(const kv_pool* pool, int group) {
-  return (pool->head_dim == 64 || pool->head_dim == 128) &&
-         pool->block_size % 16 == 0 && group >= 1 && group <= kMaxGroup;
+  const int d = pool->head_dim;
+  const bool dim_ok = d == 64 || d == 128 || (d == 96 && pool->dtype != PAGEDKV_F32);
+  return dim_ok && pool->block_size % 16 == 0 && group >= 1 && group <= kMaxGroup;
 }
 
 int mfma_chunk_tokens() { return 16 * kTilesPerStep; }
@@ -821,12 +851,16 @@ void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
   constexpr int T = kTilesPerStep;
   if (p.k_dense) {
     if (p.pool.head_dim == 128) launch_one<Stream<E, 128, T, false, true>>(p, wgs, lds, s);
+    else if (p.pool.head_dim == 96) launch_one<Stream<E, 96, T, false, true>>(p, wgs, lds, s);
     else launch_one<Stream<E, 64, T, false, true>>(p, wgs, lds, s);
     return;
   }
   if (p.pool.head_dim == 128) {
     if (append) launch_one<Stream<E, 128, T, true>>(p, wgs, lds, s);
     else launch_one<Stream<E, 128, T, false>>(p, wgs, lds, s);
+  } else if (p.pool.head_dim == 96) {
+    if (append) launch_one<Stream<E, 96, T, true>>(p, wgs, lds, s);
+    else launch_one<Stream<E, 96, T, false>>(p, wgs, lds, s);
   } else {
     if (append) launch_one<Stream<E, 64, T, true>>(p, wgs, lds, s);
     else launch_one<Stream<E, 64, T, false>>(p, wgs, lds, s);

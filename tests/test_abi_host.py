@@ -203,7 +203,7 @@ def test_entry_points_validate_before_launch():
     assert dd(k=odd) == _lib.ERR_INVALID_ARG
     assert dd(max_len=-1) == _lib.ERR_INVALID_ARG
     assert dd(dtype=_lib.F32) == _lib.ERR_UNSUPPORTED
-    assert dd(d=96) == _lib.ERR_UNSUPPORTED
+    assert dd(d=80) == _lib.ERR_UNSUPPORTED
     assert dd(hq=2 * 17) == _lib.ERR_UNSUPPORTED
     assert dd(wsb=dws - 1) == _lib.ERR_WORKSPACE
     assert dd(batch=0, out=None) == 0

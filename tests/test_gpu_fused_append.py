@@ -96,6 +96,8 @@ SHAPES = [
     ("f32", 8, 2, 64, 8),
     ("f16", 8, 2, 128, 16),
     ("f16", 8, 2, 64, 8),
+    ("bf16", 12, 4, 96, 16),
+    ("f32", 8, 2, 96, 16),
 ]
 
 

@@ -219,7 +219,9 @@ EDGE_CASES = [
     ("bf16", 16, 1, 128, 32),   # MFMA, G = 16
     ("bf16", 4, 4, 128, 64),    # MFMA, G = 1
     ("bf16", 8, 2, 64, 8),      # generic bf16 (block size 8)
-    ("bf16", 6, 2, 96, 16),     # generic bf16 (head_dim 96)
+    ("bf16", 6, 2, 96, 16),     # MFMA bf16, head_dim 96 (12-byte V rows)
+    ("bf16", 16, 2, 96, 32),    # MFMA bf16, head_dim 96, G = 8
+    ("bf16", 6, 2, 96, 8),      # generic bf16, head_dim 96 (block size 8)
     ("f32", 4, 4, 64, 16),      # MFMA fp32, MHA
     ("f32", 32, 8, 128, 16),    # MFMA fp32, G = 4
     ("f32", 14, 2, 128, 32),    # MFMA fp32, G = 7
@@ -229,7 +231,7 @@ EDGE_CASES = [
     ("f16", 14, 2, 64, 32),     # MFMA fp16, G = 7
     ("f16", 16, 1, 128, 16),    # MFMA fp16, G = 16
     ("f16", 8, 2, 64, 8),       # generic fp16 (block size 8)
-    ("f16", 6, 2, 96, 16),      # generic fp16 (head_dim 96)
+    ("f16", 6, 2, 96, 16),      # MFMA fp16, head_dim 96
     ("bf16", 8, 2, 64, 1),      # generic, one token per block
     ("bf16", 8, 2, 128, 128),   # MFMA, 128-token blocks
     ("bf16", 8, 2, 256, 16),    # generic, head_dim 256
