@@ -266,9 +266,10 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * nearest even.  T_b = 0 gives a zero row.  Work is split evenly over all
  * wavefronts the GPU holds at once; a sequence split across wavefronts is
  * merged by a second kernel on the same stream (log-sum-exp weights).
- * Kernels: MFMA for block_size a multiple of 16 and head_dim 64 or 128
- * (bf16, fp16, fp32) or 96 (bf16, fp16); a VALU kernel for head_dim up to 256
- * in steps of 4 and any block size.  At most 16 query heads per KV head and 16384 sequences per
+ * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
+ * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and for
+ * block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4 and
+ * any block size.  At most 16 query heads per KV head and 16384 sequences per
  * call; otherwise PAGEDKV_ERR_UNSUPPORTED. */
 int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
                            int layer, const int32_t* block_tables,

@@ -219,12 +219,16 @@ struct Cursor {
 // [head_dim] tensors a batched gather produces, every sequence is max_len
 // long, and a token takes part only where its mask byte is non-zero (the
 // gather-then-attend path, for comparison with the paged one).
-template <typename E, int D, int TILES, bool APPEND, bool DENSE = false>
+// With SMALL, blocks hold 4 or 8 tokens, so a 16-token tile spans several
+// blocks: each lane looks up the block of its own K row and of its four V
+// rows (which never straddle a block), one vector load each per tile.
+template <typename E, int D, int TILES, bool APPEND, bool DENSE = false, bool SMALL = false>
 struct Stream {
   static constexpr int kTiles = TILES;
   static constexpr int kChunk = 16 * TILES;   // tokens per chunk
   static constexpr bool kAppend = APPEND;
   static constexpr bool kDense = DENSE;
+  static constexpr int kPh = SMALL ? 2 * TILES : TILES;   // block entries held per chunk
   using x8 = typename E::x8;
   using Buf = ChunkBuf<E, D, TILES>;
   static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
@@ -273,6 +277,19 @@ struct Stream {
       for (int t = 0; t < TILES; ++t) ph[t] = 0;
       return;
     }
+    if constexpr (SMALL) {
+      // tokens at or past T look up the block of token T-1: their loads stay
+      // inside the pool and they are masked
+      const int32_t* trow = p.block_tables + (int64_t)c.b * p.max_blocks_per_seq;
+      const int sh = __builtin_ctz(p.pool.block_size);
+      const int tok0 = c.j * (16 * TILES);
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        ph[2 * t] = trow[min(tok0 + 16 * t + n, c.T - 1) >> sh];
+        ph[2 * t + 1] = trow[min(tok0 + 16 * t + 4 * quad, c.T - 1) >> sh];
+      }
+      return;
+    }
     const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
     const int tok0 = c.j * (16 * TILES);
     ph[0] = uni(trow[tok0 / p.pool.block_size]);
@@ -290,6 +307,15 @@ struct Stream {
                               (int64_t)g * p.pool.head_stride +
                               (int64_t)ph[t] * p.pool.block_stride +
                               (int64_t)(tok % p.pool.block_size) * D);
+  }
+
+  // SMALL blocks: byte address of token tok's K (kv = 0) or V (kv = 1) row
+  // in block phys.
+  __device__ __forceinline__ const char* row_addr(int phys, int tok, int kv) const {
+    return p.pool.base + 2 * ((int64_t)p.layer * p.pool.layer_stride +
+                              (int64_t)g * p.pool.head_stride +
+                              (int64_t)phys * p.pool.block_stride + (int64_t)kv * p.pool.kv_stride +
+                              (int64_t)(tok & (p.pool.block_size - 1)) * D);
   }
 
   // Row of the new token of (c.b, g) in k_new (kv = 0) or v_new (kv = 1).
@@ -321,7 +347,11 @@ struct Stream {
     }
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-      const char* kl = tile_base(c, ph, t) + (uint32_t)(2 * (n * D + 8 * quad));
+      const char* kl;
+      if constexpr (SMALL)
+        kl = row_addr(ph[2 * t], c.j * (16 * TILES) + 16 * t + n, 0) + 2 * 8 * quad;
+      else
+        kl = tile_base(c, ph, t) + (uint32_t)(2 * (n * D + 8 * quad));
       if constexpr (APPEND) {
         const int tok = c.j * (16 * TILES) + 16 * t + n;
         if (tok == c.pos) kl = new_row(c, 0) + 2 * 8 * quad;
@@ -352,11 +382,16 @@ struct Stream {
     }
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
-      const char* vl = tile_base(c, ph, t) + 2 * p.pool.kv_stride +
-                       (uint32_t)(2 * (4 * quad * D + VD * n));
+      const char* vl = SMALL ? nullptr
+                             : tile_base(c, ph, t) + 2 * p.pool.kv_stride +
+                                   (uint32_t)(2 * (4 * quad * D + VD * n));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const char* row = vl + 2 * r * D;
+        const char* row;
+        if constexpr (SMALL)
+          row = row_addr(ph[2 * t + 1], c.j * (16 * TILES) + 16 * t + 4 * quad + r, 1) + 2 * VD * n;
+        else
+          row = vl + 2 * r * D;
         if constexpr (APPEND) {
           const int tok = c.j * (16 * TILES) + 16 * t + 4 * quad + r;
           if (tok == c.pos) row = new_row(c, 1) + 2 * VD * n;
@@ -554,6 +589,7 @@ struct StreamF32 {
   static constexpr int kChunk = 16;
   static constexpr bool kAppend = APPEND;
   static constexpr bool kDense = false;
+  static constexpr int kPh = 1;
   static constexpr int KQ = D / 4;    // K floats per lane per tile
   static constexpr int NH = D / 64;   // float4 V loads per row per lane
   static constexpr int NB = D / 16;   // output blocks (h, e)
@@ -779,13 +815,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   st.reset();
   st.load_q(cur);
   typename S::Buf cb;
-  int ph[TILES], ph_nx[TILES], ph_n2[TILES];
+  int ph[S::kPh], ph_nx[S::kPh], ph_n2[S::kPh];
   st.fetch_phys(cur, ph);
   st.issue_k(cb, cur, ph);
   st.issue_v(cb, cur, ph);
   Cursor nx = cur;
 #pragma unroll
-  for (int t = 0; t < TILES; ++t) ph_nx[t] = 0;
+  for (int t = 0; t < S::kPh; ++t) ph_nx[t] = 0;
   if (rem > 1) {
     nx.advance(prefix, lens, poss, p.batch);
     st.fetch_phys(nx, ph_nx);
@@ -803,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     __builtin_amdgcn_sched_barrier(0);
     Cursor n2 = nx;
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) ph_n2[t] = 0;
+    for (int t = 0; t < S::kPh; ++t) ph_n2[t] = 0;
     if (i + 2 < rem) {
       n2.advance(prefix, lens, poss, p.batch);
       st.fetch_phys(n2, ph_n2);
@@ -820,7 +856,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     cur = nx;
     nx = n2;
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) ph_nx[t] = ph_n2[t];
+    for (int t = 0; t < S::kPh; ++t) ph_nx[t] = ph_n2[t];
   }
   st.qk(cb, s);
   st.attend_chunk(s, cb, cur);
@@ -832,9 +868,11 @@ size_t mfma_lds_bytes(int batch) { return sizeof(int32_t) * (size_t)(batch + 1);
 }  // namespace
 
 bool mfma_supported(const kv_pool* pool, int group) {
-  const int d = pool->head_dim;
-  const bool dim_ok = d == 64 || d == 128 || (d == 96 && pool->dtype != PAGEDKV_F32);
-  return dim_ok && pool->block_size % 16 == 0 && group >= 1 && group <= kMaxGroup;
+  const int d = pool->head_dim, bs = pool->block_size;
+  const bool half = pool->dtype != PAGEDKV_F32;
+  const bool dim_ok = d == 64 || d == 128 || (d == 96 && half);
+  const bool bs_ok = bs % 16 == 0 || ((bs == 4 || bs == 8) && half);
+  return dim_ok && bs_ok && group >= 1 && group <= kMaxGroup;
 }
 
 int mfma_chunk_tokens() { return 16 * kTilesPerStep; }
@@ -853,6 +891,19 @@ void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
     if (p.pool.head_dim == 128) launch_one<Stream<E, 128, T, false, true>>(p, wgs, lds, s);
     else if (p.pool.head_dim == 96) launch_one<Stream<E, 96, T, false, true>>(p, wgs, lds, s);
     else launch_one<Stream<E, 64, T, false, true>>(p, wgs, lds, s);
+    return;
+  }
+  if (p.pool.block_size < 16) {   // 4 or 8 tokens per block
+    if (p.pool.head_dim == 128) {
+      if (append) launch_one<Stream<E, 128, T, true, false, true>>(p, wgs, lds, s);
+      else launch_one<Stream<E, 128, T, false, false, true>>(p, wgs, lds, s);
+    } else if (p.pool.head_dim == 96) {
+      if (append) launch_one<Stream<E, 96, T, true, false, true>>(p, wgs, lds, s);
+      else launch_one<Stream<E, 96, T, false, false, true>>(p, wgs, lds, s);
+    } else {
+      if (append) launch_one<Stream<E, 64, T, true, false, true>>(p, wgs, lds, s);
+      else launch_one<Stream<E, 64, T, false, false, true>>(p, wgs, lds, s);
+    }
     return;
   }
   if (p.pool.head_dim == 128) {

@@ -97,6 +97,8 @@ SHAPES = [
     ("f16", 8, 2, 128, 16),
     ("f16", 8, 2, 64, 8),
     ("bf16", 12, 4, 96, 16),
+    ("bf16", 8, 2, 128, 4),
+    ("f16", 8, 2, 96, 8),
     ("f32", 8, 2, 96, 16),
 ]
 

@@ -218,10 +218,12 @@ EDGE_CASES = [
     ("bf16", 14, 2, 64, 16),    # MFMA, G = 7
     ("bf16", 16, 1, 128, 32),   # MFMA, G = 16
     ("bf16", 4, 4, 128, 64),    # MFMA, G = 1
-    ("bf16", 8, 2, 64, 8),      # generic bf16 (block size 8)
+    ("bf16", 8, 2, 64, 8),      # MFMA bf16, 8-token blocks (per-lane block lookups)
+    ("bf16", 8, 2, 128, 4),     # MFMA bf16, 4-token blocks
+    ("bf16", 6, 2, 64, 2),      # generic bf16 (2-token blocks)
     ("bf16", 6, 2, 96, 16),     # MFMA bf16, head_dim 96 (12-byte V rows)
     ("bf16", 16, 2, 96, 32),    # MFMA bf16, head_dim 96, G = 8
-    ("bf16", 6, 2, 96, 8),      # generic bf16, head_dim 96 (block size 8)
+    ("bf16", 6, 2, 96, 8),      # MFMA bf16, head_dim 96, 8-token blocks
     ("f32", 4, 4, 64, 16),      # MFMA fp32, MHA
     ("f32", 32, 8, 128, 16),    # MFMA fp32, G = 4
     ("f32", 14, 2, 128, 32),    # MFMA fp32, G = 7
@@ -230,7 +232,8 @@ EDGE_CASES = [
     ("f16", 8, 2, 128, 16),     # MFMA fp16, G = 4
     ("f16", 14, 2, 64, 32),     # MFMA fp16, G = 7
     ("f16", 16, 1, 128, 16),    # MFMA fp16, G = 16
-    ("f16", 8, 2, 64, 8),       # generic fp16 (block size 8)
+    ("f16", 8, 2, 64, 8),       # MFMA fp16, 8-token blocks
+    ("f16", 14, 2, 64, 4),      # MFMA fp16, 4-token blocks, G = 7
     ("f16", 6, 2, 96, 16),      # MFMA fp16, head_dim 96
     ("bf16", 8, 2, 64, 1),      # generic, one token per block
     ("bf16", 8, 2, 128, 128),   # MFMA, 128-token blocks
@@ -253,7 +256,8 @@ def test_decode_edge_lengths_with_poison(dtype, Hq, Hkv, D, BS):
     assert not dev_to_np(out)[zero_rows].any(), "empty sequences must give zero rows"
 
 
-@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("f32", 64, 16), ("f16", 128, 16)])
+@pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("f32", 64, 16), ("f16", 128, 16),
+                                        ("bf16", 128, 8)])
 def test_decode_block_permutation_invariance(dtype, D, BS):
     say(f"decode permutation invariance {dtype}")
     w = custom(dtype, 9, 8, 2, D, BS, [300, 1, 17, 0, 900, 64, 33, 2048, 5], nb_slack=40)
