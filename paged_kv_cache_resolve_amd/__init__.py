@@ -327,7 +327,9 @@ _WS_BYTES: dict = {}
 
 
 def paged_attention_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int) -> int:
-    key = (pool.handle.value, pool.device.index, batch, num_q_heads)
+    # keyed on what the size depends on, not on the pool handle: a destroyed
+    # pool's address can come back for a pool of another shape
+    key = (pool.kv_heads, pool.head_dim, batch, num_q_heads)
     n = _WS_BYTES.get(key)
     if n is None:
         n = _L.paged_attention_workspace_bytes(pool.handle, batch, num_q_heads)
