@@ -269,8 +269,12 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
  * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and for
  * block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4 and
- * any block size.  At most 16 query heads per KV head and 16384 sequences per
- * call; otherwise PAGEDKV_ERR_UNSUPPORTED. */
+ * any block size.  At most 16384 sequences per call; otherwise
+ * PAGEDKV_ERR_UNSUPPORTED.  A KV head with more than 16 query heads (MQA,
+ * wide GQA groups) is served as q "virtual" heads of G/q query heads each, q
+ * the smallest divisor of G = num_q_heads / kv_heads with G/q <= 16; each
+ * virtual head reads the KV head's rows itself, so K/V traffic is q times
+ * that of one pass. */
 int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
                            int layer, const int32_t* block_tables,
                            int max_blocks_per_seq, const int32_t* context_lens,
@@ -317,7 +321,8 @@ size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads,
  *            iff mask[b][t] != 0.  A sequence with no such token gives zeros.
  * Every one of the max_len rows is read, padding included.  Same arithmetic
  * and tolerances as paged_attention_decode.  bf16 and fp16, head_dim 64, 96
- * or 128, up to 16 query heads per KV head; otherwise PAGEDKV_ERR_UNSUPPORTED.
+ * or 128, any number of query heads per KV head (split as in
+ * paged_attention_decode); otherwise PAGEDKV_ERR_UNSUPPORTED.
  * workspace as for paged_attention_decode (256-byte aligned). */
 int dense_attention_decode(void* out, const void* q, const void* k, const void* v,
                            const uint8_t* mask, int batch, int max_len, int kv_heads,

@@ -54,6 +54,17 @@ void decode_workspace_carve(void* ws, int batch, int kv_heads, int group, int he
   *o = reinterpret_cast<float*>(p);
 }
 
+// Query heads per KV head beyond kMaxGroup (MQA, wide GQA groups): the
+// kernels serve each KV head as qsplit "virtual" KV heads of group / qsplit
+// consecutive query heads, qsplit the smallest divisor of group that brings
+// the share to kMaxGroup or less.  Every virtual head streams its KV head's
+// rows itself, so K/V are read qsplit times.
+HeadSplit head_split(int kv_heads, int group) {
+  int q = (group + kMaxGroup - 1) / kMaxGroup;
+  while (group % q != 0) ++q;
+  return HeadSplit{q, group / q, kv_heads * q};
+}
+
 }  // namespace pagedkv
 
 extern "C" {
@@ -193,8 +204,8 @@ int paged_kv_gather(void* k_out, void* v_out, uint8_t* mask, const kv_pool_t* po
 
 size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch, int num_q_heads) {
   if (!pool || batch < 0 || num_q_heads < 1 || num_q_heads % pool->kv_heads != 0) return 0;
-  return decode_workspace_bytes(batch, pool->kv_heads, num_q_heads / pool->kv_heads,
-                                pool->head_dim);
+  const HeadSplit hs = head_split(pool->kv_heads, num_q_heads / pool->kv_heads);
+  return decode_workspace_bytes(batch, hs.vheads, hs.group, pool->head_dim);
 }
 
 }  // extern "C"
@@ -217,10 +228,10 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   if (!aligned16(out) || !aligned16(q) || (append && (!aligned16(k_new) || !aligned16(v_new))))
     return PAGEDKV_ERR_INVALID_ARG;
   if (batch > kMaxBatchLds) return PAGEDKV_ERR_UNSUPPORTED;
-  const int group = num_q_heads / pool->kv_heads;
-  const bool use_mfma = mfma_supported(pool, group);
-  if (!use_mfma && !generic_supported(pool, group)) return PAGEDKV_ERR_UNSUPPORTED;
-  const size_t need = decode_workspace_bytes(batch, pool->kv_heads, group, pool->head_dim);
+  const HeadSplit hs = head_split(pool->kv_heads, num_q_heads / pool->kv_heads);
+  const bool use_mfma = mfma_supported(pool, hs.group);
+  if (!use_mfma && !generic_supported(pool, hs.group)) return PAGEDKV_ERR_UNSUPPORTED;
+  const size_t need = decode_workspace_bytes(batch, hs.vheads, hs.group, pool->head_dim);
   if (!workspace || workspace_bytes < need) return PAGEDKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PAGEDKV_ERR_WORKSPACE;
 
@@ -231,13 +242,15 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   p.out = out;
   p.block_tables = block_tables;
   p.context_lens = context_lens;
-  decode_workspace_carve(workspace, batch, pool->kv_heads, group, pool->head_dim, &p.ws_prefix,
+  decode_workspace_carve(workspace, batch, hs.vheads, hs.group, pool->head_dim, &p.ws_prefix,
                          &p.ws_ml, &p.ws_o);
   p.layer = layer;
   p.max_blocks_per_seq = max_blocks_per_seq;
   p.batch = batch;
   p.num_q_heads = num_q_heads;
-  p.group = group;
+  p.group = hs.group;
+  p.vheads = hs.vheads;
+  p.qsplit = hs.qsplit;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.dtype = pool->dtype;
   p.min_chunks = 0;   // launcher default
@@ -293,7 +306,8 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
 size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads, int head_dim) {
   if (batch < 0 || kv_heads < 1 || num_q_heads < 1 || num_q_heads % kv_heads != 0 || head_dim < 1)
     return 0;
-  return decode_workspace_bytes(batch, kv_heads, num_q_heads / kv_heads, head_dim);
+  const HeadSplit hs = head_split(kv_heads, num_q_heads / kv_heads);
+  return decode_workspace_bytes(batch, hs.vheads, hs.group, head_dim);
 }
 
 int dense_attention_decode(void* out, const void* q, const void* k, const void* v,
@@ -307,13 +321,12 @@ int dense_attention_decode(void* out, const void* q, const void* k, const void* 
   if (!out || !q || (max_len > 0 && (!k || !v || !mask))) return PAGEDKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v))
     return PAGEDKV_ERR_INVALID_ARG;
-  const int group = num_q_heads / kv_heads;
+  const HeadSplit hs = head_split(kv_heads, num_q_heads / kv_heads);
   if ((dtype != PAGEDKV_BF16 && dtype != PAGEDKV_F16) ||
-      (head_dim != 64 && head_dim != 96 && head_dim != 128) ||
-      group > kMaxGroup || batch > kMaxBatchLds)
+      (head_dim != 64 && head_dim != 96 && head_dim != 128) || batch > kMaxBatchLds)
     return PAGEDKV_ERR_UNSUPPORTED;
   if ((int64_t)batch * ((max_len + 31) / 32) > INT32_MAX) return PAGEDKV_ERR_UNSUPPORTED;
-  const size_t need = decode_workspace_bytes(batch, kv_heads, group, head_dim);
+  const size_t need = decode_workspace_bytes(batch, hs.vheads, hs.group, head_dim);
   if (!workspace || workspace_bytes < need) return PAGEDKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PAGEDKV_ERR_WORKSPACE;
 
@@ -326,11 +339,13 @@ int dense_attention_decode(void* out, const void* q, const void* k, const void* 
   p.max_blocks_per_seq = max_len > 0 ? (max_len + 15) / 16 : 1;
   p.q = q;
   p.out = out;
-  decode_workspace_carve(workspace, batch, kv_heads, group, head_dim, &p.ws_prefix, &p.ws_ml,
+  decode_workspace_carve(workspace, batch, hs.vheads, hs.group, head_dim, &p.ws_prefix, &p.ws_ml,
                          &p.ws_o);
   p.batch = batch;
   p.num_q_heads = num_q_heads;
-  p.group = group;
+  p.group = hs.group;
+  p.vheads = hs.vheads;
+  p.qsplit = hs.qsplit;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.dtype = dtype;
   p.k_dense = k ? k : q;   // max_len == 0: never read

@@ -93,7 +93,9 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
   const int BS = p.pool.block_size;
   const int T = p.context_lens[b];
   const TS* pool = reinterpret_cast<const TS*>(p.pool.base);
-  const int64_t head_off = (int64_t)p.layer * p.pool.layer_stride + (int64_t)g * p.pool.head_stride;
+  // g is a virtual KV head (G query heads); the pool's head is g / qsplit
+  const int64_t head_off =
+      (int64_t)p.layer * p.pool.layer_stride + (int64_t)(g / p.qsplit) * p.pool.head_stride;
   const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
 
   // q rows of the group, pre-multiplied by scale*log2(e)
@@ -189,7 +191,7 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
   }
 
   const bool whole = (j0 == 0 && j1 == nb);
-  const int64_t slot = partial_slot(b, g, unit, p.pool.kv_heads);
+  const int64_t slot = partial_slot(b, g, unit, p.vheads);
 #pragma unroll
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h >= G) continue;
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeParams p) {
     for (int i = threadIdx.x; i <= p.batch; i += 64) p.ws_prefix[i] = prefix[i];
 
   const int lane = threadIdx.x;
-  const int H = p.pool.kv_heads;
+  const int H = p.vheads;
   const int64_t unit = blockIdx.x / H;
   const int g = (int)(blockIdx.x - unit * H);
   const int64_t C = prefix[p.batch];
@@ -278,10 +280,10 @@ hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   int waves = wgs;
   if (waves > kMaxWaves) waves = kMaxWaves;
-  p.units = waves / p.pool.kv_heads;   // head groups
+  p.units = waves / p.vheads;   // head groups
   if (p.units < 1) {
     p.units = 1;
-    waves = p.pool.kv_heads;
+    waves = p.vheads;
   }
   if (p.min_chunks < 1) p.min_chunks = 2;
   // no more units than the largest possible chunk count can keep busy
@@ -290,7 +292,7 @@ hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s) {
   const int64_t useful = (max_chunks + p.min_chunks - 1) / p.min_chunks;
   if (useful < p.units) {
     p.units = (int)(useful < 1 ? 1 : useful);
-    waves = p.units * p.pool.kv_heads;
+    waves = p.units * p.vheads;
   }
   const dim3 grid(waves), block(64);
   if (f32) {

@@ -37,13 +37,14 @@ template <> __device__ __forceinline__ _Float16 out_cast<_Float16>(float x) { re
 // cross-lane traffic at all.
 template <typename TS>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
-  const int H = p.pool.kv_heads;
+  const int H = p.vheads;   // (virtual) KV heads of G query heads each
   const int G = p.group;
   const int D = p.pool.head_dim;
   const int lane = threadIdx.x;
   const int b = blockIdx.x / p.num_q_heads;
   const int h = blockIdx.x - b * p.num_q_heads;
-  const int g = h / G;
+  const int g = h / G;           // virtual KV head
+  const int gp = g / p.qsplit;   // the pool's KV head
   const int hn = h - g * G;
   TS* out = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + h) * D;
 
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   // append, its position and the new K/V row (one 16-byte unit per lane;
   // fused appends come with head_dim * element size <= 256 bytes, so one
   // pass of 64 lanes covers both rows).
-  const bool app = p.positions != nullptr && hn == 0;
+  const bool app = p.positions != nullptr && hn == 0 && g % p.qsplit == 0;
   const int units = D * (int)sizeof(TS) / 16;   // 16-byte units per row
   const int kv = lane >= units;
   const int u = lane - kv * units;
@@ -61,12 +62,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
     pos = p.positions[b];
     if (lane < 2 * units)
       row_unit = reinterpret_cast<const uint4*>(static_cast<const TS*>(kv ? p.v_new : p.k_new) +
-                                                ((int64_t)b * H + g) * D)[u];
+                                                ((int64_t)b * p.pool.kv_heads + gp) * D)[u];
   }
   const int pb = p.ws_prefix[b];
   const int nb = p.ws_prefix[b + 1] - pb;
   const int64_t C = p.ws_prefix[p.batch];
-  // the first wave of each (b, g) stores the new token of that KV head; the
+  // the first wave of each (b, pool head) stores the new token of that head; the
   // store is made at every exit so that the table load overlaps the merge
   const bool store_row = app && pos >= 0 && lane < 2 * units;
   const int phys =
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   auto append_row = [&]() {
     if (!store_row) return;
     const int64_t row = (int64_t)phys * p.pool.block_stride + (int64_t)p.layer * p.pool.layer_stride +
-                        (int64_t)g * p.pool.head_stride + (int64_t)(pos % p.pool.block_size) * D;
+                        (int64_t)gp * p.pool.head_stride + (int64_t)(pos % p.pool.block_size) * D;
     reinterpret_cast<uint4*>(reinterpret_cast<TS*>(const_cast<char*>(p.pool.base)) + row +
                              kv * p.pool.kv_stride)[u] = row_unit;
   };
@@ -92,7 +93,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   }
   const int K = (int)(ul - uf + 1);
 
-  // partials of (b, g) from units uf..ul sit kv_heads slots apart
+  // partials of (b, g) from units uf..ul sit H slots apart
   const int64_t slot0 = partial_slot(b, g, uf, H);
   const int64_t stride_o = (int64_t)H * G * D;
   const int64_t stride_m = (int64_t)H * G * 2;

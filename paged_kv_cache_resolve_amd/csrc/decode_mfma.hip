@@ -237,7 +237,8 @@ struct Stream {
 
   const DecodeParams& p;
   const int lane, n, quad;
-  const int g;              // KV head served by this wavefront
+  const int g;              // (virtual) KV head served by this wavefront
+  const int gp;             // the pool's KV head it reads
   const int64_t unit;       // head group (chunk range) of this wavefront
 
   x8 qop[NK];
@@ -245,7 +246,8 @@ struct Stream {
   float m, l;
 
   __device__ Stream(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
-      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), unit(unit_) {}
+      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), gp(g_ / p_.qsplit),
+        unit(unit_) {}
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -304,7 +306,7 @@ struct Stream {
   __device__ __forceinline__ const char* tile_base(const Cursor& c, const int* ph, int t) const {
     const int tok = c.j * (16 * TILES) + 16 * t;
     return p.pool.base + 2 * ((int64_t)p.layer * p.pool.layer_stride +
-                              (int64_t)g * p.pool.head_stride +
+                              (int64_t)gp * p.pool.head_stride +
                               (int64_t)ph[t] * p.pool.block_stride +
                               (int64_t)(tok % p.pool.block_size) * D);
   }
@@ -313,7 +315,7 @@ struct Stream {
   // in block phys.
   __device__ __forceinline__ const char* row_addr(int phys, int tok, int kv) const {
     return p.pool.base + 2 * ((int64_t)p.layer * p.pool.layer_stride +
-                              (int64_t)g * p.pool.head_stride +
+                              (int64_t)gp * p.pool.head_stride +
                               (int64_t)phys * p.pool.block_stride + (int64_t)kv * p.pool.kv_stride +
                               (int64_t)(tok & (p.pool.block_size - 1)) * D);
   }
@@ -321,7 +323,7 @@ struct Stream {
   // Row of the new token of (c.b, g) in k_new (kv = 0) or v_new (kv = 1).
   __device__ __forceinline__ const char* new_row(const Cursor& c, int kv) const {
     return static_cast<const char*>(kv ? p.v_new : p.k_new) +
-           2 * ((int64_t)c.b * p.pool.kv_heads + g) * D;
+           2 * ((int64_t)c.b * p.pool.kv_heads + gp) * D;
   }
 
   // Dense batches: byte address of token tok's row of head g (tokens past
@@ -330,7 +332,7 @@ struct Stream {
                                                    int tok) const {
     const int tc = min(tok, c.T - 1);
     return static_cast<const char*>(base) +
-           2 * ((((int64_t)c.b * p.dense_len + tc) * p.pool.kv_heads + g) * D);
+           2 * ((((int64_t)c.b * p.dense_len + tc) * p.pool.kv_heads + gp) * D);
   }
 
   __device__ __forceinline__ void issue_k(Buf& cb, const Cursor& c,
@@ -541,7 +543,7 @@ struct Stream {
                              E::pack2(acc[2][r] * inv, acc[3][r] * inv));
       }
     } else {
-      const int64_t slot = partial_slot(c.b, g, unit, p.pool.kv_heads);
+      const int64_t slot = partial_slot(c.b, g, unit, p.vheads);
       float* of = p.ws_o + (slot * G + n) * D + 4 * VD * quad;
       if constexpr (VD % 4 == 0) {
         float4* o = reinterpret_cast<float4*>(of);
@@ -600,7 +602,8 @@ struct StreamF32 {
 
   const DecodeParams& p;
   const int lane, n, quad;
-  const int g;
+  const int g;              // (virtual) KV head served by this wavefront
+  const int gp;             // the pool's KV head it reads
   const int64_t unit;
 
   float qop[KQ];
@@ -608,7 +611,8 @@ struct StreamF32 {
   float m, l;
 
   __device__ StreamF32(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
-      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), unit(unit_) {}
+      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), gp(g_ / p_.qsplit),
+        unit(unit_) {}
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -641,14 +645,14 @@ struct StreamF32 {
   __device__ __forceinline__ const char* tile_base(const Cursor& c, const int* ph) const {
     const int tok = c.j * 16;
     return p.pool.base + 4 * ((int64_t)p.layer * p.pool.layer_stride +
-                              (int64_t)g * p.pool.head_stride +
+                              (int64_t)gp * p.pool.head_stride +
                               (int64_t)ph[0] * p.pool.block_stride +
                               (int64_t)(tok % p.pool.block_size) * D);
   }
 
   __device__ __forceinline__ const char* new_row(const Cursor& c, int kv) const {
     return static_cast<const char*>(kv ? p.v_new : p.k_new) +
-           4 * ((int64_t)c.b * p.pool.kv_heads + g) * D;
+           4 * ((int64_t)c.b * p.pool.kv_heads + gp) * D;
   }
 
   __device__ __forceinline__ void issue_k(Buf& cb, const Cursor& c, const int* ph) const {
@@ -759,7 +763,7 @@ struct StreamF32 {
               make_float4(acc[4 * h][r] * inv, acc[4 * h + 1][r] * inv, acc[4 * h + 2][r] * inv,
                           acc[4 * h + 3][r] * inv);
     } else {
-      const int64_t slot = partial_slot(c.b, g, unit, p.pool.kv_heads);
+      const int64_t slot = partial_slot(c.b, g, unit, p.vheads);
       float* o = p.ws_o + (slot * G + n) * D + 16 * quad;
 #pragma unroll
       for (int h = 0; h < NH; ++h)
@@ -780,7 +784,7 @@ template <typename S>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ int32_t prefix[];
   __shared__ int32_t scan[kThreads];
-  const int H = p.pool.kv_heads;
+  const int H = p.vheads;   // (virtual) KV heads
 
   constexpr int TILES = S::kTiles;
   if constexpr (S::kDense) {   // every sequence is dense_len tokens long
@@ -942,10 +946,10 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   if (e != hipSuccess) return e;
   const int dev_wgs = wgs;
   wgs = decode_workgroups(dev_wgs);
-  p.units = wgs * kWaves / p.pool.kv_heads;   // head groups
-  if (p.units < 1) {                          // more KV heads than resident waves
+  p.units = wgs * kWaves / p.vheads;   // head groups
+  if (p.units < 1) {                   // more KV heads than resident waves
     p.units = 1;
-    wgs = (p.pool.kv_heads + kWaves - 1) / kWaves;
+    wgs = (p.vheads + kWaves - 1) / kWaves;
   }
   if (p.min_chunks < 1) p.min_chunks = 2;
   // no more units than the largest possible chunk count can keep busy
@@ -954,7 +958,7 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   const int64_t useful = (max_chunks + p.min_chunks - 1) / p.min_chunks;
   if (useful < p.units) {
     p.units = (int)(useful < 1 ? 1 : useful);
-    wgs = (p.units * p.pool.kv_heads + kWaves - 1) / kWaves;
+    wgs = (p.units * p.vheads + kWaves - 1) / kWaves;
   }
   if (p.dtype == PAGEDKV_F32)
     launch_f32(p, wgs, lds, s);

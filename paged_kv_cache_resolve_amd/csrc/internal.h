@@ -99,6 +99,12 @@ struct DecodeParams {
   const void* k_new;
   const void* v_new;
   const int32_t* positions;
+  // More than kMaxGroup query heads per KV head: each KV head is served as
+  // qsplit virtual KV heads of group = G / qsplit consecutive query heads
+  // (vheads = kv_heads * qsplit).  Work split, q/out rows and partial slots
+  // use the virtual head; pool addressing uses virtual / qsplit.
+  int vheads;
+  int qsplit;
   // Dense decode (null for the paged forms): K and V as [batch][dense_len]
   // [kv_heads][head_dim], token t of sequence b attended where mask[b][t] != 0.
   const void* k_dense;
@@ -112,6 +118,15 @@ constexpr int kMaxGroup = 16;            // query heads per KV head
 constexpr int kDecodeWgPerCu = 1;        // decode workgroups (4 wavefronts) per CU
 constexpr int kGenericChunk = 64;        // tokens per chunk, VALU kernel
 constexpr int kMaxBatchLds = 16384;      // sequences whose prefix fits in LDS
+
+// How the query heads of one KV head are spread over virtual KV heads of at
+// most kMaxGroup query heads each (api.cpp).
+struct HeadSplit {
+  int qsplit;   // virtual heads per KV head
+  int group;    // query heads per virtual head
+  int vheads;   // kv_heads * qsplit
+};
+HeadSplit head_split(int kv_heads, int group);
 
 size_t decode_workspace_bytes(int batch, int kv_heads, int group, int head_dim);
 void decode_workspace_carve(void* ws, int batch, int kv_heads, int group,

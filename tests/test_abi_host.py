@@ -146,7 +146,8 @@ def test_entry_points_validate_before_launch():
     assert dec(batch=-1) == _lib.ERR_INVALID_ARG
     assert dec(out=None) == _lib.ERR_INVALID_ARG
     assert dec(scale=float("nan")) == _lib.ERR_INVALID_ARG
-    assert dec(hq=2 * 17) == _lib.ERR_UNSUPPORTED                      # 17 heads per KV head
+    ws34 = L.paged_attention_workspace_bytes(h, 4, 2 * 17)             # 17 heads per KV head
+    assert ws34 > 0 and dec(hq=2 * 17, wsb=ws34 - 1) == _lib.ERR_WORKSPACE
     assert dec(wsb=ws_bytes - 1) == _lib.ERR_WORKSPACE
     assert dec(ws=None) == _lib.ERR_WORKSPACE
     assert dec(ws=ctypes.c_void_p(p.value + 64)) == _lib.ERR_WORKSPACE  # misaligned
@@ -204,12 +205,51 @@ def test_entry_points_validate_before_launch():
     assert dd(max_len=-1) == _lib.ERR_INVALID_ARG
     assert dd(dtype=_lib.F32) == _lib.ERR_UNSUPPORTED
     assert dd(d=80) == _lib.ERR_UNSUPPORTED
-    assert dd(hq=2 * 17) == _lib.ERR_UNSUPPORTED
+    dws34 = L.dense_attention_workspace_bytes(4, 2, 2 * 17, 128)
+    assert dws34 > 0 and dd(hq=2 * 17, wsb=dws34 - 1) == _lib.ERR_WORKSPACE
     assert dd(wsb=dws - 1) == _lib.ERR_WORKSPACE
     assert dd(batch=0, out=None) == 0
     assert L.paged_kv_resolve(p, p, 4, p, 4, 0, 16, None) == _lib.ERR_INVALID_ARG
     assert L.paged_kv_resolve(None, p, 4, p, 4, 16, 16, None) == _lib.ERR_INVALID_ARG
     L.kv_pool_destroy(h)
+
+
+def _align256(n):
+    return (n + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("hkv,hq,qsplit", [(2, 8, 1), (2, 32, 1), (1, 32, 2), (2, 34, 17),
+                                           (2, 40, 2), (1, 48, 3), (4, 96, 2), (1, 64, 4),
+                                           (1, 18, 2), (1, 51, 17)])
+def test_wide_groups_workspace(hkv, hq, qsplit):
+    """More than 16 query heads per KV head: the KV head is served as qsplit
+    virtual heads, qsplit the smallest divisor of the group that leaves at most
+    16 query heads each; the workspace holds one partial slot per virtual head
+    and its share of the query heads."""
+    h = _pool(nb=8, layers=1, hkv=hkv, d=64)
+    batch, g = 5, hq // hkv // qsplit
+    assert g <= 16 and (hq // hkv) % qsplit == 0
+    slots = batch * hkv * qsplit + 8192
+    want = _align256(4 * (batch + 1)) + _align256(4 * slots * g * 2) + _align256(4 * slots * g * 64)
+    assert L.paged_attention_workspace_bytes(h, batch, hq) == want
+    assert L.dense_attention_workspace_bytes(batch, hkv, hq, 64) == want
+    L.kv_pool_destroy(h)
+
+
+def test_binding_workspace_size_follows_pool_shape():
+    """The binding's workspace-size cache must not outlive a pool: a new pool
+    of another shape that reuses a destroyed pool's handle address gets its
+    own size."""
+    import types
+    sizes = []
+    for hkv, d in [(8, 128), (1, 128), (2, 64)]:
+        h = _pool(nb=8, layers=1, hkv=hkv, d=d)
+        pool = types.SimpleNamespace(handle=h, kv_heads=hkv, head_dim=d)
+        got = pk.paged_attention_workspace_bytes(pool, 300, 32)
+        assert got == L.paged_attention_workspace_bytes(h, 300, 32)
+        sizes.append(got)
+        L.kv_pool_destroy(h)
+    assert len(set(sizes)) == 3
 
 
 def test_binding_refuses_host_tensors():

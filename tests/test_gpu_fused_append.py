@@ -100,6 +100,10 @@ SHAPES = [
     ("bf16", 8, 2, 128, 4),
     ("f16", 8, 2, 96, 8),
     ("f32", 8, 2, 96, 16),
+    ("bf16", 32, 1, 128, 16),   # G = 32: the new row is stored once per KV head
+    ("f16", 40, 2, 64, 8),      # G = 20
+    ("f32", 34, 2, 64, 16),     # G = 17
+    ("bf16", 36, 2, 64, 2),     # generic, G = 18
 ]
 
 
