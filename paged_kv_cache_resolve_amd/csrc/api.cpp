@@ -55,14 +55,13 @@ void decode_workspace_carve(void* ws, int batch, int kv_heads, int group, int he
 }
 
 // Query heads per KV head beyond kMaxGroup (MQA, wide GQA groups): the
-// kernels serve each KV head as qsplit "virtual" KV heads of group / qsplit
-// consecutive query heads, qsplit the smallest divisor of group that brings
-// the share to kMaxGroup or less.  Every virtual head streams its KV head's
-// rows itself, so K/V are read qsplit times.
+// kernels serve each KV head as qsplit = ceil(group / kMaxGroup) "virtual"
+// KV heads of floor or ceil(group / qsplit) consecutive query heads each.
+// Every virtual head streams its KV head's rows itself, so K/V are
+// requested qsplit times.
 HeadSplit head_split(int kv_heads, int group) {
-  int q = (group + kMaxGroup - 1) / kMaxGroup;
-  while (group % q != 0) ++q;
-  return HeadSplit{q, group / q, kv_heads * q};
+  const int q = (group + kMaxGroup - 1) / kMaxGroup;
+  return HeadSplit{q, (group + q - 1) / q, kv_heads * q};
 }
 
 }  // namespace pagedkv
@@ -251,6 +250,7 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   p.group = hs.group;
   p.vheads = hs.vheads;
   p.qsplit = hs.qsplit;
+  p.kv_group = num_q_heads / pool->kv_heads;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.dtype = pool->dtype;
   p.min_chunks = 0;   // launcher default
@@ -346,6 +346,7 @@ int dense_attention_decode(void* out, const void* q, const void* k, const void* 
   p.group = hs.group;
   p.vheads = hs.vheads;
   p.qsplit = hs.qsplit;
+  p.kv_group = num_q_heads / kv_heads;
   p.scale_log2 = scale * 1.4426950408889634f;
   p.dtype = dtype;
   p.k_dense = k ? k : q;   // max_len == 0: never read

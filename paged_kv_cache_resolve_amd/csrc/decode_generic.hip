@@ -88,18 +88,20 @@ template <typename TS, int DPL>
 __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs, float* ps, int lane,
                                 int64_t unit, int b, int g, int j0, int j1, int nb) {
   constexpr int VB = 32 / DPL;   // V rows in flight per batch
-  const int G = p.group;
+  const int GS = p.group;   // partial slot stride
+  const VHead vh = vhead_rows(g, p.qsplit, p.kv_group);
+  const int G = vh.count;   // query heads of this (virtual) KV head
   const int D = p.pool.head_dim;
   const int BS = p.pool.block_size;
   const int T = p.context_lens[b];
   const TS* pool = reinterpret_cast<const TS*>(p.pool.base);
-  // g is a virtual KV head (G query heads); the pool's head is g / qsplit
+  // g is a virtual KV head; the pool's head is g / qsplit
   const int64_t head_off =
       (int64_t)p.layer * p.pool.layer_stride + (int64_t)(g / p.qsplit) * p.pool.head_stride;
   const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
 
   // q rows of the group, pre-multiplied by scale*log2(e)
-  const TS* q = static_cast<const TS*>(p.q) + ((int64_t)b * p.num_q_heads + (int64_t)g * G) * D;
+  const TS* q = static_cast<const TS*>(p.q) + ((int64_t)b * p.num_q_heads + vh.first) * D;
   for (int i = lane; i < G * D; i += 64) qs[i] = to_f32<TS>(q[i]) * p.scale_log2;
   __syncthreads();
 
@@ -196,7 +198,7 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
   for (int h = 0; h < kMaxGroup; ++h) {
     if (h >= G) continue;
     if (whole) {
-      TS* o = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + (int64_t)g * G + h) * D;
+      TS* o = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + vh.first + h) * D;
       const float inv = 1.0f / l[h];
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
@@ -204,15 +206,15 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
         if (d < D) o[d] = from_f32<TS>(acc[h][i] * inv);
       }
     } else {
-      float* o = p.ws_o + (slot * G + h) * D;
+      float* o = p.ws_o + (slot * GS + h) * D;
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
         const int d = lane + 64 * i;
         if (d < D) o[d] = acc[h][i];
       }
       if (lane == 0) {
-        p.ws_ml[(slot * G + h) * 2 + 0] = m[h];
-        p.ws_ml[(slot * G + h) * 2 + 1] = l[h];
+        p.ws_ml[(slot * GS + h) * 2 + 0] = m[h];
+        p.ws_ml[(slot * GS + h) * 2 + 1] = l[h];
       }
     }
   }

@@ -37,15 +37,15 @@ template <> __device__ __forceinline__ _Float16 out_cast<_Float16>(float x) { re
 // cross-lane traffic at all.
 template <typename TS>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
-  const int H = p.vheads;   // (virtual) KV heads of G query heads each
-  const int G = p.group;
+  const int H = p.vheads;   // (virtual) KV heads
+  const int G = p.group;    // partial slot stride
   const int D = p.pool.head_dim;
   const int lane = threadIdx.x;
   const int b = blockIdx.x / p.num_q_heads;
   const int h = blockIdx.x - b * p.num_q_heads;
-  const int g = h / G;           // virtual KV head
+  int g, hn;   // virtual KV head of h and h's column in it
+  vhead_of(h, p.qsplit, p.kv_group, &g, &hn);
   const int gp = g / p.qsplit;   // the pool's KV head
-  const int hn = h - g * G;
   TS* out = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + h) * D;
 
   // Independent loads first: the sequence's chunk range and, for a fused

@@ -239,6 +239,7 @@ struct Stream {
   const int lane, n, quad;
   const int g;              // (virtual) KV head served by this wavefront
   const int gp;             // the pool's KV head it reads
+  int qh0, gw;              // its query heads: qh0 .. qh0 + gw - 1
   const int64_t unit;       // head group (chunk range) of this wavefront
 
   x8 qop[NK];
@@ -247,7 +248,11 @@ struct Stream {
 
   __device__ Stream(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
       : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), gp(g_ / p_.qsplit),
-        unit(unit_) {}
+        unit(unit_) {
+    const VHead v = vhead_rows(g_, p_.qsplit, p_.kv_group);
+    qh0 = v.first;
+    gw = v.count;
+  }
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -256,15 +261,14 @@ struct Stream {
     l = 0.f;
   }
 
-  // q of the sequence's G query heads of this KV head in the B-operand
-  // layout.  MFMA columns n >= G carry a copy of head G-1: every column goes
-  // through its own softmax and accumulator and only columns n < G are ever
-  // written, so the copies cost nothing and need neither a branch nor masking.
+  // q of the sequence's gw query heads of this (virtual) KV head in the
+  // B-operand layout.  MFMA columns n >= gw carry a copy of the last head:
+  // every column goes through its own softmax and accumulator and only
+  // columns n < gw are ever written, so the copies cost nothing and need
+  // neither a branch nor masking.
   __device__ __forceinline__ void load_q(const Cursor& c) {
-    const int G = p.group;
     const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + min(n, G - 1)) * D +
-                           8 * quad;
+                           ((int64_t)c.b * p.num_q_heads + qh0 + min(n, gw - 1)) * D + 8 * quad;
 #pragma unroll
     for (int i = 0; i < NK; ++i) qop[i] = *reinterpret_cast<const x8*>(qrow + 32 * i);
   }
@@ -511,14 +515,14 @@ struct Stream {
   // End of this wavefront's part of sequence c.b: normalised output if it
   // saw the whole sequence, else a partial in its (sequence, head, unit) slot.
   __device__ void flush(const Cursor& c, bool whole) {
-    const int G = p.group;
+    const int G = p.group;   // partial slot stride
     const float lt = sum_x32(sum_x16(l));
-    if (n >= G) return;
+    if (n >= gw) return;
     // lane holds dims 4*VD*quad + VD*r + i of head n as acc[i][r]
     if (whole) {
       const float inv = DENSE && lt == 0.f ? 0.f : 1.0f / lt;   // dense: all masked -> zeros
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
-                      ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + n) * D + 4 * VD * quad;
+                      ((int64_t)c.b * p.num_q_heads + qh0 + n) * D + 4 * VD * quad;
       if constexpr (VD == 8) {
         uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
@@ -604,6 +608,7 @@ struct StreamF32 {
   const int lane, n, quad;
   const int g;              // (virtual) KV head served by this wavefront
   const int gp;             // the pool's KV head it reads
+  int qh0, gw;              // its query heads: qh0 .. qh0 + gw - 1
   const int64_t unit;
 
   float qop[KQ];
@@ -612,7 +617,11 @@ struct StreamF32 {
 
   __device__ StreamF32(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
       : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), gp(g_ / p_.qsplit),
-        unit(unit_) {}
+        unit(unit_) {
+    const VHead v = vhead_rows(g_, p_.qsplit, p_.kv_group);
+    qh0 = v.first;
+    gw = v.count;
+  }
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
@@ -621,12 +630,11 @@ struct StreamF32 {
     l = 0.f;
   }
 
-  // Columns n >= G repeat head G-1 (see the 16-bit stream).
+  // Columns n >= gw repeat the last head (see the 16-bit stream).
   __device__ __forceinline__ void load_q(const Cursor& c) {
-    const int G = p.group;
     const float4* qrow = reinterpret_cast<const float4*>(
         static_cast<const float*>(p.q) +
-        ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + min(n, G - 1)) * D + 4 * quad);
+        ((int64_t)c.b * p.num_q_heads + qh0 + min(n, gw - 1)) * D + 4 * quad);
 #pragma unroll
     for (int i = 0; i < KQ / 4; ++i) {
       const float4 v = qrow[4 * i];   // dims 16*i + 4*quad .. + 3
@@ -747,14 +755,14 @@ struct StreamF32 {
   }
 
   __device__ void flush(const Cursor& c, bool whole) {
-    const int G = p.group;
+    const int G = p.group;   // partial slot stride
     const float lt = sum_x32(sum_x16(l));
-    if (n >= G) return;
+    if (n >= gw) return;
     // lane holds dim 64*h + 16*quad + 4*r + e of head n as acc[4*h + e][r]
     if (whole) {
       const float inv = 1.0f / lt;
       float* dst = static_cast<float*>(p.out) +
-                   ((int64_t)c.b * p.num_q_heads + (int64_t)g * G + n) * D + 16 * quad;
+                   ((int64_t)c.b * p.num_q_heads + qh0 + n) * D + 16 * quad;
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll

@@ -79,4 +79,29 @@ __device__ __forceinline__ int64_t partial_slot(int b, int g, int64_t u, int kv_
   return ((int64_t)b + u) * kv_heads + g;
 }
 
+// Query heads of virtual KV head g.  The kv_group query heads of a pool KV
+// head are split over qsplit virtual heads, virtual head k taking the
+// floor-bounded range [k*kv_group/qsplit, (k+1)*kv_group/qsplit): sizes
+// differ by at most one and none is empty (qsplit <= kv_group).
+struct VHead {
+  int first;   // first query head (absolute index)
+  int count;   // query heads served
+};
+__device__ __forceinline__ VHead vhead_rows(int g, int qsplit, int kv_group) {
+  const int gp = g / qsplit;
+  const int k = g - gp * qsplit;
+  const int lo = k * kv_group / qsplit;
+  const int hi = (k + 1) * kv_group / qsplit;
+  return VHead{gp * kv_group + lo, hi - lo};
+}
+
+// The inverse: virtual head g of query head h and h's index within it.
+__device__ __forceinline__ void vhead_of(int h, int qsplit, int kv_group, int* g, int* hn) {
+  const int gp = h / kv_group;
+  const int r = h - gp * kv_group;
+  const int k = ((r + 1) * qsplit - 1) / kv_group;   // largest k with k*kv_group/qsplit <= r
+  *g = gp * qsplit + k;
+  *hn = r - k * kv_group / qsplit;
+}
+
 }  // namespace pagedkv

@@ -100,11 +100,13 @@ struct DecodeParams {
   const void* v_new;
   const int32_t* positions;
   // More than kMaxGroup query heads per KV head: each KV head is served as
-  // qsplit virtual KV heads of group = G / qsplit consecutive query heads
-  // (vheads = kv_heads * qsplit).  Work split, q/out rows and partial slots
-  // use the virtual head; pool addressing uses virtual / qsplit.
+  // qsplit virtual KV heads (vheads = kv_heads * qsplit) of at most `group`
+  // consecutive query heads each (vhead_rows in decode_split.h).  Work
+  // split, q/out rows and partial slots use the virtual head; pool
+  // addressing uses virtual / qsplit.  kv_group = num_q_heads / kv_heads.
   int vheads;
   int qsplit;
+  int kv_group;
   // Dense decode (null for the paged forms): K and V as [batch][dense_len]
   // [kv_heads][head_dim], token t of sequence b attended where mask[b][t] != 0.
   const void* k_dense;
@@ -123,7 +125,7 @@ constexpr int kMaxBatchLds = 16384;      // sequences whose prefix fits in LDS
 // most kMaxGroup query heads each (api.cpp).
 struct HeadSplit {
   int qsplit;   // virtual heads per KV head
-  int group;    // query heads per virtual head
+  int group;    // query heads per virtual head, at most (slot stride)
   int vheads;   // kv_heads * qsplit
 };
 HeadSplit head_split(int kv_heads, int group);

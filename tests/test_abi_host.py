@@ -218,19 +218,20 @@ def _align256(n):
     return (n + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("hkv,hq,qsplit", [(2, 8, 1), (2, 32, 1), (1, 32, 2), (2, 34, 17),
-                                           (2, 40, 2), (1, 48, 3), (4, 96, 2), (1, 64, 4),
-                                           (1, 18, 2), (1, 51, 17)])
-def test_wide_groups_workspace(hkv, hq, qsplit):
-    """More than 16 query heads per KV head: the KV head is served as qsplit
-    virtual heads, qsplit the smallest divisor of the group that leaves at most
-    16 query heads each; the workspace holds one partial slot per virtual head
-    and its share of the query heads."""
+@pytest.mark.parametrize("hkv,hq,qsplit,share", [(2, 8, 1, 4), (2, 32, 1, 16), (1, 32, 2, 16),
+                                                 (2, 34, 2, 9), (2, 40, 2, 10), (1, 48, 3, 16),
+                                                 (4, 96, 2, 12), (1, 64, 4, 16), (1, 18, 2, 9),
+                                                 (1, 51, 4, 13), (1, 71, 5, 15)])
+def test_wide_groups_workspace(hkv, hq, qsplit, share):
+    """More than 16 query heads per KV head: the KV head is served as
+    qsplit = ceil(G / 16) virtual heads of at most share = ceil(G / qsplit)
+    query heads; the workspace holds one partial slot per virtual head, each
+    `share` query heads wide."""
     h = _pool(nb=8, layers=1, hkv=hkv, d=64)
-    batch, g = 5, hq // hkv // qsplit
-    assert g <= 16 and (hq // hkv) % qsplit == 0
+    batch = 5
     slots = batch * hkv * qsplit + 8192
-    want = _align256(4 * (batch + 1)) + _align256(4 * slots * g * 2) + _align256(4 * slots * g * 64)
+    want = (_align256(4 * (batch + 1)) + _align256(4 * slots * share * 2) +
+            _align256(4 * slots * share * 64))
     assert L.paged_attention_workspace_bytes(h, batch, hq) == want
     assert L.dense_attention_workspace_bytes(batch, hkv, hq, 64) == want
     L.kv_pool_destroy(h)

@@ -52,7 +52,7 @@ def test_gather_then_dense_matches_oracle(idx, S, dtype):
 @pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 8, 2, 128), ("f16", 14, 2, 64),
                                             ("bf16", 16, 1, 128), ("f16", 4, 4, 128),
                                             ("bf16", 6, 2, 96), ("bf16", 32, 1, 128),
-                                            ("f16", 40, 2, 64)])
+                                            ("f16", 40, 2, 64), ("bf16", 34, 2, 128)])
 @pytest.mark.parametrize("max_len", [1, 31, 33, 200, 1000])
 def test_dense_random_masks(dtype, Hq, Hkv, D, max_len):
     say(f"dense masks {dtype} Hq={Hq} Hkv={Hkv} D={D} max_len={max_len}")
