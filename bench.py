@@ -39,12 +39,12 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "e0ffa4aa5c8adb1f6ad9af7e89e5a1022eb91e121058966fa617192e73f91668",
-        "bytes": 585626678,
+        "kernel_sha256": "83e38e3acb103558b131bdeae0996108c7bef5fcc5b949e8dfa99457772fc7b4",
+        "bytes": 585637475,
     },
     "long_context_bf16": {
-        "kernel_sha256": "e0ffa4aa5c8adb1f6ad9af7e89e5a1022eb91e121058966fa617192e73f91668",
-        "bytes": 2210887156,
+        "kernel_sha256": "83e38e3acb103558b131bdeae0996108c7bef5fcc5b949e8dfa99457772fc7b4",
+        "bytes": 2210939278,
     },
 }
 

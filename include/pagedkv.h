@@ -267,9 +267,9 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * wavefronts the GPU holds at once; a sequence split across wavefronts is
  * merged by a second kernel on the same stream (log-sum-exp weights).
  * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
- * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and for
- * block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4 and
- * any block size.  At most 16384 sequences per call; otherwise
+ * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and 256 and
+ * for block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4
+ * and any block size.  At most 16384 sequences per call; otherwise
  * PAGEDKV_ERR_UNSUPPORTED.  A KV head with more than 16 query heads (MQA,
  * wide GQA groups) is served as q "virtual" heads of G/q query heads each, q
  * the smallest divisor of G = num_q_heads / kv_heads with G/q <= 16; each

@@ -97,7 +97,7 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
   const TS* pool = reinterpret_cast<const TS*>(p.pool.base);
   // g is a virtual KV head; the pool's head is g / qsplit
   const int64_t head_off =
-      (int64_t)p.layer * p.pool.layer_stride + (int64_t)(g / p.qsplit) * p.pool.head_stride;
+      (int64_t)p.layer * p.pool.layer_stride + (int64_t)vhead_pool_head(g, p.qsplit) * p.pool.head_stride;
   const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
 
   // q rows of the group, pre-multiplied by scale*log2(e)

@@ -45,14 +45,15 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   const int h = blockIdx.x - b * p.num_q_heads;
   int g, hn;   // virtual KV head of h and h's column in it
   vhead_of(h, p.qsplit, p.kv_group, &g, &hn);
-  const int gp = g / p.qsplit;   // the pool's KV head
+  const int gp = vhead_pool_head(g, p.qsplit);   // the pool's KV head
   TS* out = static_cast<TS*>(p.out) + ((int64_t)b * p.num_q_heads + h) * D;
 
   // Independent loads first: the sequence's chunk range and, for a fused
   // append, its position and the new K/V row (one 16-byte unit per lane;
   // fused appends come with head_dim * element size <= 256 bytes, so one
   // pass of 64 lanes covers both rows).
-  const bool app = p.positions != nullptr && hn == 0 && g % p.qsplit == 0;
+  const bool app =
+      p.positions != nullptr && hn == 0 && (p.qsplit == 1 || g % p.qsplit == 0);
   const int units = D * (int)sizeof(TS) / 16;   // 16-byte units per row
   const int kv = lane >= units;
   const int u = lane - kv * units;

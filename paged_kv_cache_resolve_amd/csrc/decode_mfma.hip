@@ -1,7 +1,8 @@
 // Paged-attention decode, pass 1, on MFMA tiles (gfx950): one persistent
 // kernel body (decode_mfma_kernel<S>) over three stream types S.
 //   Stream<E, D, 2, ...>  bf16 / fp16 pools (E = Bf16Ops, F16Ops), 32-token
-//                         chunks of two 16x16 tiles; its DENSE form reads
+//                         chunks of two 16x16 tiles (head_dim 256: 16-token
+//                         chunks of one tile); its DENSE form reads
 //                         the padded [batch][max_len][kv_heads][head_dim]
 //                         tensors a batched gather writes, under a mask;
 //   StreamF32<D, ...>     fp32 pools, 16-token chunks (described at the type).
@@ -63,11 +64,21 @@ constexpr int kThreads = 64 * kWaves;
 #define PAGEDKV_TILES_PER_STEP 2
 #endif
 constexpr int kTilesPerStep = PAGEDKV_TILES_PER_STEP;   // 16-token MFMA tiles per chunk
+#ifndef PAGEDKV_TILES_D256
+#define PAGEDKV_TILES_D256 1
+#endif
+// head_dim 256: a 16-token tile already moves as many K/V bytes as a 32-token
+// chunk at head_dim 128, and one tile keeps the K/V registers at that size
+constexpr int kTilesD256 = PAGEDKV_TILES_D256;
 
 template <int D> struct VRow;
 template <> struct VRow<128> { using type = uint4; };   // 8 elements per lane
 template <> struct VRow<96> { using type = uint3; };    // 6 elements per lane
 template <> struct VRow<64> { using type = uint2; };    // 4 elements per lane
+struct u32x8_t {   // 16 elements per lane (head_dim 256): two 16-byte halves
+  uint4 lo, hi;
+};
+template <> struct VRow<256> { using type = u32x8_t; };
 
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
@@ -93,6 +104,10 @@ __device__ __forceinline__ void stream_load(uint3& d, const char* p) {
 __device__ __forceinline__ void stream_load(uint2& d, const char* p) {
   d = __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p)));
 }
+__device__ __forceinline__ void stream_load(u32x8_t& d, const char* p) {
+  stream_load(d.lo, p);
+  stream_load(d.hi, p + 16);
+}
 
 // Block tables are read-only while a decode runs; reading them through the
 // constant address space lets uniform indices become scalar loads.
@@ -106,6 +121,9 @@ __device__ __forceinline__ uint32_t dword_of(const uint3& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : v.z;
 }
 __device__ __forceinline__ uint32_t dword_of(const uint2& v, int i) { return i == 0 ? v.x : v.y; }
+__device__ __forceinline__ uint32_t dword_of(const u32x8_t& v, int i) {
+  return i < 4 ? dword_of(v.lo, i) : dword_of(v.hi, i - 4);
+}
 
 // Element operations of the two 16-bit pool types: the MFMA forms, rounding
 // of two floats to a packed pair (nearest even; lo = a, hi = b) and widening
@@ -184,6 +202,10 @@ template <int D> __device__ __forceinline__ void zero_row(typename VRow<D>::type
 template <> __device__ __forceinline__ void zero_row<128>(uint4& v) { v = make_uint4(0, 0, 0, 0); }
 template <> __device__ __forceinline__ void zero_row<96>(uint3& v) { v = make_uint3(0, 0, 0); }
 template <> __device__ __forceinline__ void zero_row<64>(uint2& v) { v = make_uint2(0, 0); }
+template <> __device__ __forceinline__ void zero_row<256>(u32x8_t& v) {
+  v.lo = make_uint4(0, 0, 0, 0);
+  v.hi = make_uint4(0, 0, 0, 0);
+}
 
 // Position in the chunk space of one KV head: chunk j of sequence b, which
 // has nb chunks and T tokens; pos is b's appended token (fused append only,
@@ -247,8 +269,8 @@ struct Stream {
   float m, l;
 
   __device__ Stream(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
-      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), gp(g_ / p_.qsplit),
-        unit(unit_) {
+      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_),
+        gp(vhead_pool_head(g_, p_.qsplit)), unit(unit_) {
     const VHead v = vhead_rows(g_, p_.qsplit, p_.kv_group);
     qh0 = v.first;
     gw = v.count;
@@ -523,14 +545,17 @@ struct Stream {
       const float inv = DENSE && lt == 0.f ? 0.f : 1.0f / lt;   // dense: all masked -> zeros
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
                       ((int64_t)c.b * p.num_q_heads + qh0 + n) * D + 4 * VD * quad;
-      if constexpr (VD == 8) {
+      if constexpr (VD % 8 == 0) {   // VD / 8 16-byte stores per r
         uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          d4[r] = make_uint4(E::pack2(acc[0][r] * inv, acc[1][r] * inv),
-                             E::pack2(acc[2][r] * inv, acc[3][r] * inv),
-                             E::pack2(acc[4][r] * inv, acc[5][r] * inv),
-                             E::pack2(acc[6][r] * inv, acc[7][r] * inv));
+#pragma unroll
+          for (int h = 0; h < VD / 8; ++h)
+            d4[r * (VD / 8) + h] =
+                make_uint4(E::pack2(acc[8 * h][r] * inv, acc[8 * h + 1][r] * inv),
+                           E::pack2(acc[8 * h + 2][r] * inv, acc[8 * h + 3][r] * inv),
+                           E::pack2(acc[8 * h + 4][r] * inv, acc[8 * h + 5][r] * inv),
+                           E::pack2(acc[8 * h + 6][r] * inv, acc[8 * h + 7][r] * inv));
       } else if constexpr (VD == 6) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {   // 12 bytes per r: three dword stores
@@ -616,8 +641,8 @@ struct StreamF32 {
   float m, l;
 
   __device__ StreamF32(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
-      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_), gp(g_ / p_.qsplit),
-        unit(unit_) {
+      : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_),
+        gp(vhead_pool_head(g_, p_.qsplit)), unit(unit_) {
     const VHead v = vhead_rows(g_, p_.qsplit, p_.kv_group);
     qh0 = v.first;
     gw = v.count;
@@ -882,12 +907,12 @@ size_t mfma_lds_bytes(int batch) { return sizeof(int32_t) * (size_t)(batch + 1);
 bool mfma_supported(const kv_pool* pool, int group) {
   const int d = pool->head_dim, bs = pool->block_size;
   const bool half = pool->dtype != PAGEDKV_F32;
-  const bool dim_ok = d == 64 || d == 128 || (d == 96 && half);
+  const bool dim_ok = d == 64 || d == 128 || ((d == 96 || d == 256) && half);
   const bool bs_ok = bs % 16 == 0 || ((bs == 4 || bs == 8) && half);
   return dim_ok && bs_ok && group >= 1 && group <= kMaxGroup;
 }
 
-int mfma_chunk_tokens() { return 16 * kTilesPerStep; }
+int mfma_chunk_tokens(int head_dim) { return 16 * (head_dim == 256 ? kTilesD256 : kTilesPerStep); }
 
 namespace {
 template <typename S>
@@ -905,8 +930,12 @@ void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
     else launch_one<Stream<E, 64, T, false, true>>(p, wgs, lds, s);
     return;
   }
+  constexpr int T2 = kTilesD256;
   if (p.pool.block_size < 16) {   // 4 or 8 tokens per block
-    if (p.pool.head_dim == 128) {
+    if (p.pool.head_dim == 256) {
+      if (append) launch_one<Stream<E, 256, T2, true, false, true>>(p, wgs, lds, s);
+      else launch_one<Stream<E, 256, T2, false, false, true>>(p, wgs, lds, s);
+    } else if (p.pool.head_dim == 128) {
       if (append) launch_one<Stream<E, 128, T, true, false, true>>(p, wgs, lds, s);
       else launch_one<Stream<E, 128, T, false, false, true>>(p, wgs, lds, s);
     } else if (p.pool.head_dim == 96) {
@@ -918,7 +947,10 @@ void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
     }
     return;
   }
-  if (p.pool.head_dim == 128) {
+  if (p.pool.head_dim == 256) {
+    if (append) launch_one<Stream<E, 256, T2, true>>(p, wgs, lds, s);
+    else launch_one<Stream<E, 256, T2, false>>(p, wgs, lds, s);
+  } else if (p.pool.head_dim == 128) {
     if (append) launch_one<Stream<E, 128, T, true>>(p, wgs, lds, s);
     else launch_one<Stream<E, 128, T, false>>(p, wgs, lds, s);
   } else if (p.pool.head_dim == 96) {
@@ -944,11 +976,14 @@ void launch_f32(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
 
 hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   const size_t lds = mfma_lds_bytes(p.batch);
-  // every instantiation has the same resources: size the grid by one
-  const void* fn = p.pool.head_dim == 128
-      ? reinterpret_cast<const void*>(&decode_mfma_kernel<Stream<Bf16Ops, 128, kTilesPerStep, false>>)
-      : reinterpret_cast<const void*>(&decode_mfma_kernel<Stream<Bf16Ops, 64, kTilesPerStep, false>>);
-  const int chunk = p.dtype == PAGEDKV_F32 ? 16 : 16 * kTilesPerStep;
+  // instantiations of one head_dim have the same resources: size the grid by one
+  const void* fn =
+      p.pool.head_dim == 256
+          ? reinterpret_cast<const void*>(&decode_mfma_kernel<Stream<Bf16Ops, 256, kTilesD256, false>>)
+      : p.pool.head_dim == 128
+          ? reinterpret_cast<const void*>(&decode_mfma_kernel<Stream<Bf16Ops, 128, kTilesPerStep, false>>)
+          : reinterpret_cast<const void*>(&decode_mfma_kernel<Stream<Bf16Ops, 64, kTilesPerStep, false>>);
+  const int chunk = p.dtype == PAGEDKV_F32 ? 16 : mfma_chunk_tokens(p.pool.head_dim);
   int wgs = 0;
   hipError_t e = resident_workgroups(fn, kThreads, lds, &wgs);
   if (e != hipSuccess) return e;

@@ -83,11 +83,17 @@ __device__ __forceinline__ int64_t partial_slot(int b, int g, int64_t u, int kv_
 // head are split over qsplit virtual heads, virtual head k taking the
 // floor-bounded range [k*kv_group/qsplit, (k+1)*kv_group/qsplit): sizes
 // differ by at most one and none is empty (qsplit <= kv_group).
+// Pool KV head of virtual head g.
+__device__ __forceinline__ int vhead_pool_head(int g, int qsplit) {
+  return qsplit == 1 ? g : g / qsplit;
+}
+
 struct VHead {
   int first;   // first query head (absolute index)
   int count;   // query heads served
 };
 __device__ __forceinline__ VHead vhead_rows(int g, int qsplit, int kv_group) {
+  if (qsplit == 1) return VHead{g * kv_group, kv_group};   // the usual case: no divisions
   const int gp = g / qsplit;
   const int k = g - gp * qsplit;
   const int lo = k * kv_group / qsplit;
@@ -97,6 +103,11 @@ __device__ __forceinline__ VHead vhead_rows(int g, int qsplit, int kv_group) {
 
 // The inverse: virtual head g of query head h and h's index within it.
 __device__ __forceinline__ void vhead_of(int h, int qsplit, int kv_group, int* g, int* hn) {
+  if (qsplit == 1) {
+    *g = h / kv_group;
+    *hn = h - *g * kv_group;
+    return;
+  }
   const int gp = h / kv_group;
   const int r = h - gp * kv_group;
   const int k = ((r + 1) * qsplit - 1) / kv_group;   // largest k with k*kv_group/qsplit <= r

@@ -187,6 +187,23 @@ def test_decode_full_size_sampled(idx, nsample):
     assert torch.equal(out.view(torch.int16), again.view(torch.int16)), "decode not deterministic"
 
 
+@pytest.mark.parametrize("Hq,Hkv,D,dtype", [(16, 8, 256, "bf16"), (32, 1, 128, "bf16"),
+                                           (71, 1, 64, "f16")])
+def test_decode_full_size_other_heads(Hq, Hkv, D, dtype):
+    """The Llama-shaped lengths (batch 64, log-normal contexts) with other head
+    shapes at full size: head_dim 256 (Gemma-like), MQA with 32 query heads,
+    and a 71-query-head MQA layer; sampled sequences against the oracle."""
+    say(f"decode full size Hq={Hq} Hkv={Hkv} D={D} {dtype}")
+    w = make_workload(2, Hq=Hq, Hkv=Hkv, D=D, dtype=dtype)
+    dw = DeviceWorkload(w)
+    out = dw.decode()
+    rng = np.random.default_rng(Hq * 1000 + D)
+    seqs = sorted(set(rng.choice(w.S, size=8, replace=False).tolist())
+                  | {int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))})
+    assert_attention_close(out, _oracle_decode(w, seqs=seqs), w.dtype, rows=seqs,
+                           what=f"Hq={Hq} D={D} full")
+
+
 def test_high_concurrency_step_full_size():
     """Workload 4: append the new token into each tail block, decode, then
     gather; decode checked on sampled sequences, gather bit-exact on them."""
@@ -237,7 +254,11 @@ EDGE_CASES = [
     ("f16", 6, 2, 96, 16),      # MFMA fp16, head_dim 96
     ("bf16", 8, 2, 64, 1),      # generic, one token per block
     ("bf16", 8, 2, 128, 128),   # MFMA, 128-token blocks
-    ("bf16", 8, 2, 256, 16),    # generic, head_dim 256
+    ("bf16", 8, 2, 256, 16),    # MFMA bf16, head_dim 256 (one 16-token tile per step)
+    ("f16", 16, 8, 256, 32),    # MFMA fp16, head_dim 256, G = 2
+    ("bf16", 16, 1, 256, 8),    # MFMA bf16, head_dim 256, 8-token blocks, G = 16
+    ("f16", 4, 4, 256, 4),      # MFMA fp16, head_dim 256, 4-token blocks, MHA
+    ("bf16", 40, 2, 256, 16),   # head_dim 256, G = 20: two virtual heads
     ("f32", 4, 1, 256, 32),     # generic fp32, head_dim 256
     ("f32", 16, 1, 64, 64),     # MFMA fp32, G = 16
     # more than 16 query heads per KV head: ceil(G/16) virtual heads of
