@@ -270,11 +270,12 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and 256 and
  * for block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4
  * and any block size.  At most 16384 sequences per call; otherwise
- * PAGEDKV_ERR_UNSUPPORTED.  A KV head with more than 16 query heads (MQA,
- * wide GQA groups) is served as q "virtual" heads of G/q query heads each, q
- * the smallest divisor of G = num_q_heads / kv_heads with G/q <= 16; each
- * virtual head reads the KV head's rows itself, so K/V traffic is q times
- * that of one pass. */
+ * PAGEDKV_ERR_UNSUPPORTED.  Any number of query heads per KV head, G =
+ * num_q_heads / kv_heads: one wavefront serves up to W of them (W = 32 for
+ * bf16/fp16 at head_dim 64 or 128 with block_size a multiple of 16, else
+ * 16), reading K/V once for all; a larger G is served as q = ceil(G/W)
+ * "virtual" KV heads of floor or ceil(G/q) query heads, each of which
+ * requests the KV head's rows itself. */
 int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
                            int layer, const int32_t* block_tables,
                            int max_blocks_per_seq, const int32_t* context_lens,

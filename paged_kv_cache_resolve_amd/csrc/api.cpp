@@ -54,15 +54,25 @@ void decode_workspace_carve(void* ws, int batch, int kv_heads, int group, int he
   *o = reinterpret_cast<float*>(p);
 }
 
-// Query heads per KV head beyond kMaxGroup (MQA, wide GQA groups): the
-// kernels serve each KV head as qsplit = ceil(group / kMaxGroup) "virtual"
+// Query heads per KV head beyond what one wavefront serves (max_group: 32
+// for the two-column-group MFMA stream, else 16; MQA, wide GQA groups): the
+// kernels serve each KV head as qsplit = ceil(group / max_group) "virtual"
 // KV heads of floor or ceil(group / qsplit) consecutive query heads each.
 // Every virtual head streams its KV head's rows itself, so K/V are
 // requested qsplit times.
-HeadSplit head_split(int kv_heads, int group) {
-  const int q = (group + kMaxGroup - 1) / kMaxGroup;
+HeadSplit head_split(int kv_heads, int group, int max_group) {
+  const int q = (group + max_group - 1) / max_group;
   return HeadSplit{q, (group + q - 1) / q, kv_heads * q};
 }
+
+namespace {
+// The split the paged decode uses: as wide as the kernel that will run takes.
+HeadSplit paged_split(const kv_pool* pool, int num_q_heads) {
+  const int group = num_q_heads / pool->kv_heads;
+  const int cap = mfma_supported(pool, 1) ? mfma_max_group(pool) : kMaxGroup;
+  return head_split(pool->kv_heads, group, cap);
+}
+}  // namespace
 
 }  // namespace pagedkv
 
@@ -203,7 +213,7 @@ int paged_kv_gather(void* k_out, void* v_out, uint8_t* mask, const kv_pool_t* po
 
 size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch, int num_q_heads) {
   if (!pool || batch < 0 || num_q_heads < 1 || num_q_heads % pool->kv_heads != 0) return 0;
-  const HeadSplit hs = head_split(pool->kv_heads, num_q_heads / pool->kv_heads);
+  const HeadSplit hs = paged_split(pool, num_q_heads);
   return decode_workspace_bytes(batch, hs.vheads, hs.group, pool->head_dim);
 }
 
@@ -227,7 +237,7 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   if (!aligned16(out) || !aligned16(q) || (append && (!aligned16(k_new) || !aligned16(v_new))))
     return PAGEDKV_ERR_INVALID_ARG;
   if (batch > kMaxBatchLds) return PAGEDKV_ERR_UNSUPPORTED;
-  const HeadSplit hs = head_split(pool->kv_heads, num_q_heads / pool->kv_heads);
+  const HeadSplit hs = paged_split(pool, num_q_heads);
   const bool use_mfma = mfma_supported(pool, hs.group);
   if (!use_mfma && !generic_supported(pool, hs.group)) return PAGEDKV_ERR_UNSUPPORTED;
   const size_t need = decode_workspace_bytes(batch, hs.vheads, hs.group, pool->head_dim);
@@ -306,7 +316,7 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
 size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads, int head_dim) {
   if (batch < 0 || kv_heads < 1 || num_q_heads < 1 || num_q_heads % kv_heads != 0 || head_dim < 1)
     return 0;
-  const HeadSplit hs = head_split(kv_heads, num_q_heads / kv_heads);
+  const HeadSplit hs = head_split(kv_heads, num_q_heads / kv_heads, kMaxGroup);
   return decode_workspace_bytes(batch, hs.vheads, hs.group, head_dim);
 }
 
@@ -321,7 +331,7 @@ int dense_attention_decode(void* out, const void* q, const void* k, const void* 
   if (!out || !q || (max_len > 0 && (!k || !v || !mask))) return PAGEDKV_ERR_INVALID_ARG;
   if (!aligned16(out) || !aligned16(q) || !aligned16(k) || !aligned16(v))
     return PAGEDKV_ERR_INVALID_ARG;
-  const HeadSplit hs = head_split(kv_heads, num_q_heads / kv_heads);
+  const HeadSplit hs = head_split(kv_heads, num_q_heads / kv_heads, kMaxGroup);
   if ((dtype != PAGEDKV_BF16 && dtype != PAGEDKV_F16) ||
       (head_dim != 64 && head_dim != 96 && head_dim != 128) || batch > kMaxBatchLds)
     return PAGEDKV_ERR_UNSUPPORTED;

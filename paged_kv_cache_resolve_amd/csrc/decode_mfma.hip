@@ -244,9 +244,15 @@ struct Cursor {
 // With SMALL, blocks hold 4 or 8 tokens, so a 16-token tile spans several
 // blocks: each lane looks up the block of its own K row and of its four V
 // rows (which never straddle a block), one vector load each per tile.
-template <typename E, int D, int TILES, bool APPEND, bool DENSE = false, bool SMALL = false>
+//
+// With NC = 2, a wavefront serves up to 32 query heads of its KV head as two
+// groups of 16 MFMA columns: each K tile feeds one QK MFMA per group and each
+// V operand one PV MFMA per group, so K/V are read once for all of them.
+template <typename E, int D, int TILES, bool APPEND, bool DENSE = false, bool SMALL = false,
+          int NC = 1>
 struct Stream {
   static constexpr int kTiles = TILES;
+  static constexpr int kCols = NC;            // groups of 16 query-head columns
   static constexpr int kChunk = 16 * TILES;   // tokens per chunk
   static constexpr bool kAppend = APPEND;
   static constexpr bool kDense = DENSE;
@@ -264,9 +270,9 @@ struct Stream {
   int qh0, gw;              // its query heads: qh0 .. qh0 + gw - 1
   const int64_t unit;       // head group (chunk range) of this wavefront
 
-  x8 qop[NK];
-  f32x4_t acc[VD];
-  float m, l;
+  x8 qop[NC][NK];
+  f32x4_t acc[NC][VD];
+  float m[NC], l[NC];
 
   __device__ Stream(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
       : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_),
@@ -278,21 +284,28 @@ struct Stream {
 
   __device__ __forceinline__ void reset() {
 #pragma unroll
-    for (int c = 0; c < VD; ++c) acc[c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    m = -INFINITY;
-    l = 0.f;
+    for (int cg = 0; cg < NC; ++cg) {
+#pragma unroll
+      for (int c = 0; c < VD; ++c) acc[cg][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      m[cg] = -INFINITY;
+      l[cg] = 0.f;
+    }
   }
 
   // q of the sequence's gw query heads of this (virtual) KV head in the
-  // B-operand layout.  MFMA columns n >= gw carry a copy of the last head:
-  // every column goes through its own softmax and accumulator and only
-  // columns n < gw are ever written, so the copies cost nothing and need
-  // neither a branch nor masking.
+  // B-operand layout: column n of group cg is head 16*cg + n.  Columns at or
+  // past gw carry a copy of the last head: every column goes through its own
+  // softmax and accumulator and only columns below gw are ever written, so
+  // the copies cost nothing and need neither a branch nor masking.
   __device__ __forceinline__ void load_q(const Cursor& c) {
-    const uint16_t* qrow = static_cast<const uint16_t*>(p.q) +
-                           ((int64_t)c.b * p.num_q_heads + qh0 + min(n, gw - 1)) * D + 8 * quad;
 #pragma unroll
-    for (int i = 0; i < NK; ++i) qop[i] = *reinterpret_cast<const x8*>(qrow + 32 * i);
+    for (int cg = 0; cg < NC; ++cg) {
+      const uint16_t* qrow =
+          static_cast<const uint16_t*>(p.q) +
+          ((int64_t)c.b * p.num_q_heads + qh0 + min(16 * cg + n, gw - 1)) * D + 8 * quad;
+#pragma unroll
+      for (int i = 0; i < NK; ++i) qop[cg][i] = *reinterpret_cast<const x8*>(qrow + 32 * i);
+    }
   }
 
   // Physical blocks of chunk c's tiles: scalar loads of block-table
@@ -429,22 +442,25 @@ struct Stream {
     }
   }
 
+  // s[cg * TILES + t]: scores of tile t against column group cg.
   __device__ __forceinline__ void qk(const Buf& cb, f32x4_t* s) const {
 #pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      s[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int cg = 0; cg < NC; ++cg)
 #pragma unroll
-      for (int i = 0; i < NK; ++i)
-        s[t] = E::mma32(cb.k[t][i], qop[i], s[t]);
-    }
+      for (int t = 0; t < TILES; ++t) {
+        f32x4_t& st = s[cg * TILES + t];
+        st = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NK; ++i) st = E::mma32(cb.k[t][i], qop[cg][i], st);
+      }
   }
 
-  // Scores -> probabilities in the pool type (already in the B-operand layout of the PV
-  // product), then the weighted V sum; updates m, l, acc.  TAIL masks tokens
-  // at or past T; masked V rows are zeroed, not weighted by zero, so unused
-  // pool slots never reach the sum.
+  // Online softmax of column group cg over one chunk: rescales its m, l and
+  // acc and returns the probabilities rounded to the pool type, packed in
+  // pairs (the B-operand layout of the PV product).
   template <bool TAIL>
-  __device__ __forceinline__ void attend(const f32x4_t* s, Buf& cb, const Cursor& c) {
+  __device__ __forceinline__ void softmax_cols(const f32x4_t* s, const Buf& cb, const Cursor& c,
+                                               int cg, uint32_t (&pw)[TILES][2]) {
     float sv[TILES][4];
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
@@ -465,22 +481,32 @@ struct Stream {
     float mref;
     {
       // branch-free rescale (alpha = 1 when no running max grows)
-      const float mn = fmaxf(m, bmax);
+      const float mn = fmaxf(m[cg], bmax);
       mref = DENSE && mn == -INFINITY ? 0.f : mn;
-      const float alpha = __builtin_amdgcn_exp2f(m - mref);
+      const float alpha = __builtin_amdgcn_exp2f(m[cg] - mref);
 #pragma unroll
-      for (int i = 0; i < VD; ++i) acc[i] *= alpha;
-      l *= alpha;
-      m = mn;
+      for (int i = 0; i < VD; ++i) acc[cg][i] *= alpha;
+      l[cg] *= alpha;
+      m[cg] = mn;
     }
-    uint32_t pw[TILES][2];
     const float mp = mref - E::kPScaleLog2;
 #pragma unroll
     for (int t = 0; t < TILES; ++t) {
       pw[t][0] = E::pack2(__builtin_amdgcn_exp2f(sv[t][0] - mp), __builtin_amdgcn_exp2f(sv[t][1] - mp));
       pw[t][1] = E::pack2(__builtin_amdgcn_exp2f(sv[t][2] - mp), __builtin_amdgcn_exp2f(sv[t][3] - mp));
-      l += (E::lo(pw[t][0]) + E::hi(pw[t][0])) + (E::lo(pw[t][1]) + E::hi(pw[t][1]));
+      l[cg] += (E::lo(pw[t][0]) + E::hi(pw[t][0])) + (E::lo(pw[t][1]) + E::hi(pw[t][1]));
     }
+  }
+
+  // Scores -> probabilities in the pool type (already in the B-operand layout of the PV
+  // product), then the weighted V sum; updates m, l, acc.  TAIL masks tokens
+  // at or past T; masked V rows are zeroed, not weighted by zero, so unused
+  // pool slots never reach the sum.
+  template <bool TAIL>
+  __device__ __forceinline__ void attend(const f32x4_t* s, Buf& cb, const Cursor& c) {
+    uint32_t pw[NC][TILES][2];
+#pragma unroll
+    for (int cg = 0; cg < NC; ++cg) softmax_cols<TAIL>(s + cg * TILES, cb, c, cg, pw[cg]);
     if (TAIL && !DENSE) {   // dense rows past the end repeat a real row; their weight is 0
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
@@ -490,7 +516,6 @@ struct Stream {
     }
     if constexpr (TILES == 1) {
       // k = 4 tokens per lane: the 16x16x16 MFMA
-      const uint2 pop = make_uint2(pw[0][0], pw[0][1]);
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         const uint32_t v0 = dword_of(cb.v[0][0], w), v1 = dword_of(cb.v[0][1], w);
@@ -499,13 +524,21 @@ struct Stream {
                                     __builtin_amdgcn_perm(v3, v2, 0x05040100u));
         const uint2 od = make_uint2(__builtin_amdgcn_perm(v1, v0, 0x07060302u),
                                     __builtin_amdgcn_perm(v3, v2, 0x07060302u));
-        acc[2 * w] = E::mma16(ev, pop, acc[2 * w]);
-        acc[2 * w + 1] = E::mma16(od, pop, acc[2 * w + 1]);
+#pragma unroll
+        for (int cg = 0; cg < NC; ++cg) {
+          const uint2 pop = make_uint2(pw[cg][0][0], pw[cg][0][1]);
+          acc[cg][2 * w] = E::mma16(ev, pop, acc[cg][2 * w]);
+          acc[cg][2 * w + 1] = E::mma16(od, pop, acc[cg][2 * w + 1]);
+        }
       }
     } else {
       // k = 8 tokens per lane (4 of each tile, in the order the lane holds
       // its scores): the 16x16x32 MFMA
-      const x8 pop = __builtin_bit_cast(x8, make_uint4(pw[0][0], pw[0][1], pw[1][0], pw[1][1]));
+      x8 pop[NC];
+#pragma unroll
+      for (int cg = 0; cg < NC; ++cg)
+        pop[cg] = __builtin_bit_cast(
+            x8, make_uint4(pw[cg][0][0], pw[cg][0][1], pw[cg][1][0], pw[cg][1][1]));
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         uint32_t ev[4], od[4];
@@ -518,10 +551,13 @@ struct Stream {
           od[2 * t] = __builtin_amdgcn_perm(v1, v0, 0x07060302u);
           od[2 * t + 1] = __builtin_amdgcn_perm(v3, v2, 0x07060302u);
         }
-        acc[2 * w] = E::mma32(__builtin_bit_cast(x8, make_uint4(ev[0], ev[1], ev[2], ev[3])), pop,
-                              acc[2 * w]);
-        acc[2 * w + 1] = E::mma32(__builtin_bit_cast(x8, make_uint4(od[0], od[1], od[2], od[3])),
-                                  pop, acc[2 * w + 1]);
+        const x8 eva = __builtin_bit_cast(x8, make_uint4(ev[0], ev[1], ev[2], ev[3]));
+        const x8 oda = __builtin_bit_cast(x8, make_uint4(od[0], od[1], od[2], od[3]));
+#pragma unroll
+        for (int cg = 0; cg < NC; ++cg) {
+          acc[cg][2 * w] = E::mma32(eva, pop[cg], acc[cg][2 * w]);
+          acc[cg][2 * w + 1] = E::mma32(oda, pop[cg], acc[cg][2 * w + 1]);
+        }
       }
     }
   }
@@ -537,14 +573,24 @@ struct Stream {
   // End of this wavefront's part of sequence c.b: normalised output if it
   // saw the whole sequence, else a partial in its (sequence, head, unit) slot.
   __device__ void flush(const Cursor& c, bool whole) {
+    float lt[NC];
+#pragma unroll
+    for (int cg = 0; cg < NC; ++cg) lt[cg] = sum_x32(sum_x16(l[cg]));
+#pragma unroll
+    for (int cg = 0; cg < NC; ++cg)
+      if (16 * cg + n < gw) flush_cols(c, whole, cg, lt[cg]);
+  }
+
+  // Column group cg's share of flush: head 16*cg + n of this (virtual) KV head.
+  __device__ __forceinline__ void flush_cols(const Cursor& c, bool whole, int cg, float lt) {
     const int G = p.group;   // partial slot stride
-    const float lt = sum_x32(sum_x16(l));
-    if (n >= gw) return;
-    // lane holds dims 4*VD*quad + VD*r + i of head n as acc[i][r]
+    const int hc = 16 * cg + n;
+    const f32x4_t* a = acc[cg];
+    // lane holds dims 4*VD*quad + VD*r + i of head hc as a[i][r]
     if (whole) {
       const float inv = DENSE && lt == 0.f ? 0.f : 1.0f / lt;   // dense: all masked -> zeros
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
-                      ((int64_t)c.b * p.num_q_heads + qh0 + n) * D + 4 * VD * quad;
+                      ((int64_t)c.b * p.num_q_heads + qh0 + hc) * D + 4 * VD * quad;
       if constexpr (VD % 8 == 0) {   // VD / 8 16-byte stores per r
         uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
@@ -552,47 +598,47 @@ struct Stream {
 #pragma unroll
           for (int h = 0; h < VD / 8; ++h)
             d4[r * (VD / 8) + h] =
-                make_uint4(E::pack2(acc[8 * h][r] * inv, acc[8 * h + 1][r] * inv),
-                           E::pack2(acc[8 * h + 2][r] * inv, acc[8 * h + 3][r] * inv),
-                           E::pack2(acc[8 * h + 4][r] * inv, acc[8 * h + 5][r] * inv),
-                           E::pack2(acc[8 * h + 6][r] * inv, acc[8 * h + 7][r] * inv));
+                make_uint4(E::pack2(a[8 * h][r] * inv, a[8 * h + 1][r] * inv),
+                           E::pack2(a[8 * h + 2][r] * inv, a[8 * h + 3][r] * inv),
+                           E::pack2(a[8 * h + 4][r] * inv, a[8 * h + 5][r] * inv),
+                           E::pack2(a[8 * h + 6][r] * inv, a[8 * h + 7][r] * inv));
       } else if constexpr (VD == 6) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {   // 12 bytes per r: three dword stores
           uint32_t* d1 = reinterpret_cast<uint32_t*>(dst + VD * r);
-          d1[0] = E::pack2(acc[0][r] * inv, acc[1][r] * inv);
-          d1[1] = E::pack2(acc[2][r] * inv, acc[3][r] * inv);
-          d1[2] = E::pack2(acc[4][r] * inv, acc[5][r] * inv);
+          d1[0] = E::pack2(a[0][r] * inv, a[1][r] * inv);
+          d1[1] = E::pack2(a[2][r] * inv, a[3][r] * inv);
+          d1[2] = E::pack2(a[4][r] * inv, a[5][r] * inv);
         }
       } else {
         uint2* d2 = reinterpret_cast<uint2*>(dst);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          d2[r] = make_uint2(E::pack2(acc[0][r] * inv, acc[1][r] * inv),
-                             E::pack2(acc[2][r] * inv, acc[3][r] * inv));
+          d2[r] = make_uint2(E::pack2(a[0][r] * inv, a[1][r] * inv),
+                             E::pack2(a[2][r] * inv, a[3][r] * inv));
       }
     } else {
       const int64_t slot = partial_slot(c.b, g, unit, p.vheads);
-      float* of = p.ws_o + (slot * G + n) * D + 4 * VD * quad;
+      float* of = p.ws_o + (slot * G + hc) * D + 4 * VD * quad;
       if constexpr (VD % 4 == 0) {
         float4* o = reinterpret_cast<float4*>(of);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int h = 0; h < VD / 4; ++h)
-            o[r * (VD / 4) + h] = make_float4(acc[4 * h][r], acc[4 * h + 1][r], acc[4 * h + 2][r],
-                                              acc[4 * h + 3][r]);
+            o[r * (VD / 4) + h] =
+                make_float4(a[4 * h][r], a[4 * h + 1][r], a[4 * h + 2][r], a[4 * h + 3][r]);
       } else {
         float2* o = reinterpret_cast<float2*>(of);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int h = 0; h < VD / 2; ++h)
-            o[r * (VD / 2) + h] = make_float2(acc[2 * h][r], acc[2 * h + 1][r]);
+            o[r * (VD / 2) + h] = make_float2(a[2 * h][r], a[2 * h + 1][r]);
       }
       if (quad == 0) {
-        p.ws_ml[(slot * G + n) * 2 + 0] = m;
-        p.ws_ml[(slot * G + n) * 2 + 1] = lt;
+        p.ws_ml[(slot * G + hc) * 2 + 0] = m[cg];
+        p.ws_ml[(slot * G + hc) * 2 + 1] = lt;
       }
     }
   }
@@ -617,6 +663,7 @@ struct Stream {
 template <int D, bool APPEND>
 struct StreamF32 {
   static constexpr int kTiles = 1;
+  static constexpr int kCols = 1;
   static constexpr int kChunk = 16;
   static constexpr bool kAppend = APPEND;
   static constexpr bool kDense = false;
@@ -865,7 +912,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   }
   bool whole_start = cur.j == 0;   // this wave has seen the current sequence from chunk 0
 
-  f32x4_t s[TILES];
+  f32x4_t s[S::kCols * TILES];
   for (int i = 0; i + 1 < rem; ++i) {
     st.qk(cb, s);
     __builtin_amdgcn_sched_barrier(0);
@@ -904,12 +951,21 @@ size_t mfma_lds_bytes(int batch) { return sizeof(int32_t) * (size_t)(batch + 1);
 
 }  // namespace
 
+// Query heads one wavefront can serve: 32 (two column groups) for 16-bit
+// pools at head_dim 64 or 128 with blocks of a multiple of 16 tokens, else 16.
+int mfma_max_group(const kv_pool* pool) {
+  const int d = pool->head_dim;
+  const bool wide = pool->dtype != PAGEDKV_F32 && (d == 64 || d == 128) &&
+                    pool->block_size % 16 == 0;
+  return wide ? 2 * kMaxGroup : kMaxGroup;
+}
+
 bool mfma_supported(const kv_pool* pool, int group) {
   const int d = pool->head_dim, bs = pool->block_size;
   const bool half = pool->dtype != PAGEDKV_F32;
   const bool dim_ok = d == 64 || d == 128 || ((d == 96 || d == 256) && half);
   const bool bs_ok = bs % 16 == 0 || ((bs == 4 || bs == 8) && half);
-  return dim_ok && bs_ok && group >= 1 && group <= kMaxGroup;
+  return dim_ok && bs_ok && group >= 1 && group <= mfma_max_group(pool);
 }
 
 int mfma_chunk_tokens(int head_dim) { return 16 * (head_dim == 256 ? kTilesD256 : kTilesPerStep); }
@@ -944,6 +1000,16 @@ void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
     } else {
       if (append) launch_one<Stream<E, 64, T, true, false, true>>(p, wgs, lds, s);
       else launch_one<Stream<E, 64, T, false, false, true>>(p, wgs, lds, s);
+    }
+    return;
+  }
+  if (p.group > kMaxGroup) {   // two column groups (head_dim 64 or 128)
+    if (p.pool.head_dim == 128) {
+      if (append) launch_one<Stream<E, 128, T, true, false, false, 2>>(p, wgs, lds, s);
+      else launch_one<Stream<E, 128, T, false, false, false, 2>>(p, wgs, lds, s);
+    } else {
+      if (append) launch_one<Stream<E, 64, T, true, false, false, 2>>(p, wgs, lds, s);
+      else launch_one<Stream<E, 64, T, false, false, false, 2>>(p, wgs, lds, s);
     }
     return;
   }

@@ -122,13 +122,13 @@ constexpr int kGenericChunk = 64;        // tokens per chunk, VALU kernel
 constexpr int kMaxBatchLds = 16384;      // sequences whose prefix fits in LDS
 
 // How the query heads of one KV head are spread over virtual KV heads of at
-// most kMaxGroup query heads each (api.cpp).
+// most max_group query heads each (api.cpp).
 struct HeadSplit {
   int qsplit;   // virtual heads per KV head
   int group;    // query heads per virtual head, at most (slot stride)
   int vheads;   // kv_heads * qsplit
 };
-HeadSplit head_split(int kv_heads, int group);
+HeadSplit head_split(int kv_heads, int group, int max_group);
 
 size_t decode_workspace_bytes(int batch, int kv_heads, int group, int head_dim);
 void decode_workspace_carve(void* ws, int batch, int kv_heads, int group,
@@ -166,6 +166,7 @@ int device_cus();
 // Decode pass 1 variants and pass 2.  The *_supported predicates say which
 // shapes each pass-1 kernel handles.
 bool mfma_supported(const kv_pool* pool, int group);
+int mfma_max_group(const kv_pool* pool);
 bool generic_supported(const kv_pool* pool, int group);
 hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s);
 hipError_t launch_decode_generic(DecodeParams& p, hipStream_t s);

@@ -218,22 +218,41 @@ def _align256(n):
     return (n + 255) // 256 * 256
 
 
-@pytest.mark.parametrize("hkv,hq,qsplit,share", [(2, 8, 1, 4), (2, 32, 1, 16), (1, 32, 2, 16),
-                                                 (2, 34, 2, 9), (2, 40, 2, 10), (1, 48, 3, 16),
-                                                 (4, 96, 2, 12), (1, 64, 4, 16), (1, 18, 2, 9),
-                                                 (1, 51, 4, 13), (1, 71, 5, 15)])
-def test_wide_groups_workspace(hkv, hq, qsplit, share):
-    """More than 16 query heads per KV head: the KV head is served as
-    qsplit = ceil(G / 16) virtual heads of at most share = ceil(G / qsplit)
-    query heads; the workspace holds one partial slot per virtual head, each
-    `share` query heads wide."""
-    h = _pool(nb=8, layers=1, hkv=hkv, d=64)
+def _ws_bytes(batch, vheads, share, d):
+    slots = batch * vheads + 8192
+    return (_align256(4 * (batch + 1)) + _align256(4 * slots * share * 2) +
+            _align256(4 * slots * share * d))
+
+
+@pytest.mark.parametrize("hkv,hq,d,bs,dtype,qsplit,share", [
+    (2, 8, 64, 16, _lib.BF16, 1, 4),
+    (2, 32, 64, 16, _lib.BF16, 1, 16),
+    (1, 32, 64, 16, _lib.BF16, 1, 32),     # MQA-32: one wavefront, two column groups
+    (2, 34, 64, 16, _lib.BF16, 1, 17),
+    (1, 48, 128, 16, _lib.F16, 2, 24),
+    (1, 64, 64, 32, _lib.BF16, 2, 32),
+    (1, 71, 64, 16, _lib.BF16, 3, 24),
+    (1, 51, 128, 16, _lib.BF16, 2, 26),
+    (1, 32, 96, 16, _lib.BF16, 2, 16),     # head_dim 96: 16 query heads per wavefront
+    (1, 32, 64, 16, _lib.F32, 2, 16),      # fp32 stream: 16
+    (1, 32, 64, 8, _lib.BF16, 2, 16),      # 8-token blocks: 16
+    (1, 71, 256, 16, _lib.BF16, 5, 15),
+    (2, 40, 80, 16, _lib.BF16, 2, 10),     # VALU kernel (head_dim 80): 16
+])
+def test_wide_groups_workspace(hkv, hq, d, bs, dtype, qsplit, share):
+    """More query heads per KV head than one wavefront serves: the KV head is
+    served as qsplit = ceil(G / W) virtual heads of at most share =
+    ceil(G / qsplit) query heads, W = 32 for the 16-bit MFMA stream at
+    head_dim 64 or 128 with blocks of a multiple of 16 tokens, else 16.  The
+    workspace holds one partial slot per virtual head, `share` heads wide.
+    The dense decode always splits at 16."""
+    h = _pool(nb=8, bs=bs, layers=1, hkv=hkv, d=d, dtype=dtype)
     batch = 5
-    slots = batch * hkv * qsplit + 8192
-    want = (_align256(4 * (batch + 1)) + _align256(4 * slots * share * 2) +
-            _align256(4 * slots * share * 64))
-    assert L.paged_attention_workspace_bytes(h, batch, hq) == want
-    assert L.dense_attention_workspace_bytes(batch, hkv, hq, 64) == want
+    assert L.paged_attention_workspace_bytes(h, batch, hq) == _ws_bytes(batch, hkv * qsplit, share, d)
+    g = hq // hkv
+    dq = -(-g // 16)
+    assert L.dense_attention_workspace_bytes(batch, hkv, hq, d) == \
+        _ws_bytes(batch, hkv * dq, -(-g // dq), d)
     L.kv_pool_destroy(h)
 
 

@@ -102,7 +102,8 @@ SHAPES = [
     ("f32", 8, 2, 96, 16),
     ("bf16", 16, 8, 256, 16),   # head_dim 256: the merge stores 1 KB rows, 16 bytes a lane
     ("f16", 8, 2, 256, 8),
-    ("bf16", 32, 1, 128, 16),   # G = 32: the new row is stored once per KV head
+    ("bf16", 32, 1, 128, 16),   # G = 32: one wavefront, two column groups
+    ("f16", 33, 1, 64, 16),     # G = 33: two virtual heads; the row is stored once per KV head
     ("f16", 40, 2, 64, 8),      # G = 20
     ("f32", 34, 2, 64, 16),     # G = 17: 8 + 9
     ("bf16", 71, 1, 64, 16),    # G = 71: five virtual heads

@@ -261,14 +261,18 @@ EDGE_CASES = [
     ("bf16", 40, 2, 256, 16),   # head_dim 256, G = 20: two virtual heads
     ("f32", 4, 1, 256, 32),     # generic fp32, head_dim 256
     ("f32", 16, 1, 64, 64),     # MFMA fp32, G = 16
-    # more than 16 query heads per KV head: ceil(G/16) virtual heads of
-    # floor- or ceil(G/q) query heads
-    ("bf16", 32, 1, 128, 16),   # MQA, G = 32: two virtual heads of 16
-    ("bf16", 40, 2, 64, 16),    # G = 20: two of 10
-    ("bf16", 34, 2, 128, 8),    # G = 17: 8 + 9, 8-token blocks
-    ("bf16", 71, 1, 64, 16),    # G = 71: 14 + 14 + 14 + 14 + 15
-    ("f16", 64, 1, 96, 16),     # G = 64: four of 16, head_dim 96
-    ("f16", 51, 1, 128, 32),    # G = 51: 12 + 13 + 13 + 13
+    # more than 16 query heads per KV head: up to 32 in one wavefront (two
+    # MFMA column groups: 16-bit, head_dim 64/128, BS a multiple of 16), else
+    # ceil(G/W) virtual heads of floor- or ceil(G/q) query heads
+    ("bf16", 32, 1, 128, 16),   # MQA, G = 32: one wavefront, 16 + 16 columns
+    ("bf16", 40, 2, 64, 16),    # G = 20: 16 + 4 columns
+    ("bf16", 17, 1, 128, 16),   # G = 17: 16 + 1 columns
+    ("f16", 48, 2, 64, 32),     # G = 24: 16 + 8 columns
+    ("bf16", 33, 1, 128, 16),   # G = 33: virtual heads of 16 (second group empty) and 17
+    ("bf16", 34, 2, 128, 8),    # G = 17 with 8-token blocks: virtual heads of 8 + 9
+    ("bf16", 71, 1, 64, 16),    # G = 71: virtual heads of 23 + 24 + 24
+    ("f16", 64, 1, 96, 16),     # G = 64, head_dim 96: four virtual heads of 16
+    ("f16", 51, 1, 128, 32),    # G = 51: virtual heads of 25 + 26
     ("f32", 48, 2, 64, 16),     # MFMA fp32, G = 24: two of 12
     ("f32", 38, 2, 128, 16),    # MFMA fp32, G = 19: 9 + 10
     ("bf16", 36, 2, 64, 2),     # generic, G = 18: two of 9
