@@ -1,6 +1,7 @@
 // Paged-attention decode, pass 1, general shapes (fp32, bf16 or fp16 pools, any
-// block size, head_dim a multiple of 4 up to 256, up to 16 query heads per KV
-// head), plain VALU arithmetic.
+// block size, head_dim a multiple of 4 up to 256, up to 16 query heads per
+// wavefront; larger groups arrive split into virtual KV heads), plain VALU
+// arithmetic.
 //
 // Same computation as the MFMA kernel ("vllmini", section "The CUDA Block
 // Kernel": per (sequence, head), resolve logical positions through the block

@@ -99,8 +99,9 @@ struct DecodeParams {
   const void* k_new;
   const void* v_new;
   const int32_t* positions;
-  // More than kMaxGroup query heads per KV head: each KV head is served as
-  // qsplit virtual KV heads (vheads = kv_heads * qsplit) of at most `group`
+  // More query heads per KV head than one wavefront serves (16, or 32 for
+  // the two-column-group MFMA stream): each KV head is served as qsplit
+  // virtual KV heads (vheads = kv_heads * qsplit) of at most `group`
   // consecutive query heads each (vhead_rows in decode_split.h).  Work
   // split, q/out rows and partial slots use the virtual head; pool
   // addressing uses virtual / qsplit.  kv_group = num_q_heads / kv_heads.
@@ -116,7 +117,7 @@ struct DecodeParams {
 };
 
 constexpr int kMaxWaves = 8192;          // upper bound on wavefronts (256 CUs x 32)
-constexpr int kMaxGroup = 16;            // query heads per KV head
+constexpr int kMaxGroup = 16;            // query heads per MFMA column group / VALU wavefront
 constexpr int kDecodeWgPerCu = 1;        // decode workgroups (4 wavefronts) per CU
 constexpr int kGenericChunk = 64;        // tokens per chunk, VALU kernel
 constexpr int kMaxBatchLds = 16384;      // sequences whose prefix fits in LDS
