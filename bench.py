@@ -39,12 +39,12 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "83e38e3acb103558b131bdeae0996108c7bef5fcc5b949e8dfa99457772fc7b4",
-        "bytes": 585637475,
+        "kernel_sha256": "f3c520a2fb1be228256ac84c4da7f62b74840c3e4b604e2e3e9b773179e5ca3a",
+        "bytes": 585643402,
     },
     "long_context_bf16": {
-        "kernel_sha256": "83e38e3acb103558b131bdeae0996108c7bef5fcc5b949e8dfa99457772fc7b4",
-        "bytes": 2210939278,
+        "kernel_sha256": "f3c520a2fb1be228256ac84c4da7f62b74840c3e4b604e2e3e9b773179e5ca3a",
+        "bytes": 2210973016,
     },
 }
 
@@ -56,6 +56,9 @@ WORKLOADS = {
     "high_concurrency_bf16": 4,
     "llama8b_decode_f32": 5,
     "llama8b_decode_f16": 6,
+    "gemma_like_d256_bf16": 7,
+    "mqa32_decode_bf16": 8,
+    "mqa32_high_concurrency_bf16": 9,
 }
 
 

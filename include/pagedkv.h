@@ -321,8 +321,8 @@ size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads,
  *   mask   : device, [batch][max_len] uint8; token t of sequence b takes part
  *            iff mask[b][t] != 0.  A sequence with no such token gives zeros.
  * Every one of the max_len rows is read, padding included.  Same arithmetic
- * and tolerances as paged_attention_decode.  bf16 and fp16, head_dim 64, 96
- * or 128, any number of query heads per KV head (split as in
+ * and tolerances as paged_attention_decode.  bf16 and fp16, head_dim 64, 96,
+ * 128 or 256, any number of query heads per KV head (split as in
  * paged_attention_decode); otherwise PAGEDKV_ERR_UNSUPPORTED.
  * workspace as for paged_attention_decode (256-byte aligned). */
 int dense_attention_decode(void* out, const void* q, const void* k, const void* v,

@@ -333,9 +333,11 @@ int dense_attention_decode(void* out, const void* q, const void* k, const void* 
     return PAGEDKV_ERR_INVALID_ARG;
   const HeadSplit hs = head_split(kv_heads, num_q_heads / kv_heads, kMaxGroup);
   if ((dtype != PAGEDKV_BF16 && dtype != PAGEDKV_F16) ||
-      (head_dim != 64 && head_dim != 96 && head_dim != 128) || batch > kMaxBatchLds)
+      (head_dim != 64 && head_dim != 96 && head_dim != 128 && head_dim != 256) ||
+      batch > kMaxBatchLds)
     return PAGEDKV_ERR_UNSUPPORTED;
-  if ((int64_t)batch * ((max_len + 31) / 32) > INT32_MAX) return PAGEDKV_ERR_UNSUPPORTED;
+  // chunk count (16-token chunks at the smallest) must fit the kernel's int32 prefix
+  if ((int64_t)batch * ((max_len + 15) / 16) > INT32_MAX) return PAGEDKV_ERR_UNSUPPORTED;
   const size_t need = decode_workspace_bytes(batch, hs.vheads, hs.group, head_dim);
   if (!workspace || workspace_bytes < need) return PAGEDKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PAGEDKV_ERR_WORKSPACE;

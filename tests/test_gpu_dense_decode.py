@@ -30,7 +30,7 @@ def dense(q, k, v, mask, scale):
 
 
 @pytest.mark.parametrize("idx,S,dtype", [(2, 6, "bf16"), (2, 6, "f16"), (1, None, "bf16"),
-                                         (4, 24, "bf16")])
+                                         (4, 24, "bf16"), (7, 6, "bf16"), (8, 6, "f16")])
 def test_gather_then_dense_matches_oracle(idx, S, dtype):
     say(f"gather then dense, workload {idx} S={S} {dtype}")
     over = {"dtype": dtype}
@@ -52,7 +52,8 @@ def test_gather_then_dense_matches_oracle(idx, S, dtype):
 @pytest.mark.parametrize("dtype,Hq,Hkv,D", [("bf16", 8, 2, 128), ("f16", 14, 2, 64),
                                             ("bf16", 16, 1, 128), ("f16", 4, 4, 128),
                                             ("bf16", 6, 2, 96), ("bf16", 32, 1, 128),
-                                            ("f16", 40, 2, 64), ("bf16", 34, 2, 128)])
+                                            ("f16", 40, 2, 64), ("bf16", 34, 2, 128),
+                                            ("bf16", 16, 8, 256), ("f16", 8, 2, 256)])
 @pytest.mark.parametrize("max_len", [1, 31, 33, 200, 1000])
 def test_dense_random_masks(dtype, Hq, Hkv, D, max_len):
     say(f"dense masks {dtype} Hq={Hq} Hkv={Hkv} D={D} max_len={max_len}")

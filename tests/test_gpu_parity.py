@@ -161,7 +161,7 @@ def test_append_then_decode_churned_pool():
     assert_attention_close(out, _oracle_decode(w), w.dtype, what="w1")
 
 
-@pytest.mark.parametrize("idx,S", [(2, 6), (3, 2), (4, 24)])
+@pytest.mark.parametrize("idx,S", [(2, 6), (3, 2), (4, 24), (7, 6), (8, 8), (9, 24)])
 def test_decode_reduced_batches(idx, S):
     """Named shapes with fewer sequences, every output compared."""
     say(f"decode workload {idx} with S={S}")
@@ -170,7 +170,7 @@ def test_decode_reduced_batches(idx, S):
     assert_attention_close(dw.decode(), _oracle_decode(w), w.dtype, what=f"w{idx} S={S}")
 
 
-@pytest.mark.parametrize("idx,nsample", [(2, 16), (3, 3)])
+@pytest.mark.parametrize("idx,nsample", [(2, 16), (3, 3), (7, 8), (9, 12)])
 def test_decode_full_size_sampled(idx, nsample):
     """Full-size workloads in the configuration the benchmark times; the
     oracle checks a seeded sample of sequences (all heads, all dims)."""

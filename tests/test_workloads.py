@@ -9,7 +9,7 @@ import pytest
 from workloads import bf16_round_bits, make_workload
 
 
-@pytest.mark.parametrize("i", range(7))
+@pytest.mark.parametrize("i", range(10))
 def test_metadata_well_formed(i):
     w = make_workload(i, with_pool=False)
     assert w.block_tables.shape == (w.S, w.MB)

@@ -38,6 +38,9 @@ CONFIG_NAMES = {
     4: "high_concurrency_bf16",
     5: "llama8b_decode_f32",
     6: "llama8b_decode_f16",
+    7: "gemma_like_d256_bf16",
+    8: "mqa32_decode_bf16",
+    9: "mqa32_high_concurrency_bf16",
 }
 
 # Sequences' context lengths count the token appended in this step: the new
@@ -59,6 +62,15 @@ _SPECS = {
     # ... and with an fp16 cache
     6: dict(dtype="f16", S=64, Hq=32, Hkv=8, D=128, BS=16, L=1, layer=0,
             lens=("lognormal", 2048.0, 0.5, 128, 8192), NB="1.1x", tables="perm"),
+    # other head shapes on the same length mixes: head_dim 256 with 16 query /
+    # 8 KV heads (a Gemma-2-9B-shaped layer), and one KV head shared by 32
+    # query heads (multi-query attention) on workload 2's and 4's lengths
+    7: dict(dtype="bf16", S=64, Hq=16, Hkv=8, D=256, BS=16, L=1, layer=0,
+            lens=("lognormal", 2048.0, 0.5, 128, 8192), NB="1.1x", tables="perm"),
+    8: dict(dtype="bf16", S=64, Hq=32, Hkv=1, D=128, BS=16, L=1, layer=0,
+            lens=("lognormal", 2048.0, 0.5, 128, 8192), NB="1.1x", tables="perm"),
+    9: dict(dtype="bf16", S=256, Hq=32, Hkv=1, D=128, BS=16, L=1, layer=0,
+            lens=("bimodal", 0.7, (16, 512), (4096, 16384)), NB="1.1x", tables="perm"),
 }
 
 _CHURN_STEPS = 20000
