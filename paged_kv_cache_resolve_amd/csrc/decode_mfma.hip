@@ -31,9 +31,10 @@
 //        rescaled branch-free; the factor is 1 unless a running max grew);
 //      - the probabilities, rounded to the pool type, already sit in the
 //        B-operand layout of the PV MFMA (k = token); V rows are loaded fully
-//        coalesced (lane = token 4*(lane/16)+r, dims VD*(lane%16)..) and
-//        transposed to the A operand with v_perm_b32.  The accumulator holds
-//        out^T: lane = head lane%16, 4*VD contiguous dims;
+//        coalesced (lane = token 4*(lane/16)+r, dims VD*(lane%16)..; at
+//        head_dim 256 eight dims from each half of the row) and transposed
+//        to the A operand with v_perm_b32.  The accumulator holds out^T:
+//        lane = head lane%16, 4*VD contiguous dims (two runs of 32 at 256);
 //      - the next chunk's K and V (and, at a sequence boundary, the next
 //        sequence's q) are in flight while this chunk is computed; the
 //        block-table entry of the chunk after that is already being fetched
@@ -104,9 +105,12 @@ __device__ __forceinline__ void stream_load(uint3& d, const char* p) {
 __device__ __forceinline__ void stream_load(uint2& d, const char* p) {
   d = __builtin_bit_cast(uint2, __builtin_nontemporal_load(reinterpret_cast<const u32x2_nt*>(p)));
 }
+// head_dim 256: a lane's 16 elements are 8 from each half of the row (the
+// halves start 256 bytes apart), so that 16 lanes read each half as one
+// contiguous 256-byte run
 __device__ __forceinline__ void stream_load(u32x8_t& d, const char* p) {
   stream_load(d.lo, p);
-  stream_load(d.hi, p + 16);
+  stream_load(d.hi, p + 256);
 }
 
 // Block tables are read-only while a decode runs; reading them through the
@@ -262,6 +266,16 @@ struct Stream {
   static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
   static constexpr int VD = D / 16;   // V dims per lane
   static constexpr int NW = VD / 2;   // dwords per lane per V row
+  // Where a lane's VD elements of a V row sit.  Lane n holds elements
+  // kVLane*n + i (i < VD), except at head_dim 256, where it holds 8n + i and
+  // 128 + 8n + (i - 8) (the two halves of the row, each read contiguously
+  // by the 16 lanes).  In the output, accumulator i of the lane with quad q
+  // and row r is dim kQuadDims*q + kRowDims*r + i (+ 120 for i >= 8 at 256).
+  static constexpr bool kSplitRow = D == 256;
+  static constexpr int kVLane = kSplitRow ? 8 : VD;
+  static constexpr int kQuadDims = 4 * kVLane;
+  static constexpr int kRowDims = kVLane;
+  static constexpr int kHalfDims = kSplitRow ? 128 : 8;   // offset of element group i / 8
 
   const DecodeParams& p;
   const int lane, n, quad;
@@ -414,7 +428,7 @@ struct Stream {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int tok = c.j * (16 * TILES) + 16 * t + 4 * quad + r;
-          stream_load(cb.v[t][r], dense_row(p.v_dense, c, tok) + 2 * VD * n);
+          stream_load(cb.v[t][r], dense_row(p.v_dense, c, tok) + 2 * kVLane * n);
           bits |= (uint32_t)mrow[min(tok, c.T - 1)] << (8 * r);
         }
         cb.mk[t] = bits;
@@ -425,17 +439,18 @@ struct Stream {
     for (int t = 0; t < TILES; ++t) {
       const char* vl = SMALL ? nullptr
                              : tile_base(c, ph, t) + 2 * p.pool.kv_stride +
-                                   (uint32_t)(2 * (4 * quad * D + VD * n));
+                                   (uint32_t)(2 * (4 * quad * D + kVLane * n));
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const char* row;
         if constexpr (SMALL)
-          row = row_addr(ph[2 * t + 1], c.j * (16 * TILES) + 16 * t + 4 * quad + r, 1) + 2 * VD * n;
+          row = row_addr(ph[2 * t + 1], c.j * (16 * TILES) + 16 * t + 4 * quad + r, 1) +
+                2 * kVLane * n;
         else
           row = vl + 2 * r * D;
         if constexpr (APPEND) {
           const int tok = c.j * (16 * TILES) + 16 * t + 4 * quad + r;
-          if (tok == c.pos) row = new_row(c, 1) + 2 * VD * n;
+          if (tok == c.pos) row = new_row(c, 1) + 2 * kVLane * n;
         }
         stream_load(cb.v[t][r], row);
       }
@@ -586,18 +601,18 @@ struct Stream {
     const int G = p.group;   // partial slot stride
     const int hc = 16 * cg + n;
     const f32x4_t* a = acc[cg];
-    // lane holds dims 4*VD*quad + VD*r + i of head hc as a[i][r]
+    // lane holds dims kQuadDims*quad + kRowDims*r + (i % 8) + kHalfDims*(i / 8)
+    // of head hc as a[i][r]
     if (whole) {
       const float inv = DENSE && lt == 0.f ? 0.f : 1.0f / lt;   // dense: all masked -> zeros
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
-                      ((int64_t)c.b * p.num_q_heads + qh0 + hc) * D + 4 * VD * quad;
+                      ((int64_t)c.b * p.num_q_heads + qh0 + hc) * D + kQuadDims * quad;
       if constexpr (VD % 8 == 0) {   // VD / 8 16-byte stores per r
-        uint4* d4 = reinterpret_cast<uint4*>(dst);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int h = 0; h < VD / 8; ++h)
-            d4[r * (VD / 8) + h] =
+            *reinterpret_cast<uint4*>(dst + kRowDims * r + kHalfDims * h) =
                 make_uint4(E::pack2(a[8 * h][r] * inv, a[8 * h + 1][r] * inv),
                            E::pack2(a[8 * h + 2][r] * inv, a[8 * h + 3][r] * inv),
                            E::pack2(a[8 * h + 4][r] * inv, a[8 * h + 5][r] * inv),
@@ -619,14 +634,13 @@ struct Stream {
       }
     } else {
       const int64_t slot = partial_slot(c.b, g, unit, p.vheads);
-      float* of = p.ws_o + (slot * G + hc) * D + 4 * VD * quad;
+      float* of = p.ws_o + (slot * G + hc) * D + kQuadDims * quad;
       if constexpr (VD % 4 == 0) {
-        float4* o = reinterpret_cast<float4*>(of);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
           for (int h = 0; h < VD / 4; ++h)
-            o[r * (VD / 4) + h] =
+            *reinterpret_cast<float4*>(of + kRowDims * r + kHalfDims * (h / 2) + 4 * (h % 2)) =
                 make_float4(a[4 * h][r], a[4 * h + 1][r], a[4 * h + 2][r], a[4 * h + 3][r]);
       } else {
         float2* o = reinterpret_cast<float2*>(of);
