@@ -288,6 +288,9 @@ def main(argv=None) -> int:
     ap.add_argument("--no-gather", action="store_true")
     ap.add_argument("--no-appends", action="store_true")
     ap.add_argument("--cpu-budget-tokens", type=int, default=0)
+    ap.add_argument("--split", choices=("auto", "chunks"), default="auto",
+                    help="decode work split: auto (per-pair workgroups for small batches) or "
+                         "chunks (always the persistent chunk split and merge kernel)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args(argv)
@@ -305,6 +308,7 @@ def main(argv=None) -> int:
     sys.path.insert(0, ROOT)
     import paged_kv_cache_resolve_amd as pk
     from workloads import make_workload
+    pk.set_split_mode(pk.SPLIT_AUTO if args.split == "auto" else pk.SPLIT_CHUNKS)
 
     idx = WORKLOADS[args.workload]
     w0 = make_workload(idx)
@@ -425,7 +429,7 @@ def main(argv=None) -> int:
     tokens_per_s = w0.S / (ms_per_step * 1e-3)
 
     result = {
-        "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s at batch x context",
+        "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s at batch\u00d7context",
         "value": round(value, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -444,6 +448,7 @@ def main(argv=None) -> int:
             "sum_context_tokens": int(w0.context_lens.sum()),
             "max_context": int(w0.context_lens.max()),
             "input_replicas": reps,
+            "split": args.split,
             "parallelism": "single GPU",
         },
         "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -266,6 +266,14 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * nearest even.  T_b = 0 gives a zero row.  Work is split evenly over all
  * wavefronts the GPU holds at once; a sequence split across wavefronts is
  * merged by a second kernel on the same stream (log-sum-exp weights).
+ * Small batches on the MFMA kernels instead run one workgroup of 8
+ * wavefronts per (sequence, KV head) pair, which merges its own pieces, so
+ * one kernel does the whole call.  That applies at head_dim 64, 96 or 128
+ * with at most 16 query heads per wavefront, when every pair's workgroup is
+ * resident at once and the longest sequence the block tables allow,
+ * max_blocks_per_seq * block_size tokens, holds at most 256 KiB of K and V
+ * per KV head (1024 tokens at head_dim 64 in bf16 or fp16, 512 at 128, 256
+ * in fp32 at 128); see paged_attention_set_split_mode.
  * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
  * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and 256 and
  * for block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4
@@ -306,6 +314,22 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new,
                                   const int32_t* context_lens, int batch,
                                   int num_q_heads, float scale, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* Work split of paged_attention_decode and paged_attention_decode_append
+ * (process-wide; the results of both splits agree within the decode
+ * tolerances but not bit for bit, since the softmax sums are taken in a
+ * different order).
+ *   PAGEDKV_SPLIT_AUTO   : per-pair workgroups where the shape allows (see
+ *                          paged_attention_decode), else the chunk split.
+ *   PAGEDKV_SPLIT_CHUNKS : always the persistent chunk split and, where a
+ *                          sequence is split, the merge kernel.
+ * Returns the previous mode, or PAGEDKV_ERR_INVALID_ARG for any other value.
+ * The mode is read when a call is enqueued; changing it while another host
+ * thread enqueues a decode is allowed but leaves which split that call uses
+ * unspecified.  For tests and measurements of either split. */
+#define PAGEDKV_SPLIT_AUTO 0
+#define PAGEDKV_SPLIT_CHUNKS 1
+int paged_attention_set_split_mode(int mode);
 
 /* Bytes of device workspace dense_attention_decode needs (0 for invalid
  * arguments). */

@@ -35,9 +35,13 @@ __all__ = [
     "paged_kv_gather", "paged_attention_decode",
     "paged_attention_decode_append", "DecodePlan", "dense_attention_decode",
     "paged_attention_workspace_bytes", "paged_kv_resolve", "validate_decode_inputs",
+    "set_split_mode", "split_mode", "SPLIT_AUTO", "SPLIT_CHUNKS",
     "PagedKVError", "OutOfBlocksError",
     "library",
 ]
+
+SPLIT_AUTO = _lib.SPLIT_AUTO      # per-pair workgroups for small batches, else the chunk split
+SPLIT_CHUNKS = _lib.SPLIT_CHUNKS  # always the persistent chunk split (+ merge kernel)
 
 _DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.float16: _lib.F16}
 
@@ -501,3 +505,28 @@ def paged_kv_resolve(block_tables: torch.Tensor, context_lens: torch.Tensor, blo
     _check(_L.paged_kv_resolve(sp, tp, int(block_tables.shape[1]), lp, batch, block_size, max_len,
                                _stream(device)), "paged_kv_resolve")
     return slots
+
+
+def set_split_mode(mode: int) -> int:
+    """Select the decode work split for the whole process (SPLIT_AUTO or
+    SPLIT_CHUNKS); returns the previous mode."""
+    prev = _L.paged_attention_set_split_mode(int(mode))
+    if prev < 0:
+        _check(prev, "paged_attention_set_split_mode")
+    return prev
+
+
+class split_mode:
+    """Context manager: run the enclosed decodes with the given split mode."""
+
+    def __init__(self, mode: int):
+        self.mode = mode
+        self.prev = None
+
+    def __enter__(self):
+        self.prev = set_split_mode(self.mode)
+        return self
+
+    def __exit__(self, *exc):
+        set_split_mode(self.prev)
+        return False

@@ -21,6 +21,9 @@ F32 = 0
 BF16 = 1
 F16 = 2
 
+SPLIT_AUTO = 0
+SPLIT_CHUNKS = 1
+
 _c_int = ctypes.c_int
 _c_size = ctypes.c_size_t
 _vp = ctypes.c_void_p
@@ -72,6 +75,7 @@ SIGNATURES = {
     "dense_attention_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "dense_attention_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                         _c_int, _c_int, ctypes.c_float, _vp, _c_size, _vp]),
+    "paged_attention_set_split_mode": (_c_int, [_c_int]),
     "paged_kv_resolve": (_c_int, [_vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp]),
     "pagedkv_status_string": (ctypes.c_char_p, [_c_int]),
 }

@@ -4,6 +4,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <new>
 
 #include "internal.h"
@@ -221,6 +222,8 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch, int num
 
 namespace {
 
+std::atomic<int> g_split_mode{PAGEDKV_SPLIT_AUTO};   // paged_attention_set_split_mode
+
 // Shared body of the decode entry points.  With k_new != nullptr the call
 // also appends each sequence's new token (the fused form).
 int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
@@ -264,6 +267,7 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   p.scale_log2 = scale * 1.4426950408889634f;
   p.dtype = pool->dtype;
   p.min_chunks = 0;   // launcher default
+  p.pair_mode = use_mfma && g_split_mode.load(std::memory_order_relaxed) == PAGEDKV_SPLIT_AUTO;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (use_mfma) {
@@ -275,6 +279,7 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
       p.positions = positions;
     }
     e = launch_decode_mfma(p, s);
+    if (e == hipSuccess && p.pair_mode) return PAGEDKV_OK;   // merged in its own workgroups
   } else {
     // the VALU kernel reads the pool only: append first, as its own launch
     if (append) {
@@ -311,6 +316,11 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
   return decode_call(out, q, pool, layer, block_tables, max_blocks_per_seq, context_lens, batch,
                      num_q_heads, scale, workspace, workspace_bytes, stream, k_new, v_new,
                      positions);
+}
+
+int paged_attention_set_split_mode(int mode) {
+  if (mode != PAGEDKV_SPLIT_AUTO && mode != PAGEDKV_SPLIT_CHUNKS) return PAGEDKV_ERR_INVALID_ARG;
+  return g_split_mode.exchange(mode);
 }
 
 size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads, int head_dim) {

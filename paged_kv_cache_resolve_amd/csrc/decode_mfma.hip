@@ -137,6 +137,7 @@ __device__ __forceinline__ uint32_t dword_of(const u32x8_t& v, int i) {
 // has fp32's exponent range and needs none).
 struct Bf16Ops {
   using x8 = bf16x8_t;
+  using elem = __bf16;
   static constexpr float kPScaleLog2 = 0.f;
   static __device__ __forceinline__ f32x4_t mma32(x8 a, x8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -158,6 +159,7 @@ struct Bf16Ops {
 
 struct F16Ops {
   using x8 = f16x8_t;
+  using elem = _Float16;
   static constexpr float kPScaleLog2 = 15.f;   // p <= 2^15 < 65504
   static __device__ __forceinline__ f32x4_t mma32(x8 a, x8 b, f32x4_t c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -262,6 +264,9 @@ struct Stream {
   static constexpr bool kDense = DENSE;
   static constexpr int kPh = SMALL ? 2 * TILES : TILES;   // block entries held per chunk
   using x8 = typename E::x8;
+  using OutElem = typename E::elem;   // element type of q, out and the pool
+  // fits the per-pair kernel's 256 registers per lane without spilling
+  static constexpr bool kPairs = !DENSE && D <= 128 && NC == 1;
   using Buf = ChunkBuf<E, D, TILES>;
   static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
   static constexpr int VD = D / 16;   // V dims per lane
@@ -685,6 +690,8 @@ struct StreamF32 {
   static constexpr int KQ = D / 4;    // K floats per lane per tile
   static constexpr int NH = D / 64;   // float4 V loads per row per lane
   static constexpr int NB = D / 16;   // output blocks (h, e)
+  using OutElem = float;
+  static constexpr bool kPairs = true;
   struct Buf {
     float4 k[KQ / 4];
     float4 v[4][NH];
@@ -873,42 +880,15 @@ struct StreamF32 {
   }
 };
 
-// One persistent kernel for every stream type S (16-bit or fp32 elements).
+// One wavefront's pass over rem >= 1 consecutive chunks of the chunk space
+// for KV head g, starting at cur: the range may cross into later sequences
+// (prefix, lens and poss are read only at such a boundary).  Each sequence
+// it touches is flushed, as a normalised output if the wavefront saw it from
+// chunk 0 to its last chunk, else as a partial in the slot of `unit`.
 template <typename S>
-__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
-  extern __shared__ int32_t prefix[];
-  __shared__ int32_t scan[kThreads];
-  const int H = p.vheads;   // (virtual) KV heads
-
-  constexpr int TILES = S::kTiles;
-  if constexpr (S::kDense) {   // every sequence is dense_len tokens long
-    const int nc = chunks_of(p.dense_len, S::kChunk);
-    for (int i = threadIdx.x; i <= p.batch; i += kThreads) prefix[i] = i * nc;
-    __syncthreads();
-  } else {
-    block_chunk_prefix<kThreads>(p.context_lens, p.batch, S::kChunk, prefix, scan);
-  }
-  if (blockIdx.x == 0)
-    for (int i = threadIdx.x; i <= p.batch; i += kThreads) p.ws_prefix[i] = prefix[i];
-
-  const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWaves + uni(threadIdx.x >> 6);
-  const int64_t unit = wave / H;
-  const int g = (int)(wave - unit * H);
-  const int64_t C = uni(prefix[p.batch]);
-  const int64_t Ue = waves_eff(C, p.units, p.min_chunks);
-  if (unit >= Ue) return;
-  const int64_t c0 = wave_begin(unit, C, Ue);
-  const int rem = (int)(wave_begin(unit + 1, C, Ue) - c0);   // >= 1
-
-  const const_i32_ptr lens = S::kDense ? nullptr : (const_i32_ptr)p.context_lens;
-  const const_i32_ptr poss = S::kAppend ? (const_i32_ptr)p.positions : nullptr;
-  Cursor cur;
-  cur.dense_T = p.dense_len;
-  cur.b = uni(seq_of_chunk(prefix, p.batch, c0));
-  cur.load_seq(prefix, lens, poss);
-  cur.j = uni((int)(c0 - prefix[cur.b]));
-
+__device__ __forceinline__ void stream_chunks(const DecodeParams& p, int lane, int g, int64_t unit,
+                                              const int32_t* prefix, const_i32_ptr lens,
+                                              const_i32_ptr poss, Cursor cur, int rem) {
   S st(p, lane, g, unit);
   st.reset();
   st.load_q(cur);
@@ -926,7 +906,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   }
   bool whole_start = cur.j == 0;   // this wave has seen the current sequence from chunk 0
 
-  f32x4_t s[S::kCols * TILES];
+  f32x4_t s[S::kCols * S::kTiles];
   for (int i = 0; i + 1 < rem; ++i) {
     st.qk(cb, s);
     __builtin_amdgcn_sched_barrier(0);
@@ -961,6 +941,150 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   st.flush(cur, whole_start && cur.j == cur.nb - 1);
 }
 
+// One persistent kernel for every stream type S (16-bit or fp32 elements).
+template <typename S>
+__global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
+  extern __shared__ int32_t prefix[];
+  __shared__ int32_t scan[kThreads];
+  const int H = p.vheads;   // (virtual) KV heads
+
+  if constexpr (S::kDense) {   // every sequence is dense_len tokens long
+    const int nc = chunks_of(p.dense_len, S::kChunk);
+    for (int i = threadIdx.x; i <= p.batch; i += kThreads) prefix[i] = i * nc;
+    __syncthreads();
+  } else {
+    block_chunk_prefix<kThreads>(p.context_lens, p.batch, S::kChunk, prefix, scan);
+  }
+  if (blockIdx.x == 0)
+    for (int i = threadIdx.x; i <= p.batch; i += kThreads) p.ws_prefix[i] = prefix[i];
+
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + uni(threadIdx.x >> 6);
+  const int64_t unit = wave / H;
+  const int g = (int)(wave - unit * H);
+  const int64_t C = uni(prefix[p.batch]);
+  const int64_t Ue = waves_eff(C, p.units, p.min_chunks);
+  if (unit >= Ue) return;
+  const int64_t c0 = wave_begin(unit, C, Ue);
+  const int rem = (int)(wave_begin(unit + 1, C, Ue) - c0);   // >= 1
+
+  const const_i32_ptr lens = S::kDense ? nullptr : (const_i32_ptr)p.context_lens;
+  const const_i32_ptr poss = S::kAppend ? (const_i32_ptr)p.positions : nullptr;
+  Cursor cur;
+  cur.dense_T = p.dense_len;
+  cur.b = uni(seq_of_chunk(prefix, p.batch, c0));
+  cur.load_seq(prefix, lens, poss);
+  cur.j = uni((int)(c0 - prefix[cur.b]));
+  stream_chunks<S>(p, lane, g, unit, prefix, lens, poss, cur, rem);
+}
+
+// Small batches: one workgroup of kPairWaves wavefronts per (sequence b,
+// virtual KV head g) pair, so that the split of a sequence and the merge of
+// its pieces stay inside one workgroup and no merge launch follows.  Of the
+// pair's n chunks, wavefront w < A = min(n, kPairWaves) streams
+// [w*n/A, (w+1)*n/A) and leaves a partial (running max, sum, unnormalised
+// output) in slot (kPairWaves*b + w)*vheads + g of the workspace.  After a
+// barrier the wavefronts combine the A partials of each query head with the
+// same log-sum-exp update as the merge pass and write the output rows.  A
+// pair one wavefront sees whole (n == 1) is written directly; an empty one
+// (T_b = 0) gets zero rows.  With a fused append the workgroup of the pool
+// head's first virtual head also stores the new K/V rows into the pool: this
+// call reads them from k_new / v_new only, so the store may come at any time.
+constexpr int kPairWaves = 8;
+// K/V bytes per wavefront up to which the per-pair kernel is used.  Measured
+// (batches of 4 to 64 sequences, head_dim 64 and 128, bf16 and fp32): one
+// workgroup per pair is 15-25% faster than the chunk split and merge kernel
+// up to ~32 KB per wavefront, even at ~48 KB, and slower beyond, where the
+// wavefronts' serial chunks outweigh the saved merge launch.
+constexpr int64_t kPairBytesPerWave = 32 << 10;
+
+template <typename S>
+__global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodeParams p) {
+  using Out = typename S::OutElem;
+  const int H = p.vheads;
+  const int b = blockIdx.x / H;
+  const int g = blockIdx.x - b * H;
+  const int lane = threadIdx.x & 63;
+  const int w = uni(threadIdx.x >> 6);
+  const const_i32_ptr lens = (const_i32_ptr)p.context_lens;
+  const const_i32_ptr poss = S::kAppend ? (const_i32_ptr)p.positions : nullptr;
+  Cursor cur;
+  cur.dense_T = 0;
+  cur.b = b;
+  cur.T = uni(lens[b]);
+  cur.pos = poss ? uni(poss[b]) : -1;
+  cur.nb = chunks_of(cur.T, S::kChunk);
+  const int n = cur.nb;
+  const int A = min(n, kPairWaves);   // wavefronts with chunks (uniform over the workgroup)
+  if (w < A) {
+    cur.j = w * n / A;
+    // unit 7b + w makes partial_slot() give slot (8b + w) * vheads + g
+    stream_chunks<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, nullptr, lens, poss, cur,
+                     (w + 1) * n / A - cur.j);
+  }
+
+  const VHead vh = vhead_rows(g, p.qsplit, p.kv_group);
+  const int D = p.pool.head_dim;
+  Out* out = static_cast<Out*>(p.out) + ((int64_t)b * p.num_q_heads + vh.first) * D;
+  if (A == 0) {
+    for (int hn = w; hn < vh.count; hn += kPairWaves)
+      for (int d = lane; d < D; d += 64) out[(int64_t)hn * D + d] = (Out)0.f;
+  } else if (A > 1) {
+    __syncthreads();   // the A partials are written (workgroup-scope release and acquire)
+    const int G = p.group;   // partial slot stride
+    for (int hn = w; hn < vh.count; hn += kPairWaves) {
+      float mv[kPairWaves], lv[kPairWaves], ov[kPairWaves][4];
+#pragma unroll
+      for (int u = 0; u < kPairWaves; ++u) {
+        const int k = min(u, A - 1);   // copies past A are not folded
+        const int64_t e = (((int64_t)kPairWaves * b + k) * H + g) * G + hn;
+        mv[u] = p.ws_ml[2 * e];
+        lv[u] = p.ws_ml[2 * e + 1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int d = lane + 64 * i;
+          ov[u][i] = d < D ? p.ws_o[e * D + d] : 0.f;
+        }
+      }
+      float M = -INFINITY, L = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kPairWaves; ++u) {
+        if (u >= A) break;
+        const float Mn = fmaxf(M, mv[u]);
+        const float sc = __builtin_amdgcn_exp2f(M - Mn);
+        const float wt = __builtin_amdgcn_exp2f(mv[u] - Mn);
+        L = L * sc + wt * lv[u];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a[i] = a[i] * sc + wt * ov[u][i];
+        M = Mn;
+      }
+      const float inv = 1.0f / L;   // every piece holds at least one token
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = lane + 64 * i;
+        if (d < D) out[(int64_t)hn * D + d] = (Out)(a[i] * inv);
+      }
+    }
+  }
+
+  if constexpr (S::kAppend) {
+    const int units = D * (int)sizeof(Out) / 16;   // 16-byte units per row
+    if (w == kPairWaves - 1 && cur.pos >= 0 && (p.qsplit == 1 || g % p.qsplit == 0) &&
+        lane < 2 * units) {
+      const int kv = lane >= units;
+      const int u = lane - kv * units;
+      const int gp = vhead_pool_head(g, p.qsplit);
+      const uint4 v = reinterpret_cast<const uint4*>(
+          static_cast<const Out*>(kv ? p.v_new : p.k_new) + ((int64_t)b * p.pool.kv_heads + gp) * D)[u];
+      const int phys = p.block_tables[(int64_t)b * p.max_blocks_per_seq + cur.pos / p.pool.block_size];
+      const int64_t row = (int64_t)phys * p.pool.block_stride + (int64_t)p.layer * p.pool.layer_stride +
+                          (int64_t)gp * p.pool.head_stride +
+                          (int64_t)(cur.pos % p.pool.block_size) * D + kv * p.pool.kv_stride;
+      reinterpret_cast<uint4*>(reinterpret_cast<Out*>(const_cast<char*>(p.pool.base)) + row)[u] = v;
+    }
+  }
+}
+
 size_t mfma_lds_bytes(int batch) { return sizeof(int32_t) * (size_t)(batch + 1); }
 
 }  // namespace
@@ -985,13 +1109,30 @@ bool mfma_supported(const kv_pool* pool, int group) {
 int mfma_chunk_tokens(int head_dim) { return 16 * (head_dim == 256 ? kTilesD256 : kTilesPerStep); }
 
 namespace {
+// Pass 1 for stream type S: the per-pair kernel when p.pair_mode asks for
+// it and every pair's workgroup is resident at once (else p.pair_mode is
+// cleared), otherwise the persistent kernel on wgs workgroups.
 template <typename S>
-void launch_one(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
+void launch_one(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
+  if constexpr (S::kPairs) {
+    if (p.pair_mode) {
+      const int64_t pairs = (int64_t)p.batch * p.vheads;
+      int resident = 0;
+      if (resident_workgroups(reinterpret_cast<const void*>(&decode_pair_kernel<S>),
+                              64 * kPairWaves, 0, &resident) == hipSuccess &&
+          pairs <= resident) {
+        hipLaunchKernelGGL((decode_pair_kernel<S>), dim3((unsigned)pairs), dim3(64 * kPairWaves), 0,
+                           s, p);
+        return;
+      }
+    }
+  }
+  p.pair_mode = 0;
   hipLaunchKernelGGL((decode_mfma_kernel<S>), dim3(wgs), dim3(kThreads), lds, s, p);
 }
 
 template <typename E>
-void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
+void launch_typed(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
   const bool append = p.positions != nullptr;
   constexpr int T = kTilesPerStep;
   constexpr int T2 = kTilesD256;
@@ -1043,7 +1184,7 @@ void launch_typed(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
   }
 }
 
-void launch_f32(const DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
+void launch_f32(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
   const bool append = p.positions != nullptr;
   if (p.pool.head_dim == 128) {
     if (append) launch_one<StreamF32<128, true>>(p, wgs, lds, s);
@@ -1088,6 +1229,16 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   if (useful < p.units) {
     p.units = (int)(useful < 1 ? 1 : useful);
     wgs = (p.units * p.vheads + kWaves - 1) / kWaves;
+  }
+  // Per-pair workgroups: only while every pair's pieces fit in the
+  // workspace slots and the longest sequence the block tables allow holds
+  // at most kPairBytesPerWave of K and V per wavefront.
+  if (p.pair_mode) {
+    const int64_t pairs = (int64_t)p.batch * p.vheads;
+    const int64_t pair_bytes = 2 * (int64_t)p.max_blocks_per_seq * p.pool.block_size *
+                               p.pool.head_dim * (p.dtype == PAGEDKV_F32 ? 4 : 2);
+    if ((kPairWaves - 1) * pairs > kMaxWaves || pair_bytes > kPairWaves * kPairBytesPerWave)
+      p.pair_mode = 0;
   }
   if (p.dtype == PAGEDKV_F32)
     launch_f32(p, wgs, lds, s);

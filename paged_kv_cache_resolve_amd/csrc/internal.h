@@ -114,6 +114,10 @@ struct DecodeParams {
   const void* v_dense;
   const uint8_t* mask;
   int dense_len;
+  // In: non-zero lets small batches run as one workgroup per (sequence,
+  // virtual KV head) pair, which merges its own pieces.  Out (set by the
+  // pass-1 launcher): non-zero if that kernel ran, so no merge pass follows.
+  int pair_mode;
 };
 
 constexpr int kMaxWaves = 8192;          // upper bound on wavefronts (256 CUs x 32)

@@ -28,3 +28,13 @@ def read_golden(name):
 @pytest.fixture
 def golden():
     return read_golden
+
+
+@pytest.fixture(params=["auto", "chunks"])
+def split(request):
+    """Run the test under both decode work splits: the default (per-pair
+    workgroups where the shape allows) and the persistent chunk split."""
+    import paged_kv_cache_resolve_amd as pk
+    mode = pk.SPLIT_AUTO if request.param == "auto" else pk.SPLIT_CHUNKS
+    with pk.split_mode(mode):
+        yield request.param

@@ -31,10 +31,24 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(L, n), f"{n} missing from libpagedkv.so"
     assert set(names) == set(_lib.SIGNATURES), "binding signatures drift from the header"
+
+
+def test_split_mode_setter():
+    """paged_attention_set_split_mode returns the previous mode and rejects
+    anything but the two declared modes (host only, nothing enqueued)."""
+    prev = L.paged_attention_set_split_mode(_lib.SPLIT_CHUNKS)
+    assert prev in (_lib.SPLIT_AUTO, _lib.SPLIT_CHUNKS)
+    try:
+        assert L.paged_attention_set_split_mode(_lib.SPLIT_AUTO) == _lib.SPLIT_CHUNKS
+        for bad in (-1, 2, 7):
+            assert L.paged_attention_set_split_mode(bad) == _lib.ERR_INVALID_ARG
+        assert L.paged_attention_set_split_mode(_lib.SPLIT_AUTO) == _lib.SPLIT_AUTO
+    finally:
+        L.paged_attention_set_split_mode(prev)
 
 
 def _pool(nb=10, bs=16, layers=2, hkv=2, d=64, dtype=_lib.BF16):

@@ -72,7 +72,7 @@ def custom(dtype, S, Hq, Hkv, D, BS, lens, positions, L=1, layer=0):
 
 
 @pytest.mark.parametrize("idx,S", [(0, None), (1, None), (2, 6), (3, 2), (4, 24)])
-def test_fused_step_named_workloads(idx, S):
+def test_fused_step_named_workloads(idx, S, split):
     say(f"fused append+decode workload {idx} S={S}")
     w = make_workload(idx, **({"S": S} if S else {}))
     positions = w.positions.copy()
@@ -112,7 +112,7 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,BS", SHAPES)
-def test_fused_position_cases(dtype, Hq, Hkv, D, BS):
+def test_fused_position_cases(dtype, Hq, Hkv, D, BS, split):
     """Last token, mid-context overwrite, first token, no token, and a
     position past T_b (written, not attended), against the oracle and
     bit-identical to the two-call form."""

@@ -41,7 +41,7 @@ def rows_of(w, b):
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,BS", [("bf16", 32, 8, 128, 16), ("f16", 14, 2, 64, 32),
                                                ("f32", 8, 2, 128, 16), ("bf16", 6, 2, 96, 16)])
-def test_output_in_convex_hull_of_v(dtype, Hq, Hkv, D, BS):
+def test_output_in_convex_hull_of_v(dtype, Hq, Hkv, D, BS, split):
     say(f"convex hull {dtype} D={D}")
     w = custom(dtype, 6, Hq, Hkv, D, BS, [1, 17, 300, 2000, 33, 64])
     out = dev_to_f64(DeviceWorkload(w).decode())
@@ -63,7 +63,7 @@ def _shift_rows(w, kv, shift):
 
 
 @pytest.mark.parametrize("D,BS", [(128, 16), (64, 32), (96, 16)])
-def test_k_shift_invariance_and_v_shift_equivariance(D, BS):
+def test_k_shift_invariance_and_v_shift_equivariance(D, BS, split):
     """fp32 pools, so that the shifted values are exact inputs."""
     say(f"K/V shift D={D} BS={BS}")
     lens = [5, 100, 1500, 37, 16]
@@ -84,7 +84,7 @@ def test_k_shift_invariance_and_v_shift_equivariance(D, BS):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_identical_sequences_identical_outputs(dtype):
+def test_identical_sequences_identical_outputs(dtype, split):
     """Sequence 4 gets sequence 1's K/V rows (in its own blocks) and its q."""
     say(f"identical sequences {dtype}")
     lens = [40, 3000, 7, 900, 3000, 1]

@@ -1,0 +1,166 @@
+"""The per-pair decode split (one workgroup of 8 wavefronts per (sequence,
+KV head) pair, which merges its own pieces) against the oracle, next to the
+persistent chunk split on the same inputs.
+
+Which split ran is read off the workspace: the chunk split's pass 1 writes
+the per-sequence chunk prefix at the start of the workspace, the per-pair
+kernel never touches it.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_resolve_amd as pk
+from workloads import make_workload
+
+from gpu_helpers import NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, say
+
+pytestmark = [
+    pytest.mark.gpu,
+    pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU"),
+]
+
+SENTINEL = 0xA5
+
+
+def workload(dtype, Hq, Hkv, D, BS, lens, L=1, layer=0):
+    lens = np.asarray(lens, dtype=np.int32)
+    mb = max(1, max(math.ceil(int(t) / BS) for t in lens))
+    nb = sum(math.ceil(int(t) / BS) for t in lens) + 3
+    w = make_workload(0, dtype=dtype, S=len(lens), Hq=Hq, Hkv=Hkv, D=D, BS=BS, L=L, layer=layer,
+                      context_lens=lens, MB=mb, NB=nb, tables="perm")
+    # NaN in every slot no sequence owns: the per-pair kernel must mask as the
+    # chunk split does
+    slots = oracle.resolve_slots(w.block_tables, w.context_lens, w.BS, max(w.max_len, 1))
+    used = np.zeros(w.NB * w.BS, dtype=bool)
+    used[slots[slots >= 0]] = True
+    blk, off = np.nonzero(~used.reshape(w.NB, w.BS))
+    w.pool[blk, :, :, :, off, :] = NAN_BITS[w.dtype]
+    return w
+
+
+def decode_with(dw, mode):
+    """Decode under `mode` with a sentinel-filled workspace; returns the
+    output and whether the chunk prefix was written (chunk split ran)."""
+    batch, hq = dw.q.shape[0], dw.q.shape[1]
+    n = pk.paged_attention_workspace_bytes(dw.pool, batch, hq)
+    ws = torch.full((n,), SENTINEL, dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(dw.q)
+    with pk.split_mode(mode):
+        pk.paged_attention_decode(out, dw.q, dw.pool, dw.w.layer, dw.tables, dw.lens, dw.w.scale,
+                                  workspace=ws)
+    torch.cuda.synchronize()
+    prefix_written = bool((ws[: 4 * (batch + 1)] != SENTINEL).any().item())
+    return out, prefix_written
+
+
+def reference(w):
+    return oracle.paged_attention_decode(w.pool, w.dtype, w.layer, w.block_tables,
+                                         w.context_lens, w.q, w.scale)
+
+
+PAIR_KV_BYTES = 256 << 10   # per (sequence, KV head): 8 wavefronts x 32 KiB
+
+
+def longest_pair_tokens(dtype, D, BS):
+    """The longest table span (a whole number of blocks) the per-pair kernel takes."""
+    e = 4 if dtype == "f32" else 2
+    return PAIR_KV_BYTES // (2 * D * e) // BS * BS
+
+
+def pair_lens(dtype, D, BS):
+    """Lengths giving 0 chunks, 1 chunk (one wavefront sees the pair whole),
+    2..7 chunks (fewer pieces than wavefronts), 8 and more (uneven pieces)
+    and the longest pair the per-pair kernel takes."""
+    c = 16 if dtype == "f32" else 32   # tokens per chunk at head_dim <= 128
+    top = longest_pair_tokens(dtype, D, BS)
+    lens = [0, 1, c - 1, c, c + 1, 3 * c + 5, 7 * c, 8 * c, 8 * c + 1, top - 1, top]
+    assert top >= 8 * c + 1
+    return lens
+
+
+CASES = [
+    ("bf16", 32, 8, 128, 16),
+    ("bf16", 14, 2, 64, 16),
+    ("bf16", 16, 1, 128, 32),
+    ("f16", 8, 2, 128, 16),
+    ("f16", 12, 4, 96, 16),
+    ("bf16", 8, 2, 64, 8),     # 8-token blocks
+    ("f16", 8, 2, 128, 4),     # 4-token blocks
+    ("bf16", 24, 1, 64, 8),    # 24 query heads on one KV head: two virtual heads of 12
+    ("f32", 4, 4, 64, 16),
+    ("f32", 32, 8, 128, 16),
+    ("f32", 24, 1, 64, 16),    # two virtual heads of 12
+]
+
+
+@pytest.mark.parametrize("dtype,Hq,Hkv,D,BS", CASES)
+def test_pair_split_matches_oracle_and_chunk_split(dtype, Hq, Hkv, D, BS):
+    say(f"pair split {dtype} Hq={Hq} Hkv={Hkv} D={D} BS={BS}")
+    lens = pair_lens(dtype, D, BS)
+    w = workload(dtype, Hq, Hkv, D, BS, lens, L=2, layer=1)
+    dw = DeviceWorkload(w)
+    ref = reference(w)
+    out_p, wrote_p = decode_with(dw, pk.SPLIT_AUTO)
+    out_c, wrote_c = decode_with(dw, pk.SPLIT_CHUNKS)
+    assert not wrote_p, "small batch did not take the per-pair split"
+    assert wrote_c, "SPLIT_CHUNKS did not take the chunk split"
+    assert_attention_close(out_p, ref, dtype, what="per-pair split")
+    assert_attention_close(out_c, ref, dtype, what="chunk split")
+    zero_rows = [i for i, t in enumerate(lens) if t == 0]
+    assert not dev_to_np(out_p)[zero_rows].any(), "empty sequences must give zero rows"
+    # deterministic: the same call twice gives the same bits
+    out_p2, _ = decode_with(dw, pk.SPLIT_AUTO)
+    assert torch.equal(out_p.view(torch.int16) if out_p.element_size() == 2 else out_p,
+                       out_p2.view(torch.int16) if out_p2.element_size() == 2 else out_p2)
+
+
+@pytest.mark.parametrize("dtype,D,extra,expect_pairs", [
+    ("bf16", 64, 0, True),     # 1024 tokens: the limit
+    ("bf16", 64, 16, False),   # one block more
+    ("bf16", 128, 0, True),    # 512 tokens
+    ("bf16", 128, 16, False),
+    ("f32", 64, 0, True),      # 512 tokens
+    ("f32", 64, 16, False),
+])
+def test_pair_split_length_limit(dtype, D, extra, expect_pairs):
+    """The choice follows max_blocks_per_seq * block_size, and both sides of
+    the limit match the oracle."""
+    longest = longest_pair_tokens(dtype, D, 16) + extra
+    say(f"pair split limit {dtype} D={D} longest={longest}")
+    w = workload(dtype, 8, 2, D, 16, [longest, 5, 300])
+    dw = DeviceWorkload(w)
+    out, wrote = decode_with(dw, pk.SPLIT_AUTO)
+    assert wrote != expect_pairs
+    assert_attention_close(out, reference(w), dtype, what=f"limit {longest}")
+
+
+def test_pair_split_not_taken_for_many_pairs():
+    """4096 (sequence, KV head) pairs: more workgroups than the GPU holds at
+    once, so the chunk split runs."""
+    say("pair split not taken: 512 sequences x 8 KV heads")
+    rng = np.random.default_rng(5)
+    lens = rng.integers(1, 200, size=512)
+    w = workload("bf16", 32, 8, 128, 16, lens)
+    dw = DeviceWorkload(w)
+    out, wrote = decode_with(dw, pk.SPLIT_AUTO)
+    assert wrote
+    assert_attention_close(out, reference(w), "bf16", what="many pairs")
+
+
+def test_pair_split_named_small_workloads():
+    """By default the tiny fp32 batch takes the per-pair split; the
+    churned-pool batch, whose tables span 2048 tokens, keeps the chunk split."""
+    for idx, expect_pairs in ((0, True), (1, False)):
+        say(f"pair split named workload {idx}")
+        w = make_workload(idx)
+        dw = DeviceWorkload(w)
+        out, wrote = decode_with(dw, pk.SPLIT_AUTO)
+        assert wrote != expect_pairs, f"workload {idx}: unexpected split"
+        assert_attention_close(out, reference(w), w.dtype, what=f"workload {idx}")

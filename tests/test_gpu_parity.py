@@ -143,14 +143,14 @@ def _oracle_decode(w, seqs=None):
                                          w.q, w.scale, seqs=seqs)
 
 
-def test_decode_tiny_fp32():
+def test_decode_tiny_fp32(split):
     say("decode workload 0 (fp32)")
     w = poison(make_workload(0))
     dw = DeviceWorkload(w)
     assert_attention_close(dw.decode(), _oracle_decode(w), w.dtype, what="w0")
 
 
-def test_append_then_decode_churned_pool():
+def test_append_then_decode_churned_pool(split):
     """Workload 1: append the new token, then decode layer 11 over it."""
     say("append+decode workload 1")
     w = make_workload(1)
@@ -162,7 +162,7 @@ def test_append_then_decode_churned_pool():
 
 
 @pytest.mark.parametrize("idx,S", [(2, 6), (3, 2), (4, 24), (7, 6), (8, 8), (9, 24)])
-def test_decode_reduced_batches(idx, S):
+def test_decode_reduced_batches(idx, S, split):
     """Named shapes with fewer sequences, every output compared."""
     say(f"decode workload {idx} with S={S}")
     w = poison(make_workload(idx, S=S))
@@ -281,7 +281,7 @@ EDGE_CASES = [
 
 
 @pytest.mark.parametrize("dtype,Hq,Hkv,D,BS", EDGE_CASES)
-def test_decode_edge_lengths_with_poison(dtype, Hq, Hkv, D, BS):
+def test_decode_edge_lengths_with_poison(dtype, Hq, Hkv, D, BS, split):
     say(f"decode edges {dtype} Hq={Hq} Hkv={Hkv} D={D} BS={BS}")
     lens = [0, 1, BS - 1, BS, BS + 1, 15, 16, 17, 63, 64, 65, 1000, 4 * BS + 3, 0]
     w = poison(custom(dtype, len(lens), Hq, Hkv, D, BS, lens, L=2, layer=1))
@@ -295,7 +295,7 @@ def test_decode_edge_lengths_with_poison(dtype, Hq, Hkv, D, BS):
 
 @pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("f32", 64, 16), ("f16", 128, 16),
                                         ("bf16", 128, 8)])
-def test_decode_block_permutation_invariance(dtype, D, BS):
+def test_decode_block_permutation_invariance(dtype, D, BS, split):
     say(f"decode permutation invariance {dtype}")
     w = custom(dtype, 9, 8, 2, D, BS, [300, 1, 17, 0, 900, 64, 33, 2048, 5], nb_slack=40)
     dw = DeviceWorkload(w)
@@ -309,7 +309,7 @@ def test_decode_block_permutation_invariance(dtype, D, BS):
     assert dev_to_np(a).tobytes() == dev_to_np(b).tobytes()
 
 
-def test_decode_scale_zero_is_mean_of_v():
+def test_decode_scale_zero_is_mean_of_v(split):
     say("decode scale 0")
     w = custom("bf16", 3, 8, 2, 128, 16, [37, 300, 1])
     w.scale = 0.0
@@ -319,7 +319,7 @@ def test_decode_scale_zero_is_mean_of_v():
     assert_attention_close(out, ref, "bf16", what="scale0")
 
 
-def test_decode_many_short_sequences():
+def test_decode_many_short_sequences(split):
     say("decode 5000 short sequences")
     rng = np.random.default_rng(8)
     lens = rng.integers(0, 41, size=5000)
@@ -390,7 +390,7 @@ def _rne_16(x32: np.ndarray, dtype: str) -> np.ndarray:
 
 @pytest.mark.parametrize("dtype,D,BS", [("bf16", 128, 16), ("bf16", 64, 8), ("f16", 128, 16),
                                         ("f16", 64, 8)])
-def test_output_rounding_is_nearest_even(dtype, D, BS):
+def test_output_rounding_is_nearest_even(dtype, D, BS, split):
     """Two cached tokens with identical K rows get weights of exactly 1/2,
     so the fp32 result is the midpoint of their V values.  V pairs are
     neighbouring representable values, so every midpoint lies exactly
