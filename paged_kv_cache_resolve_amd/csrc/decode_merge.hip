@@ -16,6 +16,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "decode_split.h"
 #include "internal.h"
 
@@ -32,9 +34,9 @@ template <> __device__ __forceinline__ uint16_t out_cast<uint16_t>(float x) {   
 template <> __device__ __forceinline__ _Float16 out_cast<_Float16>(float x) { return (_Float16)x; }
 
 // One wavefront per (sequence b, query head h).  Every lane reads the same
-// (m_k, l_k) of each partial and its own dims of o_k, eight partials per
-// round of loads, and folds them in with an online log-sum-exp; there is no
-// cross-lane traffic at all.
+// (m_k, l_k) of each partial and its own dims of o_k, eight or sixteen
+// partials per round of loads, and folds them in with an online
+// log-sum-exp; there is no cross-lane traffic at all.
 template <typename TS>
 __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
   const int H = p.vheads;   // (virtual) KV heads
@@ -105,10 +107,14 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
 #pragma unroll
   for (int i = 0; i < kDimsPerLane; ++i) a[i] = 0.f;
 
-  for (int k0 = 0; k0 < K; k0 += 8) {
-    float mv[8], lv[8], ov[8][kDimsPerLane];
+  // One round: the loads of partials k0 .. k0+N-1 are issued together, then
+  // folded in order.  Up to 8 partials (the usual case) take one round of 8;
+  // more take rounds of 16, one memory round trip per 16 partials.
+  auto fold_round = [&](int k0, auto n) {
+    constexpr int N = decltype(n)::value;
+    float mv[N], lv[N], ov[N][kDimsPerLane];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < N; ++u) {
       const int k = min(k0 + u, K - 1);   // duplicates past K are skipped below
       mv[u] = mb[(int64_t)k * stride_m];
       lv[u] = mb[(int64_t)k * stride_m + 1];
@@ -119,7 +125,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < N; ++u) {
       if (k0 + u >= K) break;
       if (mv[u] == -INFINITY) continue;   // a partial with every token masked (dense decode)
       const float Mn = fmaxf(M, mv[u]);
@@ -130,7 +136,10 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeParams p) {
       for (int i = 0; i < kDimsPerLane; ++i) a[i] = a[i] * sc + w * ov[u][i];
       M = Mn;
     }
-  }
+  };
+  int k0 = 0;
+  for (; K - k0 > 8; k0 += 16) fold_round(k0, std::integral_constant<int, 16>());
+  for (; k0 < K; k0 += 8) fold_round(k0, std::integral_constant<int, 8>());
   const float inv = L > 0.f ? 1.0f / L : 0.f;   // nothing attended: zeros
 #pragma unroll
   for (int i = 0; i < kDimsPerLane; ++i) {
