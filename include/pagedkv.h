@@ -272,8 +272,8 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * with at most 16 query heads per wavefront, when every pair's workgroup is
  * resident at once and the longest sequence the block tables allow,
  * max_blocks_per_seq * block_size tokens, holds at most 256 KiB of K and V
- * per KV head (1024 tokens at head_dim 64 in bf16 or fp16, 512 at 128, 256
- * in fp32 at 128); see paged_attention_set_split_mode.
+ * per KV head (1024 tokens at head_dim 64 in bf16 or fp16, 512 at 128; 512
+ * and 256 in fp32); see paged_attention_set_split_mode.
  * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
  * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and 256 and
  * for block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4

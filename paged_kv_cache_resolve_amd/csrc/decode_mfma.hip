@@ -267,6 +267,7 @@ struct Stream {
   using OutElem = typename E::elem;   // element type of q, out and the pool
   // fits the per-pair kernel's 256 registers per lane without spilling
   static constexpr bool kPairs = !DENSE && D <= 128 && NC == 1;
+  static constexpr int kDim = D;
   using Buf = ChunkBuf<E, D, TILES>;
   static constexpr int NK = D / 32;   // 16-byte K loads per lane per tile
   static constexpr int VD = D / 16;   // V dims per lane
@@ -692,6 +693,7 @@ struct StreamF32 {
   static constexpr int NB = D / 16;   // output blocks (h, e)
   using OutElem = float;
   static constexpr bool kPairs = true;
+  static constexpr int kDim = D;
   struct Buf {
     float4 k[KQ / 4];
     float4 v[4][NH];
@@ -994,8 +996,9 @@ constexpr int kPairWaves = 8;
 // K/V bytes per wavefront up to which the per-pair kernel is used.  Measured
 // (batches of 4 to 64 sequences, head_dim 64 and 128, bf16 and fp32): one
 // workgroup per pair is 15-25% faster than the chunk split and merge kernel
-// up to ~32 KB per wavefront, even at ~48 KB, and slower beyond, where the
-// wavefronts' serial chunks outweigh the saved merge launch.
+// up to ~32 KB per wavefront, and slower beyond: a pair's bytes then all go
+// through one CU, which streams only ~27 GB/s however many wavefronts it
+// runs (16 wavefronts per pair were slower than 8 at the same length).
 constexpr int64_t kPairBytesPerWave = 32 << 10;
 
 template <typename S>
@@ -1024,7 +1027,8 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
   }
 
   const VHead vh = vhead_rows(g, p.qsplit, p.kv_group);
-  const int D = p.pool.head_dim;
+  constexpr int D = S::kDim;
+  constexpr int DPL = (D + 63) / 64;   // dims per lane in the merge
   Out* out = static_cast<Out*>(p.out) + ((int64_t)b * p.num_q_heads + vh.first) * D;
   if (A == 0) {
     for (int hn = w; hn < vh.count; hn += kPairWaves)
@@ -1033,7 +1037,7 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
     __syncthreads();   // the A partials are written (workgroup-scope release and acquire)
     const int G = p.group;   // partial slot stride
     for (int hn = w; hn < vh.count; hn += kPairWaves) {
-      float mv[kPairWaves], lv[kPairWaves], ov[kPairWaves][4];
+      float mv[kPairWaves], lv[kPairWaves], ov[kPairWaves][DPL];
 #pragma unroll
       for (int u = 0; u < kPairWaves; ++u) {
         const int k = min(u, A - 1);   // copies past A are not folded
@@ -1041,26 +1045,29 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
         mv[u] = p.ws_ml[2 * e];
         lv[u] = p.ws_ml[2 * e + 1];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < DPL; ++i) {
           const int d = lane + 64 * i;
           ov[u][i] = d < D ? p.ws_o[e * D + d] : 0.f;
         }
       }
-      float M = -INFINITY, L = 0.f, a[4] = {0.f, 0.f, 0.f, 0.f};
+      float M = -INFINITY, L = 0.f, a[DPL];
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) a[i] = 0.f;
 #pragma unroll
       for (int u = 0; u < kPairWaves; ++u) {
-        if (u >= A) break;
-        const float Mn = fmaxf(M, mv[u]);
-        const float sc = __builtin_amdgcn_exp2f(M - Mn);
-        const float wt = __builtin_amdgcn_exp2f(mv[u] - Mn);
-        L = L * sc + wt * lv[u];
+        if (u < A) {
+          const float Mn = fmaxf(M, mv[u]);
+          const float sc = __builtin_amdgcn_exp2f(M - Mn);
+          const float wt = __builtin_amdgcn_exp2f(mv[u] - Mn);
+          L = L * sc + wt * lv[u];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) a[i] = a[i] * sc + wt * ov[u][i];
-        M = Mn;
+          for (int i = 0; i < DPL; ++i) a[i] = a[i] * sc + wt * ov[u][i];
+          M = Mn;
+        }
       }
       const float inv = 1.0f / L;   // every piece holds at least one token
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < DPL; ++i) {
         const int d = lane + 64 * i;
         if (d < D) out[(int64_t)hn * D + d] = (Out)(a[i] * inv);
       }
@@ -1109,22 +1116,37 @@ bool mfma_supported(const kv_pool* pool, int group) {
 int mfma_chunk_tokens(int head_dim) { return 16 * (head_dim == 256 ? kTilesD256 : kTilesPerStep); }
 
 namespace {
-// Pass 1 for stream type S: the per-pair kernel when p.pair_mode asks for
-// it and every pair's workgroup is resident at once (else p.pair_mode is
-// cleared), otherwise the persistent kernel on wgs workgroups.
+// Launch the per-pair kernel if its instantiation for S runs without scratch
+// (register spills), the pieces' slots fit the workspace and every pair's
+// workgroup is resident at once.
+template <typename S>
+bool launch_pairs(const DecodeParams& p, int64_t pairs, hipStream_t s) {
+  const void* fn = reinterpret_cast<const void*>(&decode_pair_kernel<S>);
+  static const bool spill_free = [fn] {
+    hipFuncAttributes a;
+    return hipFuncGetAttributes(&a, fn) == hipSuccess && a.localSizeBytes == 0;
+  }();
+  int resident = 0;
+  if (!spill_free || (kPairWaves - 1) * pairs > kMaxWaves ||
+      resident_workgroups(fn, 64 * kPairWaves, 0, &resident) != hipSuccess || pairs > resident)
+    return false;
+  hipLaunchKernelGGL((decode_pair_kernel<S>), dim3((unsigned)pairs), dim3(64 * kPairWaves), 0, s,
+                     p);
+  return true;
+}
+
+// Pass 1 for stream type S.  When p.pair_mode asks for it, the per-pair
+// kernel runs if the longest sequence the block tables allow holds at most
+// kPairBytesPerWave of K and V per wavefront; otherwise p.pair_mode is
+// cleared and the persistent kernel runs on wgs workgroups.
 template <typename S>
 void launch_one(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
   if constexpr (S::kPairs) {
     if (p.pair_mode) {
       const int64_t pairs = (int64_t)p.batch * p.vheads;
-      int resident = 0;
-      if (resident_workgroups(reinterpret_cast<const void*>(&decode_pair_kernel<S>),
-                              64 * kPairWaves, 0, &resident) == hipSuccess &&
-          pairs <= resident) {
-        hipLaunchKernelGGL((decode_pair_kernel<S>), dim3((unsigned)pairs), dim3(64 * kPairWaves), 0,
-                           s, p);
-        return;
-      }
+      const int64_t bytes = 2 * (int64_t)p.max_blocks_per_seq * p.pool.block_size *
+                            p.pool.head_dim * (p.dtype == PAGEDKV_F32 ? 4 : 2);
+      if (bytes <= kPairWaves * kPairBytesPerWave && launch_pairs<S>(p, pairs, s)) return;
     }
   }
   p.pair_mode = 0;
@@ -1229,16 +1251,6 @@ hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   if (useful < p.units) {
     p.units = (int)(useful < 1 ? 1 : useful);
     wgs = (p.units * p.vheads + kWaves - 1) / kWaves;
-  }
-  // Per-pair workgroups: only while every pair's pieces fit in the
-  // workspace slots and the longest sequence the block tables allow holds
-  // at most kPairBytesPerWave of K and V per wavefront.
-  if (p.pair_mode) {
-    const int64_t pairs = (int64_t)p.batch * p.vheads;
-    const int64_t pair_bytes = 2 * (int64_t)p.max_blocks_per_seq * p.pool.block_size *
-                               p.pool.head_dim * (p.dtype == PAGEDKV_F32 ? 4 : 2);
-    if ((kPairWaves - 1) * pairs > kMaxWaves || pair_bytes > kPairWaves * kPairBytesPerWave)
-      p.pair_mode = 0;
   }
   if (p.dtype == PAGEDKV_F32)
     launch_f32(p, wgs, lds, s);

@@ -80,9 +80,10 @@ def pair_lens(dtype, D, BS):
     and the longest pair the per-pair kernel takes."""
     c = 16 if dtype == "f32" else 32   # tokens per chunk at head_dim <= 128
     top = longest_pair_tokens(dtype, D, BS)
-    lens = [0, 1, c - 1, c, c + 1, 3 * c + 5, 7 * c, 8 * c, 8 * c + 1, top - 1, top]
+    lens = [0, 1, c - 1, c, c + 1, 3 * c + 5, 7 * c, 8 * c, 8 * c + 1, 12 * c + 3, 16 * c,
+            16 * c + 1, top - 1, top]
     assert top >= 8 * c + 1
-    return lens
+    return sorted(set(t for t in lens if t <= top))
 
 
 CASES = [
@@ -90,6 +91,7 @@ CASES = [
     ("bf16", 14, 2, 64, 16),
     ("bf16", 16, 1, 128, 32),
     ("f16", 8, 2, 128, 16),
+    ("f16", 16, 2, 64, 16),
     ("f16", 12, 4, 96, 16),
     ("bf16", 8, 2, 64, 8),     # 8-token blocks
     ("f16", 8, 2, 128, 4),     # 4-token blocks
@@ -121,20 +123,22 @@ def test_pair_split_matches_oracle_and_chunk_split(dtype, Hq, Hkv, D, BS):
                        out_p2.view(torch.int16) if out_p2.element_size() == 2 else out_p2)
 
 
-@pytest.mark.parametrize("dtype,D,extra,expect_pairs", [
-    ("bf16", 64, 0, True),     # 1024 tokens: the limit
-    ("bf16", 64, 16, False),   # one block more
-    ("bf16", 128, 0, True),    # 512 tokens
-    ("bf16", 128, 16, False),
-    ("f32", 64, 0, True),      # 512 tokens
-    ("f32", 64, 16, False),
+@pytest.mark.parametrize("dtype,D,BS,extra,expect_pairs", [
+    ("bf16", 64, 16, 0, True),     # 1024 tokens: the limit
+    ("bf16", 64, 16, 16, False),   # one block more
+    ("bf16", 64, 8, 0, True),      # 8-token blocks
+    ("bf16", 64, 8, 8, False),
+    ("bf16", 128, 16, 0, True),    # 512 tokens
+    ("bf16", 128, 16, 16, False),
+    ("f32", 64, 16, 0, True),      # 512 tokens
+    ("f32", 64, 16, 16, False),
 ])
-def test_pair_split_length_limit(dtype, D, extra, expect_pairs):
+def test_pair_split_length_limit(dtype, D, BS, extra, expect_pairs):
     """The choice follows max_blocks_per_seq * block_size, and both sides of
     the limit match the oracle."""
-    longest = longest_pair_tokens(dtype, D, 16) + extra
-    say(f"pair split limit {dtype} D={D} longest={longest}")
-    w = workload(dtype, 8, 2, D, 16, [longest, 5, 300])
+    longest = longest_pair_tokens(dtype, D, BS) + extra
+    say(f"pair split limit {dtype} D={D} BS={BS} longest={longest}")
+    w = workload(dtype, 8, 2, D, BS, [longest, 5, 300])
     dw = DeviceWorkload(w)
     out, wrote = decode_with(dw, pk.SPLIT_AUTO)
     assert wrote != expect_pairs
