@@ -39,12 +39,12 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "c123d865f0db84d80fee9ddf289490a1a9d4debe3a3cac299df9a7c2ba54f155",
-        "bytes": 585640338,
+        "kernel_sha256": "26476d9b8d3e977aeb9225676e817acbcb7ce3f10b5c58c3ad64c95bc7b03ad4",
+        "bytes": 585653099,
     },
     "long_context_bf16": {
-        "kernel_sha256": "c123d865f0db84d80fee9ddf289490a1a9d4debe3a3cac299df9a7c2ba54f155",
-        "bytes": 2210917922,
+        "kernel_sha256": "26476d9b8d3e977aeb9225676e817acbcb7ce3f10b5c58c3ad64c95bc7b03ad4",
+        "bytes": 2210953461,
     },
 }
 
