@@ -45,7 +45,7 @@ def capture(fn):
 
 
 @pytest.mark.parametrize("fused,idx,S", [(False, 2, 6), (True, 2, 6), (True, 0, None),
-                                         (True, 6, 4)])
+                                         (False, 0, None), (True, 1, None), (True, 6, 4)])
 def test_graph_replays_match_eager(fused, idx, S, split):
     say(f"graph replay fused={fused} workload {idx} S={S}")
     w = make_workload(idx, **({"S": S} if S else {}))
