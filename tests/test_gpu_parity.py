@@ -238,6 +238,9 @@ EDGE_CASES = [
     ("bf16", 8, 2, 64, 8),      # MFMA bf16, 8-token blocks (per-lane block lookups)
     ("bf16", 8, 2, 128, 4),     # MFMA bf16, 4-token blocks
     ("bf16", 6, 2, 64, 2),      # generic bf16 (2-token blocks)
+    ("f32", 6, 2, 36, 16),      # generic fp32, head_dim 36: merge lanes of 4 dims (not a multiple of 8)
+    ("f32", 4, 2, 100, 16),     # generic fp32, head_dim 100
+    ("f32", 8, 2, 20, 8),       # generic fp32, head_dim 20
     ("bf16", 6, 2, 96, 16),     # MFMA bf16, head_dim 96 (12-byte V rows)
     ("bf16", 16, 2, 96, 32),    # MFMA bf16, head_dim 96, G = 8
     ("bf16", 6, 2, 96, 8),      # MFMA bf16, head_dim 96, 8-token blocks
