@@ -423,6 +423,20 @@ def main(argv=None) -> int:
     except RuntimeError as exc:   # capture unavailable: report it, keep the rest
         print(f"[bench] graph replay skipped: {exc}", file=sys.stderr, flush=True)
 
+    # Which pass-1 form the call took: the chunk split's pass 1 writes the
+    # per-sequence chunk prefix at the start of the workspace, the per-pair
+    # kernel leaves it untouched.  (One more step on replica 0: it appends the
+    # same rows again, which leaves the pool as it was.)
+    r0 = reps_dev[0]
+    probe = torch.full((pk.paged_attention_workspace_bytes(r0["pool"], w0.S, w0.Hq),), 0xA5,
+                       dtype=torch.uint8, device="cuda")
+    pk.paged_attention_decode_append(r0["out"], r0["q"], r0["pool"], w0.layer, r0["tables"],
+                                     r0["lens"], w0.scale, r0["k"], r0["v"], r0["pos"],
+                                     workspace=probe)
+    torch.cuda.synchronize()
+    split_used = "chunks" if bool((probe[: 4 * (w0.S + 1)] != 0xA5).any().item()) else "pairs"
+    del probe
+
     step_bytes = np.mean([decode_bytes(r["w"]) + append_bytes(r["w"]) for r in reps_dev])
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = step_bytes / (dec_avg_ms * 1e-3) / 1e9
@@ -459,9 +473,12 @@ def main(argv=None) -> int:
         "calls_timed": n_dec,
         "call_ms_per_call_events_p10_p50_p90": [
             round(float(np.percentile(dec_ms, q)), 5) for q in (10, 50, 90)],
+        "split_used": split_used,
         "roofline": {
-            "kernel": "paged_attention_decode_append (decode pass 1 reading the new rows, "
-                      "then the split merge that also stores them)",
+            "kernel": ("paged_attention_decode_append (decode pass 1 reading the new rows, "
+                       "then the split merge that also stores them)") if split_used == "chunks" else
+                      ("paged_attention_decode_append (one kernel: per-pair pass 1, the merge of "
+                       "its pieces and the row store in the same workgroup)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,
