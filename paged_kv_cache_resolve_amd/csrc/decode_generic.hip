@@ -224,7 +224,7 @@ __device__ __forceinline__ void generic_segment(const DecodeParams& p, float* qs
 template <typename TS, int DPL>
 __global__ __launch_bounds__(64) void decode_generic_kernel(DecodeParams p) {
   extern __shared__ int32_t lds[];
-  __shared__ int32_t scan[64];
+  __shared__ int32_t scan[1];
   int32_t* prefix = lds;
   // q (G x D floats) and probabilities (G x 64 floats) after the prefix
   const int pre_words = ((p.batch + 1) + 3) & ~3;

@@ -947,7 +947,7 @@ __device__ __forceinline__ void stream_chunks(const DecodeParams& p, int lane, i
 template <typename S>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   extern __shared__ int32_t prefix[];
-  __shared__ int32_t scan[kThreads];
+  __shared__ int32_t scan[kThreads / 64];
   const int H = p.vheads;   // (virtual) KV heads
 
   if constexpr (S::kDense) {   // every sequence is dense_len tokens long

@@ -11,12 +11,17 @@ __device__ __forceinline__ int chunks_of(int T, int ct) {
 }
 
 // prefix[b] = sum_{b' < b} chunks_of(T_b', ct) for b in [0, batch], computed by
-// one workgroup of NT threads into LDS.  `scan` is NT ints of LDS scratch.
-// Every thread of the workgroup must call this; it ends with a barrier.
+// one workgroup of NT threads (a multiple of 64) into LDS.  Thread t sums a
+// contiguous run of sequences; the runs' totals are scanned within each
+// wavefront with lane shuffles, and the wavefront totals (NT / 64 ints of
+// `scan`, LDS) are added after one barrier.  Every thread of the workgroup
+// must call this; it ends with a barrier.
 template <int NT>
 __device__ void block_chunk_prefix(const int32_t* __restrict__ lens, int batch,
                                    int ct, int32_t* prefix, int32_t* scan) {
+  static_assert(NT % 64 == 0, "whole wavefronts");
   const int tid = threadIdx.x;
+  const int lane = tid & 63;
   const int per = (batch + NT - 1) / NT;
   const int lo = min(batch, tid * per);
   const int hi = min(batch, lo + per);
@@ -26,16 +31,16 @@ __device__ void block_chunk_prefix(const int32_t* __restrict__ lens, int batch,
     prefix[i + 1] = n;
     local += n;
   }
-  scan[tid] = local;
-  __syncthreads();
-  // Hillis-Steele inclusive scan over the NT per-thread sums.
-  for (int d = 1; d < NT; d <<= 1) {
-    const int add = tid >= d ? scan[tid - d] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
+  int incl = local;   // inclusive scan of the run totals across the wavefront
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int up = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += up;
   }
-  int run = scan[tid] - local;   // exclusive offset of this thread's segment
+  if (lane == 63) scan[tid >> 6] = incl;
+  __syncthreads();
+  int run = incl - local;   // exclusive offset of this thread's run
+  for (int w = 0; w < (tid >> 6); ++w) run += scan[w];
   for (int i = lo; i < hi; ++i) {
     run += prefix[i + 1];
     prefix[i + 1] = run;
