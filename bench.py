@@ -39,12 +39,12 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "26476d9b8d3e977aeb9225676e817acbcb7ce3f10b5c58c3ad64c95bc7b03ad4",
-        "bytes": 585653099,
+        "kernel_sha256": "8cf161c25a4e9e0cf584e40f7707d42b003804f8e2625039b2439a5cf46144f4",
+        "bytes": 585648542,
     },
     "long_context_bf16": {
-        "kernel_sha256": "26476d9b8d3e977aeb9225676e817acbcb7ce3f10b5c58c3ad64c95bc7b03ad4",
-        "bytes": 2210953461,
+        "kernel_sha256": "8cf161c25a4e9e0cf584e40f7707d42b003804f8e2625039b2439a5cf46144f4",
+        "bytes": 2210957179,
     },
 }
 
