@@ -205,8 +205,7 @@ int paged_kv_gather(void* k_out, void* v_out, uint8_t* mask, const kv_pool_t* po
   if (batch == 0 || max_len == 0) return PAGEDKV_OK;
   if (!k_out || !v_out || !mask || !block_tables || !context_lens) return PAGEDKV_ERR_INVALID_ARG;
   if (!aligned16(k_out) || !aligned16(v_out)) return PAGEDKV_ERR_INVALID_ARG;
-  const int units = pool->head_dim * elem_size(pool->dtype) / 16;
-  if (units > 256 || (units & (units - 1)) != 0) return PAGEDKV_ERR_UNSUPPORTED;
+  if (pool->head_dim * elem_size(pool->dtype) > 256 * 16) return PAGEDKV_ERR_UNSUPPORTED;
   return hip_status(launch_gather(k_out, v_out, mask, pool, layer, block_tables,
                                   max_blocks_per_seq, context_lens, batch, max_len,
                                   static_cast<hipStream_t>(stream)));

@@ -131,9 +131,11 @@ __global__ __launch_bounds__(256) void append_rows_kernel(AppendArgs a) {
   }
 }
 
-// Workgroup = 256 threads = (256 / units) tokens x units of one KV head.
-// grid = (ceil(max_len / tokens_per_iter), kv_heads, batch); each workgroup
-// walks kTokIters token tiles.
+// Workgroup = 256 threads = floor(256 / units) tokens x units (16-byte row
+// pieces) of one KV head; threads past the last whole token idle (rows of
+// 12 units, head_dim 96 in bf16, leave 4 of 256).  grid = (ceil(max_len /
+// tokens_per_iter), kv_heads, batch); each workgroup walks kTokIters token
+// tiles.
 constexpr int kTokIters = 4;
 
 __global__ __launch_bounds__(256) void gather_kernel(PoolGeom pool, int layer, int elem,
@@ -142,11 +144,11 @@ __global__ __launch_bounds__(256) void gather_kernel(PoolGeom pool, int layer, i
                                                      uint8_t* __restrict__ mask,
                                                      const int32_t* __restrict__ tables, int mb,
                                                      const int32_t* __restrict__ lens,
-                                                     int max_len, int units_log2) {
-  const int units = 1 << units_log2;
-  const int u = threadIdx.x & (units - 1);
-  const int tl = threadIdx.x >> units_log2;
-  const int tiles = 256 >> units_log2;                  // tokens per iteration
+                                                     int max_len, int units) {
+  const int tiles = 256 / units;                        // tokens per iteration
+  if ((int)threadIdx.x >= tiles * units) return;
+  const int tl = threadIdx.x / units;
+  const int u = threadIdx.x - tl * units;
   const int g = blockIdx.y;
   const int b = blockIdx.z;
   const int T = lens[b];
@@ -267,15 +269,13 @@ hipError_t launch_gather(void* k_out, void* v_out, uint8_t* mask, const kv_pool*
   const PoolGeom g = geom_of(pool);
   const int elem = elem_size(pool->dtype);
   const int units = pool->head_dim * elem / 16;
-  int units_log2 = 0;
-  while ((1 << units_log2) < units) ++units_log2;
-  if ((1 << units_log2) != units || units > 256) return hipErrorInvalidValue;
-  const int tiles = 256 >> units_log2;
+  if (units < 1 || units > 256 || units * 16 != pool->head_dim * elem) return hipErrorInvalidValue;
+  const int tiles = 256 / units;
   const int per_block = tiles * kTokIters;
   const dim3 grid((max_len + per_block - 1) / per_block, pool->kv_heads, batch);
   hipLaunchKernelGGL(gather_kernel, grid, dim3(256), 0, s, g, layer, elem,
                      static_cast<char*>(k_out), static_cast<char*>(v_out), mask, tables, mb, lens,
-                     max_len, units_log2);
+                     max_len, units);
   return hipGetLastError();
 }
 

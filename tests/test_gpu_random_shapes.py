@@ -20,7 +20,7 @@ import oracle
 import paged_kv_cache_resolve_amd as pk
 from workloads import make_workload
 
-from gpu_helpers import NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, say
+from gpu_helpers import NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say
 
 pytestmark = [
     pytest.mark.gpu,
@@ -114,3 +114,63 @@ def test_random_shape_fused_step(i, dtype, Hq, Hkv, D, BS, lens, split):
                                         w.context_lens, w.q, w.scale)
     assert_attention_close(out, ref, dtype, what=f"random fused case {i}")
     assert dev_to_np(dw.pool.data).tobytes() == ref_pool.tobytes(), "pool differs from oracle append"
+
+
+def random_rows(rng, shape, dtype):
+    """Random rows in the pool's storage format (bf16 as bit patterns)."""
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if dtype == "bf16":
+        from workloads import bf16_round_bits
+        return bf16_round_bits(x)
+    return x.astype(np.float16) if dtype == "f16" else x
+
+
+@pytest.mark.parametrize("i,dtype,Hq,Hkv,D,BS,lens", CASES[:16], ids=[f"case{c[0]}" for c in CASES[:16]])
+def test_random_shape_gather(i, dtype, Hq, Hkv, D, BS, lens):
+    """paged_kv_gather against the oracle's gather, bit for bit, with a
+    max_len past the longest sequence (all-padding tail)."""
+    say(f"random gather case {i}: {dtype} Hkv={Hkv} D={D} BS={BS} S={len(lens)}")
+    w = build(dtype, Hq, Hkv, D, BS, lens)
+    dw = DeviceWorkload(w)
+    max_len = max(lens) + 5
+    k, v, mask = pk.paged_kv_gather(dw.pool, w.layer, dw.tables, dw.lens, max_len)
+    torch.cuda.synchronize()
+    rk, rv, rm = oracle.paged_kv_gather(w.pool, w.layer, w.block_tables, w.context_lens, max_len)
+    assert dev_to_np(k).tobytes() == rk.tobytes()
+    assert dev_to_np(v).tobytes() == rv.tobytes()
+    assert mask.cpu().numpy().tobytes() == rm.tobytes()
+
+
+@pytest.mark.parametrize("i,dtype,Hq,Hkv,D,BS,lens", CASES[:16], ids=[f"case{c[0]}" for c in CASES[:16]])
+def test_random_shape_appends(i, dtype, Hq, Hkv, D, BS, lens):
+    """kv_append_tokens (a ragged run of tokens per sequence, some skipped)
+    and kv_append_layers (one token on every layer) against the oracle's
+    appends: the whole pool, bit for bit."""
+    say(f"random appends case {i}: {dtype} Hkv={Hkv} D={D} BS={BS} S={len(lens)}")
+    w = build(dtype, Hq, Hkv, D, BS, lens)
+    rng = np.random.default_rng(1000 + i)
+    S = len(lens)
+    starts = np.full(S, -1, dtype=np.int32)
+    counts = np.zeros(S, dtype=np.int32)
+    for b, T in enumerate(lens):
+        if T > 0 and rng.random() < 0.85:
+            starts[b] = rng.integers(0, T)
+            counts[b] = rng.integers(1, T - starts[b] + 1)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    total = int(offsets[-1])
+    kr = random_rows(rng, (total, Hkv, D), dtype)
+    vr = random_rows(rng, (total, Hkv, D), dtype)
+    dw = DeviceWorkload(w)
+    if total > 0:
+        pk.kv_append_tokens(dw.pool, w.layer, np_to_dev(kr, dtype), np_to_dev(vr, dtype),
+                            dw.tables, torch.from_numpy(starts).cuda(),
+                            torch.from_numpy(offsets).cuda())
+    positions = np.array([t - 1 for t in lens], dtype=np.int32)
+    kl = random_rows(rng, (S, w.L, Hkv, D), dtype)
+    vl = random_rows(rng, (S, w.L, Hkv, D), dtype)
+    pk.kv_append_layers(dw.pool, np_to_dev(kl, dtype), np_to_dev(vl, dtype), dw.tables,
+                        torch.from_numpy(positions).cuda())
+    torch.cuda.synchronize()
+    ref = oracle.kv_append_tokens(w.pool, w.layer, w.block_tables, starts, offsets, kr, vr)
+    ref = oracle.kv_append_layers(ref, w.block_tables, positions, kl, vl)
+    assert dev_to_np(dw.pool.data).tobytes() == ref.tobytes(), "pool differs from the oracle's appends"
