@@ -174,3 +174,25 @@ def test_random_shape_appends(i, dtype, Hq, Hkv, D, BS, lens):
     ref = oracle.kv_append_tokens(w.pool, w.layer, w.block_tables, starts, offsets, kr, vr)
     ref = oracle.kv_append_layers(ref, w.block_tables, positions, kl, vl)
     assert dev_to_np(dw.pool.data).tobytes() == ref.tobytes(), "pool differs from the oracle's appends"
+
+
+DENSE_CASES = [c for c in CASES if c[1] != "f32" and c[4] in (64, 96, 128, 256)][:12]
+
+
+@pytest.mark.parametrize("i,dtype,Hq,Hkv,D,BS,lens", DENSE_CASES,
+                         ids=[f"case{c[0]}" for c in DENSE_CASES])
+def test_random_shape_gather_then_dense(i, dtype, Hq, Hkv, D, BS, lens):
+    """The gather-then-attend path (paged_kv_gather, then
+    dense_attention_decode over the padded batch) against the oracle's paged
+    decode of the same pool: the padding and the mask must leave the result
+    unchanged."""
+    say(f"random gather+dense case {i}: {dtype} Hq={Hq} Hkv={Hkv} D={D} BS={BS} S={len(lens)}")
+    w = build(dtype, Hq, Hkv, D, BS, lens)
+    dw = DeviceWorkload(w)
+    k, v, mask = pk.paged_kv_gather(dw.pool, w.layer, dw.tables, dw.lens, max(lens) + 3)
+    out = torch.empty_like(dw.q)
+    pk.dense_attention_decode(out, dw.q, k, v, mask, w.scale)
+    torch.cuda.synchronize()
+    ref = oracle.paged_attention_decode(w.pool, w.dtype, w.layer, w.block_tables,
+                                        w.context_lens, w.q, w.scale)
+    assert_attention_close(out, ref, dtype, what=f"gather+dense case {i}")
