@@ -961,9 +961,23 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     for (int i = threadIdx.x; i <= p.batch; i += kThreads) p.ws_prefix[i] = prefix[i];
 
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * kWaves + uni(threadIdx.x >> 6);
-  const int64_t unit = wave / H;
-  const int g = (int)(wave - unit * H);
+  // A unit's H wavefronts span npu = H / kWaves workgroups.  Those workgroups
+  // are blockIdx u, u + grid/npu, ...: workgroups go to the XCDs round-robin,
+  // so a unit's workgroups share an XCD when grid/npu is a multiple of 8.
+  int64_t unit;
+  int g;
+  const int w = uni(threadIdx.x >> 6);
+  const int npu = H / kWaves;
+  if (H % kWaves == 0 && npu > 1 && gridDim.x % npu == 0) {
+    const int stride = gridDim.x / npu;
+    const int k = blockIdx.x / stride;
+    unit = blockIdx.x - k * stride;
+    g = k * kWaves + w;
+  } else {
+    const int64_t wave = (int64_t)blockIdx.x * kWaves + w;
+    unit = wave / H;
+    g = (int)(wave - unit * H);
+  }
   const int64_t C = uni(prefix[p.batch]);
   const int64_t Ue = waves_eff(C, p.units, p.min_chunks);
   if (unit >= Ue) return;
