@@ -39,12 +39,12 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "8cf161c25a4e9e0cf584e40f7707d42b003804f8e2625039b2439a5cf46144f4",
-        "bytes": 585648542,
+        "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
+        "bytes": 585595523,
     },
     "long_context_bf16": {
-        "kernel_sha256": "8cf161c25a4e9e0cf584e40f7707d42b003804f8e2625039b2439a5cf46144f4",
-        "bytes": 2210957179,
+        "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
+        "bytes": 2210996659,
     },
 }
 
