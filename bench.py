@@ -5,15 +5,28 @@ sequence's new token K/V goes into its tail block and paged-attention decode
 runs over the cache (block-table resolve, K/V stream, scaled QK^T, online
 softmax, PV, split merge, output write), both in one library call
 (paged_attention_decode_append, issued through a DecodePlan: the step's
-buffers are fixed, so they are checked once).  The batched paged-KV gather is timed
-separately and reported beside the step, and so are the two multi-row appends
-(a prompt's tokens into one layer; one token into every layer).
+buffers are fixed, so they are checked once).
 
     python bench.py [--workload llama8b_decode_bf16] [--steps K] [--warmup W]
+                    [--extra long_context_bf16,churned_pool_bf16_gqa7]
 
-Prints one JSON line.  `value` is effective HBM GB/s of the step (algorithmic
-bytes / step time, inputs resident in HBM).  Inputs are rotated among
-replicas so that consecutive steps do not hit in the 256 MB Infinity Cache.
+Prints one JSON line.  The top level is the main workload (the Llama-8B-
+shaped layer by default): `value` is effective HBM GB/s of its step
+(algorithmic bytes / step time, inputs resident in HBM).  `workloads` holds
+the same measurement for each --extra workload (by default the long-context
+batch, the other configuration the 70%-of-peak target names, and the
+churned-pool batch with its standalone one-token append).  Beside them: the
+batched paged-KV gather and the dense decode over its output, the two
+multi-row appends, the host block manager, an HBM read-ceiling probe, and
+the CPU oracle's rate on a bounded sample.  Inputs are rotated among
+replicas (same context lengths, redrawn tables and values) so that
+consecutive steps do not hit in the 256 MB Infinity Cache.
+
+    python bench.py --all-workloads --results-out profiles/results.json
+    python bench.py --render profiles/results.json
+
+measure every workload (one record each) and print the results table built
+from such a record.
 """
 
 from __future__ import annotations
@@ -223,7 +236,9 @@ def measure_manager(torch, pk, w, steps: int = 2000) -> dict:
 def cpu_baseline(w, budget_tokens: int, min_seconds: float = 10.0):
     """The oracle, as it stands, on a bounded sample of the same batch: whole
     sequences in a seeded order until `budget_tokens` cached tokens, run
-    repeatedly until `min_seconds` of CPU work; the median run is reported."""
+    repeatedly until `min_seconds` of CPU work; the median run is reported.
+    `cores` is the BLAS thread count its matrix products run on;
+    `host_cores_allowed` the CPUs this process may use."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -267,6 +282,7 @@ def cpu_baseline(w, budget_tokens: int, min_seconds: float = 10.0):
         "value": round(sample_bytes / dt / 1e9, 4),
         "unit": "GB/s",
         "cores": int(blas_threads),
+        "host_cores_allowed": len(os.sched_getaffinity(0)),
         "kind": "oracle",
         "sample": f"{len(seqs)} of {w.S} sequences ({toks} cached tokens) of the same batch, "
                   f"fp64 numpy gather-then-attend, median of {len(runs)} runs "
@@ -277,24 +293,380 @@ def cpu_baseline(w, budget_tokens: int, min_seconds: float = 10.0):
     }
 
 
+def _to_dev(torch, x, dtype):
+    """float32 / float16 array or bf16 bit patterns -> device tensor."""
+    if dtype in ("f32", "f16"):
+        return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+
+
+TORCH_DTYPES = {"f32": "float32", "bf16": "bfloat16", "f16": "float16"}
+
+
+def load_replicas(torch, pk, name: str, rotate: int, split: str):
+    """The workload's input replicas on the GPU, each with a DecodePlan of the
+    fused step.  Replica r > 0 keeps replica 0's context lengths (the same
+    bytes) and redraws tables, pool values, q and new rows."""
+    from workloads import make_workload
+    idx = WORKLOADS[name]
+    w0 = make_workload(idx)
+    kvb = decode_bytes(w0)
+    n = rotate or max(1, min(4, math.ceil(4 * MALL_BYTES / max(kvb, 1))))
+    ws = [w0] + [make_workload(idx, seed_offset=r, keep_lens=True) for r in range(1, n)]
+    tdt = getattr(torch, TORCH_DTYPES[w0.dtype])
+    reps = []
+    for w in ws:
+        pool = pk.KVPool(w.NB, w.BS, w.L, w.Hkv, w.D, tdt, data=_to_dev(torch, w.pool, w.dtype))
+        r = dict(w=w, pool=pool, tables=torch.from_numpy(w.block_tables).cuda(),
+                 lens=torch.from_numpy(w.context_lens).cuda(),
+                 pos=torch.from_numpy(w.positions).cuda(), q=_to_dev(torch, w.q, w.dtype),
+                 k=_to_dev(torch, w.k_new, w.dtype), v=_to_dev(torch, w.v_new, w.dtype),
+                 out=torch.empty(w.S, w.Hq, w.D, dtype=tdt, device="cuda"))
+        r["plan"] = pk.DecodePlan(r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"],
+                                  w.scale, r["k"], r["v"], r["pos"], split=split)
+        reps.append(r)
+    print(f"[bench] workload {name}: S={w0.S} Hq={w0.Hq} Hkv={w0.Hkv} D={w0.D} BS={w0.BS} "
+          f"sum(T)={int(w0.context_lens.sum())} replicas={n}", file=sys.stderr, flush=True)
+    return reps
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def back_to_back_ms(torch, fn, n: int) -> float:
+    """Mean duration of fn(i), i < n, enqueued back to back on the current
+    stream between one pair of HIP events (after one untimed call)."""
+    stream = torch.cuda.current_stream()
+    fn(0)
+    torch.cuda.synchronize()
+    a, b = _events(torch)
+    a.record(stream)
+    for i in range(n):
+        fn(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / n
+
+
+def measure_step(torch, pk, name: str, steps: int, warmup: int, split: str, rotate: int = 0,
+                 graph: bool = True):
+    """Time the fused decode step of workload `name`.  Returns (record, replicas).
+
+    - ms_per_step: wall clock over exactly `steps` steps after `warmup`
+      untimed ones, bracketed by torch.cuda.synchronize();
+    - call_ms: the same call back to back between one pair of HIP events on
+      the launch stream (>= 100 calls): the roofline's kernel time;
+    - per-call event pairs for the p10/p50/p90 spread (each pair adds a small
+      gap, so these read slightly high);
+    - graph_ms_per_step: 32 steps captured in one HIP graph, replayed."""
+    reps = load_replicas(torch, pk, name, rotate, split)
+    w0 = reps[0]["w"]
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        reps[i % len(reps)]["plan"].run()
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = _events(torch)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / steps
+    gpu_ms_per_step = e0.elapsed_time(e1) / steps
+
+    n_dec = max(steps, 100)
+    call_ms = back_to_back_ms(torch, step, n_dec)
+    ev = [_events(torch) for _ in range(n_dec)]
+    for i in range(n_dec):
+        ev[i][0].record(stream)
+        step(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_call = [a.elapsed_time(b) for a, b in ev]
+
+    graph_ms = None
+    if graph:
+        try:
+            gplans = []
+            for r in reps:
+                w = r["w"]
+                wsb = pk.paged_attention_workspace_bytes(r["pool"], w.S, w.Hq)
+                gplans.append(pk.DecodePlan(
+                    r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"], w.scale,
+                    r["k"], r["v"], r["pos"],
+                    workspace=torch.zeros(wsb, dtype=torch.uint8, device="cuda"), split=split))
+            n_graph = 32
+
+            def graph_body():
+                for i in range(n_graph):
+                    gplans[i % len(gplans)].run()
+
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                graph_body()
+            stream.wait_stream(side)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                graph_body()
+            g.replay()
+            torch.cuda.synchronize()
+            g0, g1 = _events(torch)
+            g0.record(stream)
+            for _ in range(5):
+                g.replay()
+            g1.record(stream)
+            torch.cuda.synchronize()
+            graph_ms = g0.elapsed_time(g1) / (5 * n_graph)
+            del g, gplans
+        except RuntimeError as exc:   # capture unavailable: report it, keep the rest
+            print(f"[bench] graph replay skipped: {exc}", file=sys.stderr, flush=True)
+
+    # Which pass-1 form the call took: the chunk split's pass 1 writes the
+    # per-sequence chunk prefix at the start of the workspace (its first
+    # section), the per-pair kernel leaves it untouched.  The rest of the
+    # workspace stays zero, as the library requires of a new workspace.  (One
+    # more step on replica 0: it appends the same rows again, which leaves
+    # the pool as it was.)
+    r0 = reps[0]
+    nbytes = pk.paged_attention_workspace_bytes(r0["pool"], w0.S, w0.Hq)
+    probe = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    probe[: 4 * (w0.S + 1)] = 0xA5
+    pk.paged_attention_decode_append(r0["out"], r0["q"], r0["pool"], w0.layer, r0["tables"],
+                                     r0["lens"], w0.scale, r0["k"], r0["v"], r0["pos"],
+                                     workspace=probe, split=split)
+    torch.cuda.synchronize()
+    split_used = "chunks" if bool((probe[: 4 * (w0.S + 1)] != 0xA5).any().item()) else "pairs"
+    del probe
+
+    step_bytes = float(np.mean([decode_bytes(r["w"]) + append_bytes(r["w"]) for r in reps]))
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = step_bytes / (call_ms * 1e-3) / 1e9
+    rec = {
+        "workload": name,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "ms_per_step": round(ms_per_step, 5),
+        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "tokens_per_s": round(w0.S / (ms_per_step * 1e-3), 1),
+        "gpu_ms_per_step": round(gpu_ms_per_step, 5),
+        "call_ms": round(call_ms, 5),
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "calls_timed": n_dec,
+        "call_ms_per_call_events_p10_p50_p90": [
+            round(float(np.percentile(per_call, q)), 5) for q in (10, 50, 90)],
+        "split_used": split_used,
+        "dtype": w0.dtype,
+        "config": {
+            "workload": name,
+            "batch": w0.S, "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.D,
+            "block_size": w0.BS, "layers_in_pool": w0.L, "layer": w0.layer,
+            "sum_context_tokens": int(w0.context_lens.astype(np.int64).sum()),
+            "max_context": int(w0.context_lens.max()),
+            "input_replicas": len(reps),
+            "replicas_share_context_lens": True,
+            "split": split,
+            "parallelism": "single GPU",
+        },
+        "roofline": {
+            "kernel": "paged_attention_decode_append (one call: decode pass 1 reading the new "
+                      "rows, the merge of split sequences and the row store)",
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(name),
+            "algorithmic_bytes_per_launch": int(step_bytes),
+        },
+    }
+    return rec, reps
+
+
+def measure_append_only(torch, pk, reps, n: int = 200) -> dict:
+    """kv_append of one new token per sequence on its own (one launch),
+    back to back over the replicas."""
+    w0 = reps[0]["w"]
+
+    def app(i):
+        r = reps[i % len(reps)]
+        pk.kv_append(r["pool"], r["w"].layer, r["k"], r["v"], r["tables"], r["pos"])
+
+    ms = back_to_back_ms(torch, app, n)
+    b = append_bytes(w0)
+    return {"what": "kv_append of one token per sequence (all KV heads of the attended layer)",
+            "ms": round(ms, 5), "bytes": b, "GB_per_s": round(b / (ms * 1e-3) / 1e9, 2)}
+
+
+def measure_decode_only(torch, pk, reps, split: str, n: int = 200) -> float:
+    """paged_attention_decode alone (no append), back to back."""
+    def dec(i):
+        r = reps[i % len(reps)]
+        w = r["w"]
+        pk.paged_attention_decode(r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"],
+                                  w.scale, split=split)
+    return round(back_to_back_ms(torch, dec, n), 5)
+
+
+def measure_gather(torch, pk, rec_call_ms, r, tdt) -> dict:
+    w = r["w"]
+    max_len = w.max_len
+    out = {}
+    stream = torch.cuda.current_stream()
+    outs = (torch.empty(w.S, max_len, w.Hkv, w.D, dtype=tdt, device="cuda"),
+            torch.empty(w.S, max_len, w.Hkv, w.D, dtype=tdt, device="cuda"),
+            torch.empty(w.S, max_len, dtype=torch.uint8, device="cuda"))
+    gev = [_events(torch) for _ in range(5)]
+    pk.paged_kv_gather(r["pool"], w.layer, r["tables"], r["lens"], max_len, out=outs)
+    for a, b in gev:
+        a.record(stream)
+        pk.paged_kv_gather(r["pool"], w.layer, r["tables"], r["lens"], max_len, out=outs)
+        b.record(stream)
+    torch.cuda.synchronize()
+    gms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
+    gb = gather_bytes(w, max_len)
+    out["gather"] = {"ms": round(gms, 4), "bytes": gb, "GB_per_s": round(gb / (gms * 1e-3) / 1e9, 1)}
+    if w.dtype != "f32":
+        # the rest of the gather-then-attend path: dense decode over the
+        # padded batch (every max_len row, padding included)
+        dout = torch.empty_like(r["q"])
+        pk.dense_attention_decode(dout, r["q"], outs[0], outs[1], outs[2], w.scale)
+        for a, b in gev:
+            a.record(stream)
+            pk.dense_attention_decode(dout, r["q"], outs[0], outs[1], outs[2], w.scale)
+            b.record(stream)
+        torch.cuda.synchronize()
+        dms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
+        e = 2
+        db = 2 * w.S * max_len * w.Hkv * w.D * e + w.S * max_len + 2 * w.S * w.Hq * w.D * e
+        out["gather_then_dense"] = {
+            "dense_ms": round(dms, 4), "dense_bytes": db,
+            "dense_GB_per_s": round(db / (dms * 1e-3) / 1e9, 1),
+            "total_ms": round(gms + dms, 4), "total_bytes": gb + db,
+            "paged_step_ms": round(rec_call_ms, 4),
+            "total_over_paged": round((gms + dms) / rec_call_ms, 2),
+        }
+    del outs
+    return out
+
+
+PROBE_LIB = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "libpagedkv_probe.so")
+
+
+def read_ceiling(torch, buffer_gib: int = 4) -> dict:
+    """HBM read ceiling of this GPU from the committed probe kernel
+    (include/pagedkv_probe.h): a 4 GiB buffer (16x the Infinity Cache) read
+    as 1 MiB slabs in order and as 4/8/32/64 KiB slabs in a random order,
+    at 256..2048 workgroups; the best rate of each pattern, in GB/s."""
+    import ctypes
+    lib = ctypes.CDLL(PROBE_LIB)
+    fn = lib.pagedkv_read_probe
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = buffer_gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(1)
+    stream = torch.cuda.current_stream()
+    grids = (256, 512, 1024, 2048)
+    sink = torch.empty(max(grids) * 256, dtype=torch.int32, device="cuda")
+    gen = torch.Generator(device="cpu").manual_seed(5)
+    res = {"unit": "GB/s", "buffer_GiB": buffer_gib, "kernel": "pagedkv_read_probe"}
+    best_wg = {}
+    for label, slab, order in (("sequential_1MiB", 1 << 20, "seq"), ("random_4KiB", 4 << 10, "rand"),
+                               ("random_8KiB", 8 << 10, "rand"), ("random_32KiB", 32 << 10, "rand"),
+                               ("random_64KiB", 64 << 10, "rand")):
+        n = nbytes // slab
+        ids = (torch.arange(n, dtype=torch.int32) if order == "seq"
+               else torch.randperm(n, generator=gen).to(torch.int32)).cuda()
+        best, best_g = 0.0, None
+        for g in grids:
+            def run(_i, g=g):
+                rc = fn(buf.data_ptr(), nbytes, ids.data_ptr(), n, slab, g, sink.data_ptr(),
+                        stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"pagedkv_read_probe returned {rc}")
+            ms = back_to_back_ms(torch, run, 5)
+            gbs = n * slab / (ms * 1e-3) / 1e9
+            if gbs > best:
+                best, best_g = gbs, g
+        res[label] = round(best, 1)
+        best_wg[label] = best_g
+        del ids
+    res["best_workgroups"] = best_wg
+    del buf, sink
+    return res
+
+
+def _ceiling_for(ceiling: dict, w) -> tuple:
+    """The random-slab ceiling whose slab matches the contiguous bytes of one
+    block's K (or V) part in the attended layer: block_size x kv_heads x
+    head_dim elements."""
+    e = 4 if w.dtype == "f32" else 2
+    run = w.BS * w.Hkv * w.D * e
+    best = None
+    for kib in (4, 8, 32, 64):
+        if kib << 10 <= run:
+            best = kib
+    if best is None:
+        best = 4
+    key = f"random_{best}KiB"
+    return key, ceiling.get(key)
+
+
+def render_table(path: str) -> str:
+    """Markdown results table from a record written by --results-out."""
+    with open(path) as f:
+        rec = json.load(f)
+    rows = ["| Workload | Step (wall clock) | Call back to back | Step GB/s | % of 8 TB/s "
+            "(step / call) | Split | tokens/s (one layer) |",
+            "|---|---|---|---|---|---|---|"]
+    for name, r in rec["workloads"].items():
+        frac_call = r["roofline"]["frac"] * 100
+        rows.append(f"| {name} | {r['ms_per_step'] * 1e3:.1f} µs | {r['call_ms'] * 1e3:.1f} µs | "
+                    f"{r['value']:.0f} | {r['pct_of_peak']:.1f}% / {frac_call:.1f}% | "
+                    f"{r['split_used']} | {r['tokens_per_s']:.2g} |")
+    return "\n".join(rows)
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="llama8b_decode_bf16", choices=sorted(WORKLOADS))
+    ap.add_argument("--extra", default="long_context_bf16,churned_pool_bf16_gqa7",
+                    help="comma-separated workloads also measured (sub-records), or 'none'")
+    ap.add_argument("--extra-steps", type=int, default=100)
     ap.add_argument("--rotate", type=int, default=0, help="input replicas (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gather", action="store_true")
     ap.add_argument("--no-appends", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true")
     ap.add_argument("--cpu-budget-tokens", type=int, default=0)
     ap.add_argument("--split", choices=("auto", "chunks"), default="auto",
                     help="decode work split: auto (per-pair workgroups for small batches) or "
-                         "chunks (always the persistent chunk split and merge kernel)")
+                         "chunks (always the persistent chunk split)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="also run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="measure every workload (a record per workload) and nothing else")
+    ap.add_argument("--results-out", default=None, help="with --all-workloads: write the record")
+    ap.add_argument("--render", default=None, metavar="RECORD",
+                    help="print the markdown results table of a --results-out record and exit")
     args = ap.parse_args(argv)
 
+    if args.render:
+        print(render_table(args.render))
+        return 0
     if args.gpus != 1:
         print(f"bench.py: this path runs on one GPU only; --gpus {args.gpus} is not supported",
               file=sys.stderr, flush=True)
@@ -307,242 +679,107 @@ def main(argv=None) -> int:
 
     sys.path.insert(0, ROOT)
     import paged_kv_cache_resolve_amd as pk
-    from workloads import make_workload
-    pk.set_split_mode(pk.SPLIT_AUTO if args.split == "auto" else pk.SPLIT_CHUNKS)
 
-    idx = WORKLOADS[args.workload]
-    w0 = make_workload(idx)
-    kvb = decode_bytes(w0)
-    reps = args.rotate or max(1, min(4, math.ceil(4 * MALL_BYTES / max(kvb, 1))))
-    ws = [w0] + [make_workload(idx, seed_offset=r) for r in range(1, reps)]
-    print(f"[bench] workload {args.workload}: S={w0.S} Hq={w0.Hq} Hkv={w0.Hkv} D={w0.D} "
-          f"BS={w0.BS} sum(T)={int(w0.context_lens.sum())} replicas={reps}", file=sys.stderr,
-          flush=True)
+    if args.all_workloads:
+        out = {"workloads": {}, "steps": args.steps, "warmup": args.warmup, "split": args.split,
+               "device": torch.cuda.get_device_name(0)}
+        for name in sorted(WORKLOADS, key=WORKLOADS.get):
+            rec, reps = measure_step(torch, pk, name, args.steps, args.warmup, args.split,
+                                     args.rotate, graph=False)
+            if name == "churned_pool_bf16_gqa7":
+                rec["append_only"] = measure_append_only(torch, pk, reps)
+            rec["decode_only_call_ms"] = measure_decode_only(torch, pk, reps, args.split)
+            out["workloads"][name] = rec
+            print(f"[bench] {name}: {rec['ms_per_step'] * 1e3:.1f} us/step, "
+                  f"{rec['pct_of_peak']:.1f}% of 8 TB/s", file=sys.stderr, flush=True)
+            del reps
+            torch.cuda.empty_cache()
+        if not args.no_read_ceiling:
+            out["read_ceiling"] = read_ceiling(torch)
+        text = json.dumps(out)
+        if args.results_out:
+            with open(args.results_out, "w") as f:
+                f.write(json.dumps(out, indent=1) + "\n")
+        print(text, flush=True)
+        return 0
 
-    tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}[w0.dtype]
-
-    def dev(x):
-        if w0.dtype in ("f32", "f16"):
-            return torch.from_numpy(np.ascontiguousarray(x)).cuda()
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
-
-    reps_dev = []
-    for w in ws:
-        pool = pk.KVPool(w.NB, w.BS, w.L, w.Hkv, w.D, tdt, data=dev(w.pool))
-        reps_dev.append(dict(
-            w=w, pool=pool, tables=torch.from_numpy(w.block_tables).cuda(),
-            lens=torch.from_numpy(w.context_lens).cuda(),
-            pos=torch.from_numpy(w.positions).cuda(), q=dev(w.q), k=dev(w.k_new), v=dev(w.v_new),
-            out=torch.empty(w.S, w.Hq, w.D, dtype=tdt, device="cuda")))
-        r = reps_dev[-1]
-        # the step's buffers are fixed, so a plan checks them once
-        r["plan"] = pk.DecodePlan(r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"],
-                                  w.scale, r["k"], r["v"], r["pos"])
-    stream = torch.cuda.current_stream()
-
-    def step(i):
-        reps_dev[i % len(reps_dev)]["plan"].run()
-
-    def ev_pair():
-        return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-
-    # Timed region: exactly `steps` steps, nothing else enqueued in between.
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = ev_pair()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
-
-    # The same call back to back on the same stream, bracketed by one event
-    # pair: the average call duration used for the roofline.
-    n_dec = max(args.steps, 100)
-    torch.cuda.synchronize()
-    d0, d1 = ev_pair()
-    d0.record(stream)
-    for i in range(n_dec):
-        step(i)
-    d1.record(stream)
-    torch.cuda.synchronize()
-    dec_avg_ms = d0.elapsed_time(d1) / n_dec
-    # Per-call distribution (an event pair per call adds its own gaps, so
-    # these read slightly high).
-    ev = [ev_pair() for _ in range(n_dec)]
-    for i in range(n_dec):
-        ev[i][0].record(stream)
-        step(i)
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    dec_ms = [a.elapsed_time(b) for a, b in ev]
-
-    # The same step replayed from a HIP graph: 32 consecutive steps (what one
-    # iteration of a 32-layer model enqueues) captured once, replayed.  Each
-    # plan gets its own workspace, since a capture uses its own stream.
-    graph_ms = None
-    try:
-        gplans = []
-        for r in reps_dev:
-            w = r["w"]
-            wsb = pk.paged_attention_workspace_bytes(r["pool"], w.S, w.Hq)
-            gplans.append(pk.DecodePlan(
-                r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"], w.scale,
-                r["k"], r["v"], r["pos"],
-                workspace=torch.empty(wsb, dtype=torch.uint8, device="cuda")))
-        n_graph = 32
-
-        def graph_body():
-            for i in range(n_graph):
-                gplans[i % len(gplans)].run()
-
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            graph_body()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            graph_body()
-        graph.replay()
-        torch.cuda.synchronize()
-        g0, g1 = ev_pair()
-        g0.record(stream)
-        for _ in range(5):
-            graph.replay()
-        g1.record(stream)
-        torch.cuda.synchronize()
-        graph_ms = g0.elapsed_time(g1) / (5 * n_graph)
-        del graph, gplans
-    except RuntimeError as exc:   # capture unavailable: report it, keep the rest
-        print(f"[bench] graph replay skipped: {exc}", file=sys.stderr, flush=True)
-
-    # Which pass-1 form the call took: the chunk split's pass 1 writes the
-    # per-sequence chunk prefix at the start of the workspace, the per-pair
-    # kernel leaves it untouched.  (One more step on replica 0: it appends the
-    # same rows again, which leaves the pool as it was.)
-    r0 = reps_dev[0]
-    probe = torch.full((pk.paged_attention_workspace_bytes(r0["pool"], w0.S, w0.Hq),), 0xA5,
-                       dtype=torch.uint8, device="cuda")
-    pk.paged_attention_decode_append(r0["out"], r0["q"], r0["pool"], w0.layer, r0["tables"],
-                                     r0["lens"], w0.scale, r0["k"], r0["v"], r0["pos"],
-                                     workspace=probe)
-    torch.cuda.synchronize()
-    split_used = "chunks" if bool((probe[: 4 * (w0.S + 1)] != 0xA5).any().item()) else "pairs"
-    del probe
-
-    step_bytes = np.mean([decode_bytes(r["w"]) + append_bytes(r["w"]) for r in reps_dev])
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = step_bytes / (dec_avg_ms * 1e-3) / 1e9
-    tokens_per_s = w0.S / (ms_per_step * 1e-3)
-
+    rec, reps = measure_step(torch, pk, args.workload, args.steps, args.warmup, args.split,
+                             args.rotate)
+    w0 = reps[0]["w"]
+    tdt = getattr(torch, TORCH_DTYPES[w0.dtype])
     result = {
-        "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s at batch\u00d7context",
-        "value": round(value, 2),
+        "metric": "decode-attn effective HBM GB/s (% of peak) + tokens/s at batch×context",
+        "value": rec["value"],
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": rec["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w0.dtype,
         "data": "synthetic (seeded N(0,1) K/V/q, seeded context lengths and block tables)",
-        "config": {
-            "workload": args.workload,
-            "batch": w0.S, "q_heads": w0.Hq, "kv_heads": w0.Hkv, "head_dim": w0.D,
-            "block_size": w0.BS, "layers_in_pool": w0.L, "layer": w0.layer,
-            "sum_context_tokens": int(w0.context_lens.sum()),
-            "max_context": int(w0.context_lens.max()),
-            "input_replicas": reps,
-            "split": args.split,
-            "parallelism": "single GPU",
-        },
-        "pct_of_peak": round(100 * value / HBM_PEAK_GBS, 2),
-        "tokens_per_s": round(tokens_per_s, 1),
-        "gpu_ms_per_step": round(gpu_ms_per_step, 5),
-        "call_ms": round(dec_avg_ms, 5),
-        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
-        "calls_timed": n_dec,
-        "call_ms_per_call_events_p10_p50_p90": [
-            round(float(np.percentile(dec_ms, q)), 5) for q in (10, 50, 90)],
-        "split_used": split_used,
-        "roofline": {
-            "kernel": ("paged_attention_decode_append (decode pass 1 reading the new rows, "
-                       "then the split merge that also stores them)") if split_used == "chunks" else
-                      ("paged_attention_decode_append (one kernel: per-pair pass 1, the merge of "
-                       "its pieces and the row store in the same workgroup)"),
-            "bound": "hbm",
-            "achieved": round(achieved, 2),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(args.workload),
-            "algorithmic_bytes_per_launch": int(step_bytes),
-        },
+        "config": rec["config"],
     }
+    for key in ("pct_of_peak", "tokens_per_s", "gpu_ms_per_step", "call_ms", "graph_ms_per_step",
+                "calls_timed", "call_ms_per_call_events_p10_p50_p90", "split_used", "roofline"):
+        result[key] = rec[key]
 
     if not args.no_gather:
-        r = reps_dev[0]
-        w = r["w"]
-        max_len = w.max_len
         try:
-            outs = (torch.empty(w.S, max_len, w.Hkv, w.D, dtype=tdt, device="cuda"),
-                    torch.empty(w.S, max_len, w.Hkv, w.D, dtype=tdt, device="cuda"),
-                    torch.empty(w.S, max_len, dtype=torch.uint8, device="cuda"))
-            gev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                   for _ in range(5)]
-            pk.paged_kv_gather(r["pool"], w.layer, r["tables"], r["lens"], max_len, out=outs)
-            for a, b in gev:
-                a.record(stream)
-                pk.paged_kv_gather(r["pool"], w.layer, r["tables"], r["lens"], max_len, out=outs)
-                b.record(stream)
-            torch.cuda.synchronize()
-            gms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
-            gb = gather_bytes(w, max_len)
-            result["gather"] = {"ms": round(gms, 4), "bytes": gb,
-                                "GB_per_s": round(gb / (gms * 1e-3) / 1e9, 1)}
-            if w.dtype != "f32":
-                # the rest of the gather-then-attend path: dense decode over
-                # the padded batch (every max_len row, padding included)
-                dout = torch.empty_like(r["q"])
-                pk.dense_attention_decode(dout, r["q"], outs[0], outs[1], outs[2], w.scale)
-                for a, b in gev:
-                    a.record(stream)
-                    pk.dense_attention_decode(dout, r["q"], outs[0], outs[1], outs[2], w.scale)
-                    b.record(stream)
-                torch.cuda.synchronize()
-                dms = float(np.mean([a.elapsed_time(b) for a, b in gev]))
-                e = 2
-                db = (2 * w.S * max_len * w.Hkv * w.D * e + w.S * max_len
-                      + 2 * w.S * w.Hq * w.D * e)
-                result["gather_then_dense"] = {
-                    "dense_ms": round(dms, 4), "dense_bytes": db,
-                    "dense_GB_per_s": round(db / (dms * 1e-3) / 1e9, 1),
-                    "total_ms": round(gms + dms, 4),
-                    "total_bytes": gb + db,
-                    "paged_step_ms": round(dec_avg_ms, 4),
-                    "total_over_paged": round((gms + dms) / dec_avg_ms, 2),
-                }
-            del outs
+            result.update(measure_gather(torch, pk, rec["call_ms"], reps[0], tdt))
         except torch.cuda.OutOfMemoryError:
             result["gather"] = None
+    del reps
+    torch.cuda.empty_cache()
+
+    extras = [] if args.extra in ("", "none") else [x for x in args.extra.split(",") if x]
+    subs = {}
+    for name in extras:
+        if name == args.workload:
+            continue
+        if name not in WORKLOADS:
+            raise SystemExit(f"unknown workload {name}")
+        sub, sreps = measure_step(torch, pk, name, args.extra_steps, args.warmup, args.split,
+                                  args.rotate, graph=False)
+        sub.pop("dtype", None)
+        if name == "churned_pool_bf16_gqa7":
+            sub["append_only"] = measure_append_only(torch, pk, sreps)
+            sub["decode_only_call_ms"] = measure_decode_only(torch, pk, sreps, args.split)
+        subs[name] = sub
+        del sreps
+        torch.cuda.empty_cache()
+    if subs:
+        result["workloads"] = subs
 
     if not args.no_appends:
         try:
             result["appends"] = measure_appends(torch, pk)
         except torch.cuda.OutOfMemoryError:
             result["appends"] = None
+        from workloads import make_workload
+        result["host_block_manager"] = measure_manager(torch, pk, make_workload(
+            WORKLOADS[args.workload], with_pool=False))
 
-    if not args.no_appends:
-        result["host_block_manager"] = measure_manager(torch, pk, w0)
+    if not args.no_read_ceiling:
+        try:
+            ceiling = read_ceiling(torch)
+            result["roofline"]["read_ceiling"] = ceiling
+            key, val = _ceiling_for(ceiling, w0)
+            if val:
+                result["roofline"]["frac_of_read_ceiling"] = {
+                    "pattern": key, "frac": round(result["roofline"]["achieved"] / val, 4)}
+            for name, sub in subs.items():
+                from workloads import make_workload
+                wk = make_workload(WORKLOADS[name], with_pool=False)
+                key, val = _ceiling_for(ceiling, wk)
+                if val:
+                    sub["roofline"]["frac_of_read_ceiling"] = {
+                        "pattern": key, "frac": round(sub["roofline"]["achieved"] / val, 4)}
+        except (OSError, RuntimeError, torch.cuda.OutOfMemoryError) as exc:
+            result["roofline"]["read_ceiling"] = None
+            print(f"[bench] read ceiling skipped: {exc}", file=sys.stderr, flush=True)
 
     if args.copy_calibration:
         n = args.copy_calibration << 20

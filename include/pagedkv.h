@@ -273,7 +273,8 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * resident at once and the longest sequence the block tables allow,
  * max_blocks_per_seq * block_size tokens, holds at most 256 KiB of K and V
  * per KV head (1024 tokens at head_dim 64 in bf16 or fp16, 512 at 128; 512
- * and 256 in fp32); see paged_attention_set_split_mode.
+ * and 256 in fp32); flags = PAGEDKV_DECODE_CHUNKS keeps every call on the
+ * chunk split (below).
  * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
  * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and 256 and
  * for block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4
@@ -289,7 +290,7 @@ int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool,
                            int max_blocks_per_seq, const int32_t* context_lens,
                            int batch, int num_q_heads, float scale,
                            void* workspace, size_t workspace_bytes,
-                           void* stream);
+                           unsigned flags, void* stream);
 
 /* One decode step: append each sequence's new token, then decode
  * ([kv-cache] section 2: generation fills the tail block one token at a
@@ -313,23 +314,17 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new,
                                   int max_blocks_per_seq,
                                   const int32_t* context_lens, int batch,
                                   int num_q_heads, float scale, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+                                  size_t workspace_bytes, unsigned flags, void* stream);
 
-/* Work split of paged_attention_decode and paged_attention_decode_append
- * (process-wide; the results of both splits agree within the decode
- * tolerances but not bit for bit, since the softmax sums are taken in a
- * different order).
- *   PAGEDKV_SPLIT_AUTO   : per-pair workgroups where the shape allows (see
- *                          paged_attention_decode), else the chunk split.
- *   PAGEDKV_SPLIT_CHUNKS : always the persistent chunk split and, where a
- *                          sequence is split, the merge kernel.
- * Returns the previous mode, or PAGEDKV_ERR_INVALID_ARG for any other value.
- * The mode is read when a call is enqueued; changing it while another host
- * thread enqueues a decode is allowed but leaves which split that call uses
- * unspecified.  For tests and measurements of either split. */
-#define PAGEDKV_SPLIT_AUTO 0
-#define PAGEDKV_SPLIT_CHUNKS 1
-int paged_attention_set_split_mode(int mode);
+/* Flags of paged_attention_decode and paged_attention_decode_append, per
+ * call; any other bit set is PAGEDKV_ERR_INVALID_ARG.
+ *   0                     : per-pair workgroups where the shape allows (see
+ *                           paged_attention_decode), else the chunk split.
+ *   PAGEDKV_DECODE_CHUNKS : always the persistent chunk split.
+ * The two splits agree within the decode tolerances but not bit for bit,
+ * since the softmax sums are taken in a different order.  Each split is
+ * deterministic: the same inputs and flags give the same bits. */
+#define PAGEDKV_DECODE_CHUNKS 1u
 
 /* Bytes of device workspace dense_attention_decode needs (0 for invalid
  * arguments). */

@@ -74,7 +74,7 @@ class BlockManagerModel:
         seqs, counts = list(seqs), list(counts)
         need = self._check_step(seqs, counts)
         if need > len(self.stack):
-            raise OutOfBlocks("Out of KV-Cache Physical Blocks")
+            raise OutOfBlocks("no free block left in the pool")
         starts = []
         for s, c in zip(seqs, counts):
             while len(self.tables[s]) < self.blocks_for(self.lens[s] + c):

@@ -367,7 +367,7 @@ class FreeBlockStack:
 
     def allocate(self) -> int:
         if self._top == 0:
-            raise OutOfBlocks("Out of KV-Cache Physical Blocks")
+            raise OutOfBlocks("no free block left in the pool")
         self._top -= 1
         return int(self._stack[self._top])
 

@@ -21,6 +21,7 @@ streams.
 from __future__ import annotations
 
 import ctypes
+import threading
 
 import numpy as np
 import torch
@@ -28,35 +29,53 @@ import torch
 from . import _lib
 from ._lib import OutOfBlocksError, PagedKVError  # noqa: F401
 
-_L = _lib.load()
+# The library is loaded on first use (so that the build module imports on a
+# tree where it has not been built yet); a missing library raises there.
+_L = _lib.LazyLib()
 
 __all__ = [
     "KVPool", "kv_pool_create", "BlockManager", "kv_append", "kv_append_layers", "kv_append_tokens",
     "paged_kv_gather", "paged_attention_decode",
     "paged_attention_decode_append", "DecodePlan", "dense_attention_decode",
     "paged_attention_workspace_bytes", "paged_kv_resolve", "validate_decode_inputs",
-    "set_split_mode", "split_mode", "SPLIT_AUTO", "SPLIT_CHUNKS",
+    "split_mode", "SPLIT_AUTO", "SPLIT_CHUNKS",
     "PagedKVError", "OutOfBlocksError",
     "library",
 ]
 
-SPLIT_AUTO = _lib.SPLIT_AUTO      # per-pair workgroups for small batches, else the chunk split
-SPLIT_CHUNKS = _lib.SPLIT_CHUNKS  # always the persistent chunk split (+ merge kernel)
+# decode work split, passed to the library as per-call flags
+SPLIT_AUTO = 0                      # per-pair workgroups for small batches, else the chunk split
+SPLIT_CHUNKS = _lib.DECODE_CHUNKS   # always the persistent chunk split
 
 _DTYPES = {torch.float32: _lib.F32, torch.bfloat16: _lib.BF16, torch.float16: _lib.F16}
 
 
 def library() -> ctypes.CDLL:
-    """The loaded libpagedkv.so."""
-    return _L
+    """The loaded libpagedkv.so (loads it if needed)."""
+    return _lib.lib()
 
 
 def _check(status: int, what: str) -> None:
     if status == _lib.OK:
         return
     if status == _lib.ERR_OUT_OF_BLOCKS:
-        raise OutOfBlocksError(status, what, _L)
-    raise PagedKVError(status, what, _L)
+        raise OutOfBlocksError(status, what)
+    raise PagedKVError(status, what)
+
+
+_split_default = threading.local()
+
+
+def _split_flags(split) -> int:
+    """Decode flags for `split` (SPLIT_AUTO, SPLIT_CHUNKS, "auto", "chunks";
+    None = this thread's default, set by the split_mode context manager)."""
+    if split is None:
+        return getattr(_split_default, "flags", SPLIT_AUTO)
+    if split in ("auto", SPLIT_AUTO):
+        return SPLIT_AUTO
+    if split in ("chunks", SPLIT_CHUNKS):
+        return SPLIT_CHUNKS
+    raise ValueError(f"unknown split {split!r}")
 
 
 # The checks below run on every call, so they use the cheapest tensor
@@ -327,19 +346,12 @@ def paged_kv_gather(pool: KVPool, layer: int, block_tables: torch.Tensor,
     return k, v, mask
 
 
-_WS_BYTES: dict = {}
-
-
 def paged_attention_workspace_bytes(pool: KVPool, batch: int, num_q_heads: int) -> int:
-    # keyed on what the size depends on, not on the pool handle: a destroyed
-    # pool's address can come back for a pool of another shape
-    key = (pool.kv_heads, pool.head_dim, batch, num_q_heads)
-    n = _WS_BYTES.get(key)
-    if n is None:
-        n = _L.paged_attention_workspace_bytes(pool.handle, batch, num_q_heads)
-        if n == 0 and batch >= 0:
-            raise PagedKVError(_lib.ERR_INVALID_ARG, "paged_attention_workspace_bytes", _L)
-        _WS_BYTES[key] = n
+    """Device workspace bytes of a decode of this shape (the library's own
+    query: the size depends on the pool's dtype, block size and head shape)."""
+    n = _L.paged_attention_workspace_bytes(pool.handle, batch, num_q_heads)
+    if n == 0 and batch >= 0:
+        raise PagedKVError(_lib.ERR_INVALID_ARG, "paged_attention_workspace_bytes")
     return n
 
 
@@ -350,7 +362,7 @@ def _workspace(device: torch.device, nbytes: int, stream: int) -> torch.Tensor:
     key = (device.index, stream)
     ws = _WORKSPACES.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
+        ws = torch.zeros(max(nbytes, 1 << 20), dtype=torch.uint8, device=device)
         _WORKSPACES[key] = ws
     return ws
 
@@ -375,15 +387,17 @@ def _decode_args(out, q, pool, block_tables, context_lens, workspace):
 
 def paged_attention_decode(out: torch.Tensor, q: torch.Tensor, pool: KVPool, layer: int,
                            block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
-                           workspace: torch.Tensor | None = None) -> torch.Tensor:
+                           workspace: torch.Tensor | None = None, split=None) -> torch.Tensor:
     """out[b, h] = softmax_t(scale * q[b, h] . K_t) V_t over the T_b cached
     tokens of sequence b, resolved through its block table.  q and out are
     [batch, num_q_heads, head_dim] in the pool dtype.  A workspace is taken
-    from a per-stream cache unless one is given."""
+    from a per-stream cache unless one is given.  `split`: SPLIT_AUTO or
+    SPLIT_CHUNKS (None = the thread's default, see split_mode)."""
     batch, hq, qp, op, tp, mb, lp, wp, wn, stream = _decode_args(out, q, pool, block_tables,
                                                                  context_lens, workspace)
     _check(_L.paged_attention_decode(op, qp, pool.handle, layer, tp, mb, lp, batch, hq, scale,
-                                     wp, wn, stream), "paged_attention_decode")
+                                     wp, wn, _split_flags(split), stream),
+           "paged_attention_decode")
     return out
 
 
@@ -391,7 +405,8 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, pool: KVPo
                                   block_tables: torch.Tensor, context_lens: torch.Tensor,
                                   scale: float, k_new: torch.Tensor, v_new: torch.Tensor,
                                   positions: torch.Tensor,
-                                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+                                  workspace: torch.Tensor | None = None,
+                                  split=None) -> torch.Tensor:
     """kv_append(pool, layer, k_new, v_new, block_tables, positions) followed
     by paged_attention_decode(out, q, ...), as one library call (the decode
     kernel reads the new rows from k_new / v_new where it can, saving the
@@ -403,7 +418,8 @@ def paged_attention_decode_append(out: torch.Tensor, q: torch.Tensor, pool: KVPo
     vp = _dev_tensor(v_new, "v_new", pool.device, pool.dtype, shape)
     pp = _dev_tensor(positions, "positions", pool.device, torch.int32, (batch,))
     _check(_L.paged_attention_decode_append(op, qp, kp, vp, pp, pool.handle, layer, tp, mb, lp,
-                                            batch, hq, scale, wp, wn, stream),
+                                            batch, hq, scale, wp, wn, _split_flags(split),
+                                            stream),
            "paged_attention_decode_append")
     return out
 
@@ -419,7 +435,8 @@ class DecodePlan:
     def __init__(self, out: torch.Tensor, q: torch.Tensor, pool: KVPool, layer: int,
                  block_tables: torch.Tensor, context_lens: torch.Tensor, scale: float,
                  k_new: torch.Tensor | None = None, v_new: torch.Tensor | None = None,
-                 positions: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+                 positions: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 split=None):
         append = k_new is not None or v_new is not None or positions is not None
         if append and (k_new is None or v_new is None or positions is None):
             raise ValueError("k_new, v_new and positions go together")
@@ -438,11 +455,12 @@ class DecodePlan:
             pp = _dev_tensor(positions, "positions", pool.device, torch.int32, (batch,))
             self._fn = _L.paged_attention_decode_append
             self._args = (op, qp, kp, vp, pp, pool.handle, layer, tp, mb, lp, batch, hq,
-                          float(scale), wp, wn)
+                          float(scale), wp, wn, _split_flags(split))
             self._what = "paged_attention_decode_append"
         else:
             self._fn = _L.paged_attention_decode
-            self._args = (op, qp, pool.handle, layer, tp, mb, lp, batch, hq, float(scale), wp, wn)
+            self._args = (op, qp, pool.handle, layer, tp, mb, lp, batch, hq, float(scale), wp, wn,
+                          _split_flags(split))
             self._what = "paged_attention_decode"
 
     def run(self) -> torch.Tensor:
@@ -507,26 +525,21 @@ def paged_kv_resolve(block_tables: torch.Tensor, context_lens: torch.Tensor, blo
     return slots
 
 
-def set_split_mode(mode: int) -> int:
-    """Select the decode work split for the whole process (SPLIT_AUTO or
-    SPLIT_CHUNKS); returns the previous mode."""
-    prev = _L.paged_attention_set_split_mode(int(mode))
-    if prev < 0:
-        _check(prev, "paged_attention_set_split_mode")
-    return prev
-
-
 class split_mode:
-    """Context manager: run the enclosed decodes with the given split mode."""
+    """Context manager: decode calls made by this thread inside it that pass
+    no `split` use `mode` (SPLIT_AUTO or SPLIT_CHUNKS).  The setting is
+    per thread and lives in the binding only: the library takes the split as
+    a per-call flag, so other threads' calls are not affected."""
 
-    def __init__(self, mode: int):
-        self.mode = mode
+    def __init__(self, mode):
+        self.flags = _split_flags(mode)
         self.prev = None
 
     def __enter__(self):
-        self.prev = set_split_mode(self.mode)
+        self.prev = getattr(_split_default, "flags", SPLIT_AUTO)
+        _split_default.flags = self.flags
         return self
 
     def __exit__(self, *exc):
-        set_split_mode(self.prev)
+        _split_default.flags = self.prev
         return False

@@ -1,6 +1,8 @@
 """ctypes view of libpagedkv.so (the C ABI declared in include/pagedkv.h).
 
-Loading fails loudly: there is no fallback implementation.
+The library is loaded on first use (`lib()`), so that the package and its
+build module import on a tree where it has not been built yet.  Loading
+fails loudly: there is no fallback implementation.
 """
 
 from __future__ import annotations
@@ -21,8 +23,8 @@ F32 = 0
 BF16 = 1
 F16 = 2
 
-SPLIT_AUTO = 0
-SPLIT_CHUNKS = 1
+# flags of the decode calls
+DECODE_CHUNKS = 1
 
 _c_int = ctypes.c_int
 _c_size = ctypes.c_size_t
@@ -68,14 +70,13 @@ SIGNATURES = {
                                  _vp]),
     "paged_attention_workspace_bytes": (_c_size, [_vp, _c_int, _c_int]),
     "paged_attention_decode": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int, _c_int,
-                                        ctypes.c_float, _vp, _c_size, _vp]),
+                                        ctypes.c_float, _vp, _c_size, ctypes.c_uint, _vp]),
     "paged_attention_decode_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int,
                                                _vp, _c_int, _c_int, ctypes.c_float, _vp, _c_size,
-                                               _vp]),
+                                               ctypes.c_uint, _vp]),
     "dense_attention_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "dense_attention_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                         _c_int, _c_int, ctypes.c_float, _vp, _c_size, _vp]),
-    "paged_attention_set_split_mode": (_c_int, [_c_int]),
     "paged_kv_resolve": (_c_int, [_vp, _vp, _c_int, _vp, _c_int, _c_int, _c_int, _vp]),
     "pagedkv_status_string": (ctypes.c_char_p, [_c_int]),
 }
@@ -94,10 +95,29 @@ def load() -> ctypes.CDLL:
     return lib
 
 
+_LIB = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (loaded on the first call; raises ImportError if it
+    has not been built)."""
+    global _LIB
+    if _LIB is None:
+        _LIB = load()
+    return _LIB
+
+
+class LazyLib:
+    """Attribute access loads the library on first use, then forwards."""
+
+    def __getattr__(self, name):
+        return getattr(lib(), name)
+
+
 class PagedKVError(RuntimeError):
-    def __init__(self, status: int, what: str, lib: ctypes.CDLL):
+    def __init__(self, status: int, what: str, library=None):
         self.status = status
-        msg = lib.pagedkv_status_string(status).decode()
+        msg = (library or lib()).pagedkv_status_string(status).decode()
         super().__init__(f"{what}: {msg} (status {status})")
 
 

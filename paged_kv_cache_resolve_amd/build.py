@@ -3,7 +3,11 @@
     python -m paged_kv_cache_resolve_amd.build [-v]
 
 Objects go to paged_kv_cache_resolve_amd/_build/, the library to
-paged_kv_cache_resolve_amd/libpagedkv.so.  Every call recompiles.
+paged_kv_cache_resolve_amd/libpagedkv.so, and the HBM read-ceiling probe
+(a measurement helper with its own small ABI, include/pagedkv_probe.h) to
+paged_kv_cache_resolve_amd/libpagedkv_probe.so.  Every call recompiles.
+Importing the package does not load the library, so this module runs on a
+tree where it has not been built yet.
 """
 
 from __future__ import annotations
@@ -20,6 +24,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpagedkv.so")
+PROBE_LIB_PATH = os.path.join(HERE, "libpagedkv_probe.so")
+PROBE_SOURCES = ["probe/read_ceiling.hip"]
 
 SOURCES = [
     "api.cpp",
@@ -46,7 +52,7 @@ COMMON = [
 
 
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+    obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0].replace("/", "_") + ".o")
     cmd = [HIPCC, *COMMON, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -60,18 +66,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(min(len(SOURCES), 8)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str, verbose: bool) -> None:
+    tmp = path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+        raise RuntimeError(f"link of {os.path.basename(path)} failed:\n{r.stderr}")
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(min(len(srcs), 8)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB_PATH, verbose)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH, verbose)
     return LIB_PATH
 
 

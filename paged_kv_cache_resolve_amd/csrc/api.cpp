@@ -221,16 +221,16 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch, int num
 
 namespace {
 
-std::atomic<int> g_split_mode{PAGEDKV_SPLIT_AUTO};   // paged_attention_set_split_mode
-
 // Shared body of the decode entry points.  With k_new != nullptr the call
 // also appends each sequence's new token (the fused form).
 int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                 int batch, int num_q_heads, float scale, void* workspace, size_t workspace_bytes,
-                void* stream, const void* k_new, const void* v_new, const int32_t* positions) {
+                unsigned flags, void* stream, const void* k_new, const void* v_new,
+                const int32_t* positions) {
   if (!pool || batch < 0 || layer < 0 || layer >= pool->layers || max_blocks_per_seq < 1 ||
-      num_q_heads < 1 || num_q_heads % pool->kv_heads != 0 || !isfinite(scale))
+      num_q_heads < 1 || num_q_heads % pool->kv_heads != 0 || !isfinite(scale) ||
+      (flags & ~PAGEDKV_DECODE_CHUNKS) != 0)
     return PAGEDKV_ERR_INVALID_ARG;
   if (batch == 0) return PAGEDKV_OK;
   if (!out || !q || !block_tables || !context_lens) return PAGEDKV_ERR_INVALID_ARG;
@@ -239,6 +239,11 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   if (!aligned16(out) || !aligned16(q) || (append && (!aligned16(k_new) || !aligned16(v_new))))
     return PAGEDKV_ERR_INVALID_ARG;
   if (batch > kMaxBatchLds) return PAGEDKV_ERR_UNSUPPORTED;
+  // The kernels keep chunk counts and their prefix sums in int32: the
+  // longest sequence the tables allow, cut into 16-token chunks (the
+  // smallest chunk of any kernel), times the batch must fit.
+  const int64_t max_tokens = (int64_t)max_blocks_per_seq * pool->block_size;
+  if ((int64_t)batch * ((max_tokens + 15) / 16) > INT32_MAX) return PAGEDKV_ERR_UNSUPPORTED;
   const HeadSplit hs = paged_split(pool, num_q_heads);
   const bool use_mfma = mfma_supported(pool, hs.group);
   if (!use_mfma && !generic_supported(pool, hs.group)) return PAGEDKV_ERR_UNSUPPORTED;
@@ -266,7 +271,7 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   p.scale_log2 = scale * 1.4426950408889634f;
   p.dtype = pool->dtype;
   p.min_chunks = 0;   // launcher default
-  p.pair_mode = use_mfma && g_split_mode.load(std::memory_order_relaxed) == PAGEDKV_SPLIT_AUTO;
+  p.pair_mode = use_mfma && (flags & PAGEDKV_DECODE_CHUNKS) == 0;
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   if (use_mfma) {
@@ -299,10 +304,11 @@ extern "C" {
 int paged_attention_decode(void* out, const void* q, const kv_pool_t* pool, int layer,
                            const int32_t* block_tables, int max_blocks_per_seq,
                            const int32_t* context_lens, int batch, int num_q_heads, float scale,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           void* workspace, size_t workspace_bytes, unsigned flags,
+                           void* stream) {
   return decode_call(out, q, pool, layer, block_tables, max_blocks_per_seq, context_lens, batch,
-                     num_q_heads, scale, workspace, workspace_bytes, stream, nullptr, nullptr,
-                     nullptr);
+                     num_q_heads, scale, workspace, workspace_bytes, flags, stream, nullptr,
+                     nullptr, nullptr);
 }
 
 int paged_attention_decode_append(void* out, const void* q, const void* k_new, const void* v_new,
@@ -310,16 +316,11 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
                                   const int32_t* block_tables, int max_blocks_per_seq,
                                   const int32_t* context_lens, int batch, int num_q_heads,
                                   float scale, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
+                                  unsigned flags, void* stream) {
   if (batch > 0 && (!k_new || !v_new || !positions)) return PAGEDKV_ERR_INVALID_ARG;
   return decode_call(out, q, pool, layer, block_tables, max_blocks_per_seq, context_lens, batch,
-                     num_q_heads, scale, workspace, workspace_bytes, stream, k_new, v_new,
+                     num_q_heads, scale, workspace, workspace_bytes, flags, stream, k_new, v_new,
                      positions);
-}
-
-int paged_attention_set_split_mode(int mode) {
-  if (mode != PAGEDKV_SPLIT_AUTO && mode != PAGEDKV_SPLIT_CHUNKS) return PAGEDKV_ERR_INVALID_ARG;
-  return g_split_mode.exchange(mode);
 }
 
 size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads, int head_dim) {
@@ -394,7 +395,7 @@ const char* pagedkv_status_string(int status) {
   switch (status) {
     case PAGEDKV_OK: return "ok";
     case PAGEDKV_ERR_INVALID_ARG: return "invalid argument";
-    case PAGEDKV_ERR_OUT_OF_BLOCKS: return "Out of KV-Cache Physical Blocks";
+    case PAGEDKV_ERR_OUT_OF_BLOCKS: return "no free block left in the pool";
     case PAGEDKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PAGEDKV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PAGEDKV_ERR_HIP: return "HIP runtime error";

@@ -161,9 +161,9 @@ hipError_t launch_resolve(int64_t* slots, const int32_t* tables, int mb,
 
 // Workgroups the device holds at once for kernel `fn` (cached per device).
 hipError_t resident_workgroups(const void* fn, int threads, size_t lds, int* out);
-// Decode pass-1 workgroups to launch: kDecodeWgPerCu per CU (the
-// PAGEDKV_DECODE_WG_PER_CU environment variable overrides it, for launch-shape
-// sweeps), never more than `resident`.
+// Decode pass-1 workgroups to launch: kDecodeWgPerCu per CU (a build with
+// -DPAGEDKV_LAUNCH_SWEEP takes the count from PAGEDKV_DECODE_WG_PER_CU, for
+// launch-shape sweeps), never more than `resident`.
 int decode_workgroups(int resident);
 // Compute units of the current device (0 if the runtime cannot tell).
 int device_cus();

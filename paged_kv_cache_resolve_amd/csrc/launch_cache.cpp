@@ -86,11 +86,18 @@ int device_cus() {
 }
 
 int decode_workgroups(int resident) {
+#ifdef PAGEDKV_LAUNCH_SWEEP
+  // Launch-shape sweeps only: a library built with -DPAGEDKV_LAUNCH_SWEEP
+  // reads the workgroups per CU from PAGEDKV_DECODE_WG_PER_CU.  The normal
+  // build has no such override.
   static const int per_cu = [] {
     const char* v = getenv("PAGEDKV_DECODE_WG_PER_CU");
     const int x = v ? atoi(v) : 0;
     return x > 0 ? x : kDecodeWgPerCu;
   }();
+#else
+  constexpr int per_cu = kDecodeWgPerCu;
+#endif
   const int cus = device_cus();
   if (cus <= 0) return resident;
   const int want = cus * per_cu;

@@ -62,7 +62,7 @@ int main() {
   kv_pool_t* pool = nullptr;
   kv_pool_create(&pool, 8, 16, 2, 2, 64, PAGEDKV_BF16, fake, kv_pool_bytes(8, 16, 2, 2, 64, PAGEDKV_BF16));
   if (kv_append(pool, 5, fake, fake, (int32_t*)fake, 4, (int32_t*)fake, 4, nullptr) != PAGEDKV_ERR_INVALID_ARG) ++fails;
-  if (paged_attention_decode(fake, fake, pool, 0, (int32_t*)fake, 4, (int32_t*)fake, 4, 7, 0.1f, fake, 1 << 20, nullptr) != PAGEDKV_ERR_INVALID_ARG) ++fails;
+  if (paged_attention_decode(fake, fake, pool, 0, (int32_t*)fake, 4, (int32_t*)fake, 4, 7, 0.1f, fake, 1 << 20, 0u, nullptr) != PAGEDKV_ERR_INVALID_ARG) ++fails;
   kv_pool_destroy(pool);
   printf("host checks done, %d failures\n", fails);
   return fails ? 3 : 0;

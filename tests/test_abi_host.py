@@ -31,24 +31,30 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 27, names
+    assert len(names) == 26, names
     for n in names:
         assert hasattr(L, n), f"{n} missing from libpagedkv.so"
     assert set(names) == set(_lib.SIGNATURES), "binding signatures drift from the header"
 
 
-def test_split_mode_setter():
-    """paged_attention_set_split_mode returns the previous mode and rejects
-    anything but the two declared modes (host only, nothing enqueued)."""
-    prev = L.paged_attention_set_split_mode(_lib.SPLIT_CHUNKS)
-    assert prev in (_lib.SPLIT_AUTO, _lib.SPLIT_CHUNKS)
-    try:
-        assert L.paged_attention_set_split_mode(_lib.SPLIT_AUTO) == _lib.SPLIT_CHUNKS
-        for bad in (-1, 2, 7):
-            assert L.paged_attention_set_split_mode(bad) == _lib.ERR_INVALID_ARG
-        assert L.paged_attention_set_split_mode(_lib.SPLIT_AUTO) == _lib.SPLIT_AUTO
-    finally:
-        L.paged_attention_set_split_mode(prev)
+def test_decode_flags_are_per_call():
+    """The decode split is a per-call flag: the only process-wide setter is
+    gone, and a flag bit the header does not define is an argument error
+    (host only, nothing enqueued)."""
+    assert not hasattr(L, "paged_attention_set_split_mode")
+    h = _pool(nb=8, layers=1, hkv=2, d=64)
+    p = FAKE_DEVICE_PTR
+    wsb = L.paged_attention_workspace_bytes(h, 4, 8)
+    for bad in (2, 4, 0x80000000, 3):
+        assert L.paged_attention_decode(p, p, h, 0, p, 4, p, 4, 8, ctypes.c_float(0.1), p, wsb,
+                                        bad, None) == _lib.ERR_INVALID_ARG
+        assert L.paged_attention_decode_append(p, p, p, p, p, h, 0, p, 4, p, 4, 8,
+                                               ctypes.c_float(0.1), p, wsb, bad,
+                                               None) == _lib.ERR_INVALID_ARG
+    for ok in (0, _lib.DECODE_CHUNKS):   # batch 0: validated, nothing to do
+        assert L.paged_attention_decode(p, p, h, 0, p, 4, p, 0, 8, ctypes.c_float(0.1), p, wsb,
+                                        ok, None) == 0
+    L.kv_pool_destroy(h)
 
 
 def _pool(nb=10, bs=16, layers=2, hkv=2, d=64, dtype=_lib.BF16):
@@ -126,7 +132,7 @@ def test_first_allocation_and_exhaustion():
         got.append(out.value)
     assert got == [2, 1, 0]
     assert L.kv_pool_alloc_block(h, ctypes.byref(out)) == _lib.ERR_OUT_OF_BLOCKS
-    assert L.pagedkv_status_string(_lib.ERR_OUT_OF_BLOCKS) == b"Out of KV-Cache Physical Blocks"
+    assert L.pagedkv_status_string(_lib.ERR_OUT_OF_BLOCKS) == b"no free block left in the pool"
     L.kv_pool_destroy(h)
 
 
@@ -152,7 +158,7 @@ def test_entry_points_validate_before_launch():
     dec = lambda **kw: L.paged_attention_decode(  # noqa: E731
         kw.get("out", p), kw.get("q", p), h, kw.get("layer", 0), p, kw.get("mb", 4), p,
         kw.get("batch", 4), kw.get("hq", 8), ctypes.c_float(kw.get("scale", 0.125)),
-        kw.get("ws", p), kw.get("wsb", ws_bytes), None)
+        kw.get("ws", p), kw.get("wsb", ws_bytes), kw.get("flags", 0), None)
     assert dec(layer=2) == _lib.ERR_INVALID_ARG
     assert dec(layer=-1) == _lib.ERR_INVALID_ARG
     assert dec(hq=6 + 1) == _lib.ERR_INVALID_ARG
@@ -168,7 +174,7 @@ def test_entry_points_validate_before_launch():
     assert dec(batch=0) == 0                                            # nothing to do
     fused = lambda **kw: L.paged_attention_decode_append(  # noqa: E731
         p, p, kw.get("k", p), kw.get("v", p), kw.get("pos", p), h, kw.get("layer", 0), p, 4, p,
-        kw.get("batch", 4), 8, ctypes.c_float(0.125), p, kw.get("wsb", ws_bytes), None)
+        kw.get("batch", 4), 8, ctypes.c_float(0.125), p, kw.get("wsb", ws_bytes), 0, None)
     assert fused(k=None) == _lib.ERR_INVALID_ARG
     assert fused(v=None) == _lib.ERR_INVALID_ARG
     assert fused(pos=None) == _lib.ERR_INVALID_ARG
@@ -271,19 +277,70 @@ def test_wide_groups_workspace(hkv, hq, d, bs, dtype, qsplit, share):
 
 
 def test_binding_workspace_size_follows_pool_shape():
-    """The binding's workspace-size cache must not outlive a pool: a new pool
-    of another shape that reuses a destroyed pool's handle address gets its
-    own size."""
+    """The binding asks the library for every workspace size: pools of the
+    same head shape but another dtype or block size split their query heads
+    differently (32 per wavefront only for 16-bit pools with blocks of a
+    multiple of 16 tokens), so their sizes differ, whichever was asked first.
+    A new pool that reuses a destroyed pool's handle address gets its own
+    size too."""
     import types
+    cases = [(1, 128, 16, _lib.F32), (1, 128, 16, _lib.BF16), (1, 64, 8, _lib.BF16),
+             (1, 64, 16, _lib.BF16), (8, 128, 16, _lib.BF16), (2, 64, 16, _lib.F16)]
     sizes = []
-    for hkv, d in [(8, 128), (1, 128), (2, 64)]:
-        h = _pool(nb=8, layers=1, hkv=hkv, d=d)
-        pool = types.SimpleNamespace(handle=h, kv_heads=hkv, head_dim=d)
+    for hkv, d, bs, dt in cases:
+        h = _pool(nb=8, bs=bs, layers=1, hkv=hkv, d=d, dtype=dt)
+        pool = types.SimpleNamespace(handle=h, kv_heads=hkv, head_dim=d, block_size=bs, dtype=dt)
         got = pk.paged_attention_workspace_bytes(pool, 300, 32)
         assert got == L.paged_attention_workspace_bytes(h, 300, 32)
         sizes.append(got)
         L.kv_pool_destroy(h)
-    assert len(set(sizes)) == 3
+    # fp32 and 8-token blocks: 16 query heads per virtual head; bf16 with 16-token blocks: 32
+    assert sizes[0] != sizes[1] and sizes[2] != sizes[3]
+
+
+def test_decode_refuses_chunk_counts_past_int32():
+    """The kernels keep per-sequence chunk counts and their prefix sums in
+    int32: a batch whose tables allow more than 2^31 - 1 chunks of 16 tokens
+    in total is refused before any launch."""
+    h = _pool(nb=8, bs=16, layers=1, hkv=2, d=64)
+    p = FAKE_DEVICE_PTR
+    batch = 16384
+    wsb = L.paged_attention_workspace_bytes(h, batch, 8)
+    dec = lambda mb: L.paged_attention_decode(  # noqa: E731
+        p, p, h, 0, p, mb, p, batch, 8, ctypes.c_float(0.1), p, wsb, 0, None)
+    limit_mb = (2**31 - 1) // batch          # chunks per sequence that still fit
+    assert dec(limit_mb + 1) == _lib.ERR_UNSUPPORTED
+    assert dec(2**30) == _lib.ERR_UNSUPPORTED
+    fused = L.paged_attention_decode_append(p, p, p, p, p, h, 0, p, limit_mb + 1, p, batch, 8,
+                                            ctypes.c_float(0.1), p, wsb, 0, None)
+    assert fused == _lib.ERR_UNSUPPORTED
+    L.kv_pool_destroy(h)
+
+
+def test_build_module_runs_without_the_library(tmp_path):
+    """`python -m paged_kv_cache_resolve_amd.build` works on a checkout where
+    the library has not been built yet: importing the package does not load
+    it, and the build writes it.  Run on a copy of the sources."""
+    import shutil
+    import subprocess
+    import sys
+    pkg = os.path.join(ROOT, "paged_kv_cache_resolve_amd")
+    shutil.copytree(pkg, tmp_path / "paged_kv_cache_resolve_amd",
+                    ignore=shutil.ignore_patterns("*.so", "*.so.tmp*", "_build", "__pycache__"))
+    shutil.copytree(os.path.join(ROOT, "include"), tmp_path / "include")
+    assert not (tmp_path / "paged_kv_cache_resolve_amd" / "libpagedkv.so").exists()
+    env = dict(os.environ)
+    env.pop("PYTHONPATH", None)
+    probe = subprocess.run(
+        [sys.executable, "-c", "import paged_kv_cache_resolve_amd as pk\n"
+         "try:\n    pk.library()\nexcept ImportError as e:\n    print('missing:', e)\n"],
+        cwd=tmp_path, env=env, capture_output=True, text=True, timeout=300)
+    assert probe.returncode == 0, probe.stderr
+    assert "missing:" in probe.stdout and "paged_kv_cache_resolve_amd.build" in probe.stdout
+    r = subprocess.run([sys.executable, "-m", "paged_kv_cache_resolve_amd.build"], cwd=tmp_path,
+                       env=env, capture_output=True, text=True, timeout=900)
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert (tmp_path / "paged_kv_cache_resolve_amd" / "libpagedkv.so").exists()
 
 
 def test_binding_refuses_host_tensors():

@@ -19,7 +19,8 @@ import oracle
 import paged_kv_cache_resolve_amd as pk
 from workloads import make_workload
 
-from gpu_helpers import NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say
+from gpu_helpers import (NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, np_to_dev, say,
+                         workload_vmax)
 
 pytestmark = [
     pytest.mark.gpu,
@@ -80,7 +81,8 @@ def test_fused_step_named_workloads(idx, S, split):
     dw = DeviceWorkload(w)
     out = run_fused(dw, positions)
     ref_pool, ref = oracle_step(w, positions)
-    assert_attention_close(out, ref, w.dtype, what=f"fused w{idx}")
+    assert_attention_close(out, ref, w.dtype, what=f"fused w{idx}",
+                           vmax=workload_vmax(w, pool=ref_pool))
     assert dev_to_np(dw.pool.data).tobytes() == ref_pool.tobytes(), "pool differs from oracle append"
 
 
@@ -126,7 +128,8 @@ def test_fused_position_cases(dtype, Hq, Hkv, D, BS, split):
     fused = DeviceWorkload(w)
     out = run_fused(fused, positions)
     ref_pool, ref = oracle_step(w, positions)
-    assert_attention_close(out, ref, dtype, what="fused positions")
+    assert_attention_close(out, ref, dtype, what="fused positions",
+                           vmax=workload_vmax(w, pool=ref_pool))
     assert dev_to_np(fused.pool.data).tobytes() == ref_pool.tobytes()
     pos = torch.from_numpy(np.asarray(positions, np.int32)).cuda()
     pk.kv_append(two.pool, w.layer, two.k_new, two.v_new, two.tables, pos)
@@ -138,24 +141,22 @@ def test_fused_position_cases(dtype, Hq, Hkv, D, BS, split):
     assert not dev_to_np(out)[8].any(), "empty sequence must give a zero row"
 
 
-@pytest.mark.parametrize("idx", [2, 3])
+@pytest.mark.parametrize("idx", [2, 3, 4])
 def test_fused_step_full_size(idx):
-    """The benchmarked configurations (the Llama-shaped layer and the long
-    contexts) at full size, through the benchmarked call: sampled rows
-    checked, the whole pool bit-exact against the oracle's append."""
-    say(f"fused append+decode workload {idx} full size")
+    """The benchmarked configurations (the Llama-shaped layer, the long
+    contexts, the high-concurrency batch) at full size, through the
+    benchmarked call: every output row against the oracle, the whole pool
+    bit-exact against the oracle's append."""
+    say(f"fused append+decode workload {idx} full size, every row")
     w = make_workload(idx)
     positions = w.positions.copy()
     poison_append_slots(w, positions)
     dw = DeviceWorkload(w)
     out = run_fused(dw, positions)
     ref_pool = oracle.kv_append(w.pool, w.layer, w.block_tables, positions, w.k_new, w.v_new)
-    rng = np.random.default_rng(202)
-    seqs = sorted(set(rng.choice(w.S, size=min(12, w.S // 2), replace=False).tolist())
-                  | {int(np.argmax(w.context_lens)), int(np.argmin(w.context_lens))})
     ref = oracle.paged_attention_decode(ref_pool, w.dtype, w.layer, w.block_tables,
-                                        w.context_lens, w.q, w.scale, seqs=seqs)
-    assert_attention_close(out, ref, w.dtype, rows=seqs, what=f"fused w{idx} full")
+                                        w.context_lens, w.q, w.scale)
+    assert_attention_close(out, ref, w.dtype, what=f"fused w{idx} full")
     assert dev_to_np(dw.pool.data).tobytes() == ref_pool.tobytes()
     # a second step over the same inputs reads the appended rows from the pool
     # (now holding the same values), so the output must not change

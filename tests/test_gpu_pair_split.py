@@ -19,7 +19,7 @@ import oracle
 import paged_kv_cache_resolve_amd as pk
 from workloads import make_workload
 
-from gpu_helpers import NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, say
+from gpu_helpers import NAN_BITS, DeviceWorkload, assert_attention_close, dev_to_np, say, workload_vmax
 
 pytestmark = [
     pytest.mark.gpu,
@@ -46,15 +46,17 @@ def workload(dtype, Hq, Hkv, D, BS, lens, L=1, layer=0):
 
 
 def decode_with(dw, mode):
-    """Decode under `mode` with a sentinel-filled workspace; returns the
-    output and whether the chunk prefix was written (chunk split ran)."""
+    """Decode under `mode` with a fresh workspace whose chunk-prefix section
+    (its first bytes) holds a sentinel and the rest zeros (as a new
+    workspace must be); returns the output and whether the chunk prefix was
+    written (the chunk split ran)."""
     batch, hq = dw.q.shape[0], dw.q.shape[1]
     n = pk.paged_attention_workspace_bytes(dw.pool, batch, hq)
-    ws = torch.full((n,), SENTINEL, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros((n,), dtype=torch.uint8, device="cuda")
+    ws[: 4 * (batch + 1)] = SENTINEL
     out = torch.empty_like(dw.q)
-    with pk.split_mode(mode):
-        pk.paged_attention_decode(out, dw.q, dw.pool, dw.w.layer, dw.tables, dw.lens, dw.w.scale,
-                                  workspace=ws)
+    pk.paged_attention_decode(out, dw.q, dw.pool, dw.w.layer, dw.tables, dw.lens, dw.w.scale,
+                              workspace=ws, split=mode)
     torch.cuda.synchronize()
     prefix_written = bool((ws[: 4 * (batch + 1)] != SENTINEL).any().item())
     return out, prefix_written
@@ -113,8 +115,9 @@ def test_pair_split_matches_oracle_and_chunk_split(dtype, Hq, Hkv, D, BS):
     out_c, wrote_c = decode_with(dw, pk.SPLIT_CHUNKS)
     assert not wrote_p, "small batch did not take the per-pair split"
     assert wrote_c, "SPLIT_CHUNKS did not take the chunk split"
-    assert_attention_close(out_p, ref, dtype, what="per-pair split")
-    assert_attention_close(out_c, ref, dtype, what="chunk split")
+    vmax = workload_vmax(w)
+    assert_attention_close(out_p, ref, dtype, what="per-pair split", vmax=vmax)
+    assert_attention_close(out_c, ref, dtype, what="chunk split", vmax=vmax)
     zero_rows = [i for i, t in enumerate(lens) if t == 0]
     assert not dev_to_np(out_p)[zero_rows].any(), "empty sequences must give zero rows"
     # deterministic: the same call twice gives the same bits
@@ -142,7 +145,8 @@ def test_pair_split_length_limit(dtype, D, BS, extra, expect_pairs):
     dw = DeviceWorkload(w)
     out, wrote = decode_with(dw, pk.SPLIT_AUTO)
     assert wrote != expect_pairs
-    assert_attention_close(out, reference(w), dtype, what=f"limit {longest}")
+    assert_attention_close(out, reference(w), dtype, what=f"limit {longest}",
+                           vmax=workload_vmax(w))
 
 
 def test_pair_split_not_taken_for_many_pairs():
@@ -167,4 +171,5 @@ def test_pair_split_named_small_workloads():
         dw = DeviceWorkload(w)
         out, wrote = decode_with(dw, pk.SPLIT_AUTO)
         assert wrote != expect_pairs, f"workload {idx}: unexpected split"
-        assert_attention_close(out, reference(w), w.dtype, what=f"workload {idx}")
+        assert_attention_close(out, reference(w), w.dtype, what=f"workload {idx}",
+                               vmax=workload_vmax(w))

@@ -248,17 +248,21 @@ def _fill_pool(seed_seq: np.random.SeedSequence, nb, L, layer, hkv, bs, d, dtype
 
 
 def make_workload(index: int, *, with_pool: bool = True, seed_offset: int = 0,
-                  threads: int | None = None, **overrides) -> Workload:
-    """Build workload ``index`` (0..4).
+                  keep_lens: bool = False, threads: int | None = None, **overrides) -> Workload:
+    """Build workload ``index`` (0..9).
 
     ``overrides`` replaces spec entries (e.g. ``S=8`` for a reduced batch of
     the same shape family); ``seed_offset`` selects an independent replica
-    (used to rotate inputs so that timed runs do not hit in cache).
+    (used to rotate inputs so that timed runs do not hit in cache).  With
+    ``keep_lens`` the replica keeps replica 0's context lengths (so the same
+    bytes are moved) and redraws only tables, pool values, q and new rows.
     """
     spec = config_spec(index)
     spec.update(overrides)
     ss = np.random.SeedSequence(1000 + index + 7919 * seed_offset)
     s_lens, s_tab, s_pool, s_q, s_k, s_v = ss.spawn(6)
+    if keep_lens:
+        s_lens = np.random.SeedSequence(1000 + index).spawn(6)[0]
     S, Hq, Hkv, D, BS = spec["S"], spec["Hq"], spec["Hkv"], spec["D"], spec["BS"]
     L, layer, dtype = spec["L"], spec["layer"], spec["dtype"]
 
