@@ -60,6 +60,7 @@ extern "C" {
 #define PAGEDKV_ERR_UNSUPPORTED (-3)   /* shape/dtype combination with no kernel */
 #define PAGEDKV_ERR_WORKSPACE (-4)     /* workspace missing or too small */
 #define PAGEDKV_ERR_HIP (-5)           /* a HIP runtime call or launch failed */
+#define PAGEDKV_ERR_SCRATCH (-6)       /* call needs more than the library's static scratch */
 
 /* Element types of the pool (and of q / out / new tokens / gather output). */
 typedef enum {
@@ -316,8 +317,9 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new,
                                   int num_q_heads, float scale, void* workspace,
                                   size_t workspace_bytes, unsigned flags, void* stream);
 
-/* Flags of paged_attention_decode and paged_attention_decode_append, per
- * call; any other bit set is PAGEDKV_ERR_INVALID_ARG.
+/* Flags of paged_attention_decode, paged_attention_decode_append and
+ * paged_attention_decode_noalloc, per call; any other bit set is
+ * PAGEDKV_ERR_INVALID_ARG.
  *   0                     : per-pair workgroups where the shape allows (see
  *                           paged_attention_decode), else the chunk split.
  *   PAGEDKV_DECODE_CHUNKS : always the persistent chunk split.
@@ -325,6 +327,32 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new,
  * since the softmax sums are taken in a different order.  Each split is
  * deterministic: the same inputs and flags give the same bits. */
 #define PAGEDKV_DECODE_CHUNKS 1u
+
+/* paged_attention_decode without a workspace argument, for callers that
+ * cannot allocate device memory: code recorded under HIP graph capture,
+ * serving loops and harnesses that forbid allocation.  The call allocates
+ * nothing.  Its scratch (what the workspace holds for
+ * paged_attention_decode: chunk prefix, partial results of split
+ * sequences) is a static device array of 64 MiB inside the library, one per
+ * GPU, which exists from the loading of the library's device code until the
+ * process ends; its address is looked up once per GPU (hipGetSymbolAddress)
+ * on the first call made with that GPU current.
+ *   - A call whose paged_attention_workspace_bytes(pool, batch,
+ *     num_q_heads) exceeds 64 MiB returns PAGEDKV_ERR_SCRATCH before
+ *     anything is enqueued (e.g. batch 64 with 8 KV heads of 4 query heads
+ *     at head_dim 128 needs 18 MB; batch 256 with 8 KV heads of 8 query
+ *     heads, 42 MB).
+ *   - Every call on one GPU uses that GPU's one array and leaves its
+ *     contents behind; the kernels need no clearing between calls.  Calls
+ *     on one stream are ordered and safe; calls that overlap on one GPU
+ *     (several streams, or host threads without ordering) race on the array
+ *     and give undefined results.
+ * Arguments, results and other errors as paged_attention_decode. */
+int paged_attention_decode_noalloc(void* out, const void* q, const kv_pool_t* pool,
+                                   int layer, const int32_t* block_tables,
+                                   int max_blocks_per_seq, const int32_t* context_lens,
+                                   int batch, int num_q_heads, float scale,
+                                   unsigned flags, void* stream);
 
 /* Bytes of device workspace dense_attention_decode needs (0 for invalid
  * arguments). */

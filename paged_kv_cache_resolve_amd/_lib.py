@@ -18,6 +18,7 @@ ERR_OUT_OF_BLOCKS = -2
 ERR_UNSUPPORTED = -3
 ERR_WORKSPACE = -4
 ERR_HIP = -5
+ERR_SCRATCH = -6
 
 F32 = 0
 BF16 = 1
@@ -74,6 +75,8 @@ SIGNATURES = {
     "paged_attention_decode_append": (_c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _c_int, _vp, _c_int,
                                                _vp, _c_int, _c_int, ctypes.c_float, _vp, _c_size,
                                                ctypes.c_uint, _vp]),
+    "paged_attention_decode_noalloc": (_c_int, [_vp, _vp, _vp, _c_int, _vp, _c_int, _vp, _c_int,
+                                                _c_int, ctypes.c_float, ctypes.c_uint, _vp]),
     "dense_attention_workspace_bytes": (_c_size, [_c_int, _c_int, _c_int, _c_int]),
     "dense_attention_decode": (_c_int, [_vp, _vp, _vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int,
                                         _c_int, _c_int, ctypes.c_float, _vp, _c_size, _vp]),

@@ -5,6 +5,7 @@
 #include <string.h>
 
 #include <atomic>
+#include <mutex>
 #include <new>
 
 #include "internal.h"
@@ -221,13 +222,48 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch, int num
 
 namespace {
 
+// Device scratch of paged_attention_decode_noalloc: one copy per GPU, held
+// from module load to process end.  Host code must not use the array's name
+// as a device address: every use goes through the address returned by
+// hipGetSymbolAddress on that device (scratch_address below).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kScratchDevices = 64;
+std::atomic<void*> g_scratch_addr[kScratchDevices];
+std::mutex g_scratch_mu;
+
+// Device address of the current GPU's scratch array, looked up once per
+// device with that device current.
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PAGEDKV_ERR_HIP;
+  if (dev < 0 || dev >= kScratchDevices) return PAGEDKV_ERR_UNSUPPORTED;
+  void* a = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!a) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    a = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!a) {
+      void* sym = nullptr;
+      if (hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch)) != hipSuccess || !sym)
+        return PAGEDKV_ERR_HIP;
+      g_scratch_addr[dev].store(sym, std::memory_order_release);
+      a = sym;
+    }
+  }
+  *out = a;
+  return PAGEDKV_OK;
+}
+
 // Shared body of the decode entry points.  With k_new != nullptr the call
-// also appends each sequence's new token (the fused form).
+// also appends each sequence's new token (the fused form).  With
+// use_scratch the workspace is the library's static device scratch (the
+// workspace arguments are ignored).
 int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
                 const int32_t* block_tables, int max_blocks_per_seq, const int32_t* context_lens,
                 int batch, int num_q_heads, float scale, void* workspace, size_t workspace_bytes,
                 unsigned flags, void* stream, const void* k_new, const void* v_new,
-                const int32_t* positions) {
+                const int32_t* positions, bool use_scratch = false) {
   if (!pool || batch < 0 || layer < 0 || layer >= pool->layers || max_blocks_per_seq < 1 ||
       num_q_heads < 1 || num_q_heads % pool->kv_heads != 0 || !isfinite(scale) ||
       (flags & ~PAGEDKV_DECODE_CHUNKS) != 0)
@@ -248,6 +284,12 @@ int decode_call(void* out, const void* q, const kv_pool_t* pool, int layer,
   const bool use_mfma = mfma_supported(pool, hs.group);
   if (!use_mfma && !generic_supported(pool, hs.group)) return PAGEDKV_ERR_UNSUPPORTED;
   const size_t need = decode_workspace_bytes(batch, hs.vheads, hs.group, pool->head_dim);
+  if (use_scratch) {
+    if (need > kScratchBytes) return PAGEDKV_ERR_SCRATCH;
+    const int st = scratch_address(&workspace);
+    if (st != PAGEDKV_OK) return st;
+    workspace_bytes = kScratchBytes;
+  }
   if (!workspace || workspace_bytes < need) return PAGEDKV_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return PAGEDKV_ERR_WORKSPACE;
 
@@ -321,6 +363,15 @@ int paged_attention_decode_append(void* out, const void* q, const void* k_new, c
   return decode_call(out, q, pool, layer, block_tables, max_blocks_per_seq, context_lens, batch,
                      num_q_heads, scale, workspace, workspace_bytes, flags, stream, k_new, v_new,
                      positions);
+}
+
+int paged_attention_decode_noalloc(void* out, const void* q, const kv_pool_t* pool, int layer,
+                                   const int32_t* block_tables, int max_blocks_per_seq,
+                                   const int32_t* context_lens, int batch, int num_q_heads,
+                                   float scale, unsigned flags, void* stream) {
+  return decode_call(out, q, pool, layer, block_tables, max_blocks_per_seq, context_lens, batch,
+                     num_q_heads, scale, nullptr, 0, flags, stream, nullptr, nullptr, nullptr,
+                     /*use_scratch=*/true);
 }
 
 size_t dense_attention_workspace_bytes(int batch, int kv_heads, int num_q_heads, int head_dim) {
@@ -399,6 +450,8 @@ const char* pagedkv_status_string(int status) {
     case PAGEDKV_ERR_UNSUPPORTED: return "unsupported shape or dtype";
     case PAGEDKV_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case PAGEDKV_ERR_HIP: return "HIP runtime error";
+    case PAGEDKV_ERR_SCRATCH:
+      return "call needs more than the 64 MiB static scratch of paged_attention_decode_noalloc";
     default: return "unknown status";
   }
 }

@@ -31,7 +31,7 @@ def _declared_functions():
 
 def test_every_declared_symbol_is_exported():
     names = _declared_functions()
-    assert len(names) == 26, names
+    assert len(names) == 27, names
     for n in names:
         assert hasattr(L, n), f"{n} missing from libpagedkv.so"
     assert set(names) == set(_lib.SIGNATURES), "binding signatures drift from the header"
@@ -314,6 +314,33 @@ def test_decode_refuses_chunk_counts_past_int32():
     fused = L.paged_attention_decode_append(p, p, p, p, p, h, 0, p, limit_mb + 1, p, batch, 8,
                                             ctypes.c_float(0.1), p, wsb, 0, None)
     assert fused == _lib.ERR_UNSUPPORTED
+    L.kv_pool_destroy(h)
+
+
+def test_noalloc_decode_validates_and_refuses_oversized_calls():
+    """paged_attention_decode_noalloc checks its arguments as
+    paged_attention_decode does, and refuses a call whose workspace would
+    exceed its 64 MiB static scratch with PAGEDKV_ERR_SCRATCH; both before
+    anything touches the GPU."""
+    h = _pool(nb=8, bs=16, layers=1, hkv=8, d=128)
+    p = FAKE_DEVICE_PTR
+    dec = lambda batch, hq=32, layer=0, flags=0, out=p: L.paged_attention_decode_noalloc(  # noqa: E731
+        out, p, h, layer, p, 4, p, batch, hq, ctypes.c_float(0.1), flags, None)
+    assert dec(4, layer=1) == _lib.ERR_INVALID_ARG
+    assert dec(4, hq=31) == _lib.ERR_INVALID_ARG
+    assert dec(4, flags=2) == _lib.ERR_INVALID_ARG
+    assert dec(4, out=None) == _lib.ERR_INVALID_ARG
+    assert dec(0) == 0
+    assert dec(16385) == _lib.ERR_UNSUPPORTED
+    limit = 64 << 20
+    fits = [b for b in (1000, 2000, 3000, 4000, 8000, 16384)
+            if L.paged_attention_workspace_bytes(h, b, 32) <= limit]
+    over = [b for b in (1000, 2000, 3000, 4000, 8000, 16384)
+            if L.paged_attention_workspace_bytes(h, b, 32) > limit]
+    assert fits and over
+    for b in over:
+        assert dec(b) == _lib.ERR_SCRATCH
+    assert b"64 MiB" in L.pagedkv_status_string(_lib.ERR_SCRATCH)
     L.kv_pool_destroy(h)
 
 
