@@ -27,7 +27,7 @@ extern "C" {
  * (buffer_bytes long): slab i of the visit order starts at byte
  * slab_ids[i] * slab_bytes.  The visit order is cut into `workgroups` x 4
  * equal contiguous ranges, one per wavefront; each wavefront reads its
- * slabs 1 KiB (64 lanes x 16 bytes) at a time with 16 loads per lane in
+ * slabs 1 KiB (64 lanes x 16 bytes) at a time with 32 loads per lane in
  * flight.  Each thread folds what it read into one word of sink
  * (device, workgroups * 256 uint32), so no load is dead.
  *   slab_ids    : device, int32 [n_slabs]; values are clamped to

@@ -10,10 +10,22 @@
 
 namespace {
 
-constexpr int kLoadsInFlight = 16;   // 1 KiB lines per wavefront per round
+constexpr int kLoadsInFlight = 32;   // 1 KiB lines per wavefront in flight
 
 typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+// Address of this lane's 16 bytes of 1 KiB line `line` (wave-uniform) of the
+// visit order.
+__device__ __forceinline__ const u32x4_nt* line_addr(const char* base, const_i32_ptr ids,
+                                                     int64_t line, int lines_shift,
+                                                     int slab_shift, int max_id, int lane) {
+  int slab = ids[line >> lines_shift];   // uniform index: a scalar load
+  slab = slab < 0 ? 0 : (slab > max_id ? max_id : slab);
+  const int64_t lines_mask = ((int64_t)1 << lines_shift) - 1;
+  return reinterpret_cast<const u32x4_nt*>(base + ((int64_t)slab << slab_shift) +
+                                           ((line & lines_mask) << 10) + 16 * lane);
+}
 
 __global__ __launch_bounds__(256) void read_probe_kernel(const char* __restrict__ base,
                                                          const int32_t* __restrict__ ids,
@@ -21,29 +33,28 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const char* __restrict_
                                                          int slab_shift, int max_id,
                                                          uint32_t* __restrict__ sink) {
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t wave = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t waves = (int64_t)gridDim.x * 4;
   const int64_t l0 = wave * n_lines / waves;
   const int64_t l1 = (wave + 1) * n_lines / waves;
-  const int64_t lines_mask = ((int64_t)1 << lines_shift) - 1;
   const const_i32_ptr sid = (const_i32_ptr)ids;
   uint32_t acc = 0;
-  for (int64_t l = l0; l < l1; l += kLoadsInFlight) {
+  int64_t l = l0;
+  // whole groups: every load of the group issued before any is consumed
+  for (; l + kLoadsInFlight <= l1; l += kLoadsInFlight) {
     u32x4_nt v[kLoadsInFlight];
 #pragma unroll
-    for (int j = 0; j < kLoadsInFlight; ++j) {
-      const int64_t line = l + j;
-      if (line < l1) {   // wave-uniform
-        int slab = __builtin_amdgcn_readfirstlane(sid[line >> lines_shift]);
-        slab = slab < 0 ? 0 : (slab > max_id ? max_id : slab);
-        const char* p = base + ((int64_t)slab << slab_shift) + ((line & lines_mask) << 10) + 16 * lane;
-        v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
-      } else {
-        v[j] = u32x4_nt{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int j = 0; j < kLoadsInFlight; ++j)
+      v[j] = __builtin_nontemporal_load(
+          line_addr(base, sid, l + j, lines_shift, slab_shift, max_id, lane));
+    __builtin_amdgcn_sched_barrier(0);   // keep every load of the group ahead of its use
 #pragma unroll
     for (int j = 0; j < kLoadsInFlight; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+  }
+  for (; l < l1; ++l) {   // the rest of the range, a line at a time
+    const u32x4_nt v = __builtin_nontemporal_load(
+        line_addr(base, sid, l, lines_shift, slab_shift, max_id, lane));
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   sink[(int64_t)blockIdx.x * 256 + threadIdx.x] = acc;
 }

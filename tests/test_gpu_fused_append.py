@@ -119,10 +119,11 @@ def test_fused_position_cases(dtype, Hq, Hkv, D, BS, split):
     position past T_b (written, not attended), against the oracle and
     bit-identical to the two-call form."""
     say(f"fused positions {dtype} Hq={Hq} Hkv={Hkv} D={D} BS={BS}")
-    lens = [1, BS, BS + 1, 33, 100, 257, 64, 5, 0, 40]
-    positions = [0, BS - 1, BS, 17, -1, 256, 70, 2, -3, 0]
+    lens = [1, BS, BS + 1, 33, 100, 257, 64, 5, 0, 40, 0]
+    positions = [0, BS - 1, BS, 17, -1, 256, 70, 2, -3, 0, 5]
     w = custom(dtype, len(lens), Hq, Hkv, D, BS, lens, positions, L=2, layer=1)
-    # 70 >= T = 64 and the empty sequence's -3: written / skipped, never attended
+    # 70 >= T = 64 and the last, empty sequence's 5: written, never attended;
+    # the other empty sequence's -3: skipped
     poison_append_slots(w, positions)
     two = DeviceWorkload(w)
     fused = DeviceWorkload(w)
@@ -138,7 +139,7 @@ def test_fused_position_cases(dtype, Hq, Hkv, D, BS, split):
     assert torch.equal(out.view(torch.int16) if out.element_size() == 2 else out,
                        out2.view(torch.int16) if out2.element_size() == 2 else out2), \
         "fused output differs from append + decode"
-    assert not dev_to_np(out)[8].any(), "empty sequence must give a zero row"
+    assert not dev_to_np(out)[[8, 10]].any(), "empty sequences must give zero rows"
 
 
 @pytest.mark.parametrize("idx", [2, 3, 4])
