@@ -47,17 +47,26 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 
 # HBM bytes per decode pass-1 launch, from two rocprofv3 PMC passes
 # (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000; the factors make a 1 GiB device
-# copy read and write 1 GiB), averaged over the rotated input replicas.  Only
-# valid for the pass-1 kernel source whose SHA-256 is recorded; otherwise the
-# JSON reports null.
+# copy read and write 1 GiB), averaged over the dispatches of the profiled
+# run (the input replicas share the context lengths, so they move the same
+# bytes).  Only valid for the pass-1 kernel source whose SHA-256 is recorded;
+# otherwise the JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
         "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
-        "bytes": 585595523,
+        "bytes": 542149257,
     },
     "long_context_bf16": {
         "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
-        "bytes": 2210996659,
+        "bytes": 2210997390,
+    },
+    "churned_pool_bf16_gqa7": {
+        "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
+        "bytes": 21581971,
+    },
+    "high_concurrency_bf16": {
+        "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
+        "bytes": 3819908795,
     },
 }
 
@@ -492,28 +501,58 @@ def measure_step(torch, pk, name: str, steps: int, warmup: int, split: str, rota
 
 
 def measure_append_only(torch, pk, reps, n: int = 200) -> dict:
-    """kv_append of one new token per sequence on its own (one launch),
-    back to back over the replicas."""
+    """kv_append of one new token per sequence on its own (one launch).
+    `ms_host_loop`: back to back from Python (each call goes through the
+    binding's checks, so a small append is bound by the host); `ms`: 16
+    appends (rotating over the replicas) captured in one HIP graph and
+    replayed, i.e. the GPU time per append."""
     w0 = reps[0]["w"]
+    stream = torch.cuda.current_stream()
 
     def app(i):
         r = reps[i % len(reps)]
         pk.kv_append(r["pool"], r["w"].layer, r["k"], r["v"], r["tables"], r["pos"])
 
-    ms = back_to_back_ms(torch, app, n)
+    host_ms = back_to_back_ms(torch, app, n)
+    graph_ms = None
+    try:
+        n_graph = 16
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(n_graph):
+                app(i)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n_graph):
+                app(i)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = _events(torch)
+        a.record(stream)
+        for _ in range(10):
+            g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b) / (10 * n_graph)
+        del g
+    except RuntimeError as exc:
+        print(f"[bench] append graph skipped: {exc}", file=sys.stderr, flush=True)
     b = append_bytes(w0)
+    ms = graph_ms if graph_ms is not None else host_ms
     return {"what": "kv_append of one token per sequence (all KV heads of the attended layer)",
-            "ms": round(ms, 5), "bytes": b, "GB_per_s": round(b / (ms * 1e-3) / 1e9, 2)}
+            "ms": round(ms, 5), "ms_host_loop": round(host_ms, 5), "bytes": b,
+            "GB_per_s": round(b / (ms * 1e-3) / 1e9, 2)}
 
 
 def measure_decode_only(torch, pk, reps, split: str, n: int = 200) -> float:
-    """paged_attention_decode alone (no append), back to back."""
-    def dec(i):
-        r = reps[i % len(reps)]
-        w = r["w"]
-        pk.paged_attention_decode(r["out"], r["q"], r["pool"], w.layer, r["tables"], r["lens"],
-                                  w.scale, split=split)
-    return round(back_to_back_ms(torch, dec, n), 5)
+    """paged_attention_decode alone (no append), back to back, through a
+    plain DecodePlan per replica (tensors checked once, as for the step)."""
+    plans = [pk.DecodePlan(r["out"], r["q"], r["pool"], r["w"].layer, r["tables"], r["lens"],
+                           r["w"].scale, split=split) for r in reps]
+    return round(back_to_back_ms(torch, lambda i: plans[i % len(plans)].run(), n), 5)
 
 
 def measure_gather(torch, pk, rec_call_ms, r, tdt) -> dict:
@@ -623,18 +662,45 @@ def _ceiling_for(ceiling: dict, w) -> tuple:
 
 
 def render_table(path: str) -> str:
-    """Markdown results table from a record written by --results-out."""
+    """Markdown results table from a record written by --results-out: per
+    workload the step and call times, effective GB/s, the fraction of the
+    8 TB/s nameplate and of the measured read ceiling for slabs of the
+    workload's block size, and the split used."""
+    sys.path.insert(0, ROOT)
+    from workloads import make_workload
     with open(path) as f:
         rec = json.load(f)
+    ceil = rec.get("read_ceiling") or {}
     rows = ["| Workload | Step (wall clock) | Call back to back | Step GB/s | % of 8 TB/s "
-            "(step / call) | Split | tokens/s (one layer) |",
-            "|---|---|---|---|---|---|---|"]
+            "(step / call) | Call / read ceiling (slab) | Split | tokens/s (one layer) |",
+            "|---|---|---|---|---|---|---|---|"]
     for name, r in rec["workloads"].items():
         frac_call = r["roofline"]["frac"] * 100
+        key, val = _ceiling_for(ceil, make_workload(WORKLOADS[name], with_pool=False))
+        cfrac = (f"{r['roofline']['achieved'] / val * 100:.1f}% ({key.split('_')[1]})"
+                 if val else "-")
         rows.append(f"| {name} | {r['ms_per_step'] * 1e3:.1f} µs | {r['call_ms'] * 1e3:.1f} µs | "
-                    f"{r['value']:.0f} | {r['pct_of_peak']:.1f}% / {frac_call:.1f}% | "
+                    f"{r['value']:.0f} | {r['pct_of_peak']:.1f}% / {frac_call:.1f}% | {cfrac} | "
                     f"{r['split_used']} | {r['tokens_per_s']:.2g} |")
-    return "\n".join(rows)
+    notes = []
+    if ceil:
+        notes.append("Read ceiling (pagedkv_read_probe, 4 GiB buffer): " + ", ".join(
+            f"{k.replace('_', ' ')} {ceil[k]:.0f} GB/s" for k in
+            ("sequential_1MiB", "random_4KiB", "random_8KiB", "random_32KiB", "random_64KiB")
+            if k in ceil) + ".")
+    cpu = rec.get("cpu_baseline")
+    if cpu:
+        one = cpu.get("single_core") or {}
+        notes.append(f"CPU oracle ({cpu.get('workload', '')}, {cpu['sample']}): {cpu['value']} GB/s with "
+                     f"{cpu['cores']} BLAS threads ({cpu.get('host_cores_allowed', '?')} cores allowed)"
+                     + (f", {one['value']} GB/s on 1 thread." if one else "."))
+    app = rec["workloads"].get("churned_pool_bf16_gqa7", {}).get("append_only")
+    if app:
+        host = app.get("ms_host_loop")
+        notes.append(f"churned_pool_bf16_gqa7 one-token kv_append on its own: {app['ms'] * 1e3:.2f} µs "
+                     f"per append replayed from a HIP graph ({app['bytes']} bytes)" +
+                     (f"; {host * 1e3:.2f} µs per call from a Python loop." if host else "."))
+    return "\n".join(rows) + ("\n\n" + "\n".join(notes) if notes else "")
 
 
 def main(argv=None) -> int:
@@ -696,6 +762,11 @@ def main(argv=None) -> int:
             torch.cuda.empty_cache()
         if not args.no_read_ceiling:
             out["read_ceiling"] = read_ceiling(torch)
+        if not args.no_cpu_baseline:
+            from workloads import make_workload
+            out["cpu_baseline"] = cpu_baseline(make_workload(WORKLOADS["llama8b_decode_bf16"]),
+                                               args.cpu_budget_tokens or 600000)
+            out["cpu_baseline"]["workload"] = "llama8b_decode_bf16"
         text = json.dumps(out)
         if args.results_out:
             with open(args.results_out, "w") as f:
