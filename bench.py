@@ -604,7 +604,9 @@ def read_ceiling(torch, buffer_gib: int = 4) -> dict:
     """HBM read ceiling of this GPU from the committed probe kernel
     (include/pagedkv_probe.h): a 4 GiB buffer (16x the Infinity Cache) read
     as 1 MiB slabs in order and as 4/8/32/64 KiB slabs in a random order,
-    at 256..2048 workgroups; the best rate of each pattern, in GB/s."""
+    at 256..2048 workgroups; the best rate of each pattern, in GB/s.  Also
+    what one workgroup (one CU) streams on its own, and each of eight
+    (per_workgroup_random_2KiB, GB/s per workgroup)."""
     import ctypes
     lib = ctypes.CDLL(PROBE_LIB)
     fn = lib.pagedkv_read_probe
@@ -641,7 +643,22 @@ def read_ceiling(torch, buffer_gib: int = 4) -> dict:
         best_wg[label] = best_g
         del ids
     res["best_workgroups"] = best_wg
-    del buf, sink
+    # What one CU streams: 2 MiB of random 2 KiB slabs (one block's K or V
+    # part at head_dim 64 in 16-bit types) read by one workgroup (4
+    # wavefronts, 32 KiB in flight each), and by eight, per workgroup.
+    slab, n = 2 << 10, 1024
+    ids = torch.randperm(nbytes // slab, generator=gen)[:n].to(torch.int32).cuda()
+    per_wg = {}
+    for g in (1, 8):
+        def run(_i, g=g):
+            rc = fn(buf.data_ptr(), nbytes, ids.data_ptr(), n, slab, g, sink.data_ptr(),
+                    stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"pagedkv_read_probe returned {rc}")
+        ms = back_to_back_ms(torch, run, 20)
+        per_wg[str(g)] = round(n * slab / (ms * 1e-3) / 1e9 / g, 1)
+    res["per_workgroup_random_2KiB"] = per_wg
+    del buf, sink, ids
     return res
 
 
@@ -688,6 +705,11 @@ def render_table(path: str) -> str:
             f"{k.replace('_', ' ')} {ceil[k]:.0f} GB/s" for k in
             ("sequential_1MiB", "random_4KiB", "random_8KiB", "random_32KiB", "random_64KiB")
             if k in ceil) + ".")
+        pw = ceil.get("per_workgroup_random_2KiB")
+        if pw:
+            notes.append(f"One workgroup (one CU, 4 wavefronts with 32 KiB in flight each) streams "
+                         f"{pw['1']:.0f} GB/s of random 2 KiB slabs; eight stream "
+                         f"{pw['8']:.0f} GB/s each.")
     cpu = rec.get("cpu_baseline")
     if cpu:
         one = cpu.get("single_core") or {}
