@@ -606,7 +606,8 @@ def read_ceiling(torch, buffer_gib: int = 4) -> dict:
     as 1 MiB slabs in order and as 4/8/32/64 KiB slabs in a random order,
     at 256..2048 workgroups; the best rate of each pattern, in GB/s.  Also
     what one workgroup (one CU) streams on its own, and each of eight
-    (per_workgroup_random_2KiB, GB/s per workgroup)."""
+    (per_workgroup_random_2KiB, GB/s per workgroup), and a single 512 MiB
+    read at 256 workgroups (random_32KiB_512MiB_256wg)."""
     import ctypes
     lib = ctypes.CDLL(PROBE_LIB)
     fn = lib.pagedkv_read_probe
@@ -658,6 +659,19 @@ def read_ceiling(torch, buffer_gib: int = 4) -> dict:
         ms = back_to_back_ms(torch, run, 20)
         per_wg[str(g)] = round(n * slab / (ms * 1e-3) / 1e9 / g, 1)
     res["per_workgroup_random_2KiB"] = per_wg
+    # A read of the Llama-shaped step's size in its launch shape: 512 MiB of
+    # random 32 KiB slabs by 256 workgroups of 4 wavefronts (start-up and
+    # tail included, as in one decode call).
+    slab, n = 32 << 10, (512 << 20) // (32 << 10)
+    ids = torch.randperm(nbytes // slab, generator=gen)[:n].to(torch.int32).cuda()
+
+    def run(_i):
+        rc = fn(buf.data_ptr(), nbytes, ids.data_ptr(), n, slab, 256, sink.data_ptr(),
+                stream.cuda_stream)
+        if rc != 0:
+            raise RuntimeError(f"pagedkv_read_probe returned {rc}")
+    ms = back_to_back_ms(torch, run, 20)
+    res["random_32KiB_512MiB_256wg"] = round(n * slab / (ms * 1e-3) / 1e9, 1)
     del buf, sink, ids
     return res
 
@@ -705,6 +719,10 @@ def render_table(path: str) -> str:
             f"{k.replace('_', ' ')} {ceil[k]:.0f} GB/s" for k in
             ("sequential_1MiB", "random_4KiB", "random_8KiB", "random_32KiB", "random_64KiB")
             if k in ceil) + ".")
+        r512 = ceil.get("random_32KiB_512MiB_256wg")
+        if r512:
+            notes.append(f"A 512 MiB read of random 32 KiB slabs by 256 workgroups (the Llama-shaped "
+                         f"step's size and launch shape, start-up and tail included): {r512:.0f} GB/s.")
         pw = ceil.get("per_workgroup_random_2KiB")
         if pw:
             notes.append(f"One workgroup (one CU, 4 wavefronts with 32 KiB in flight each) streams "
