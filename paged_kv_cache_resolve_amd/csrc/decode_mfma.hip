@@ -463,6 +463,101 @@ struct Stream {
     }
   }
 
+  // LDS-staged streaming (the per-pair kernel at head_dim 64, see
+  // stream_pair_lds): a chunk's K and V rows are copied into an LDS slot by
+  // LDS-direct loads (global_load_lds_dwordx4, 16 bytes per lane), which
+  // need no registers while in flight, and read into the Buf registers when
+  // the chunk is computed.
+  static constexpr bool kLdsStream = !DENSE && !SMALL && D == 64 && NC == 1 && TILES == 2;
+  static constexpr uint32_t kSlotBytes = 2 * TILES * 16 * D * 2;   // K then V of one chunk
+
+  // Copy chunk c into the slot at LDS byte address `slot`.  Tile t's K rows
+  // go to slot + t * 2 KiB, its V rows to slot + (TILES + t) * 2 KiB: 16
+  // rows of 128 bytes, row r's 16-byte column q stored at column q ^ (r & 7)
+  // (so that the reads below hit distinct banks).  Unit u = 64 h + lane of
+  // instruction h is LDS column u & 7 of row u >> 3.  The appended token's
+  // row comes from k_new / v_new, as in issue_k / issue_v.
+  __device__ __forceinline__ void dma_chunk(const Cursor& c, const int* ph, uint32_t slot) const {
+    typedef __attribute__((address_space(3))) void* lds_ptr;
+#pragma unroll
+    for (int kv = 0; kv < 2; ++kv)
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int u = 64 * h + lane;
+          const int r = u >> 3;
+          const int col = (u & 7) ^ (r & 7);
+          const char* src =
+              tile_base(c, ph, t) + (kv ? 2 * p.pool.kv_stride : 0) + (uint32_t)(2 * r * D + 16 * col);
+          if constexpr (APPEND) {
+            if (c.j * kChunk + 16 * t + r == c.pos) src = new_row(c, kv) + 16 * col;
+          }
+          __builtin_amdgcn_global_load_lds(
+              src, (lds_ptr)(uintptr_t)(slot + (uint32_t)((kv * TILES + t) * 2048 + h * 1024)), 16, 0, 0);
+        }
+  }
+
+  // Read the chunk in the slot at `slot` into the Buf registers, in the
+  // layouts issue_k and issue_v load: lane (n, quad) takes K row n, columns
+  // quad and quad + 4 of each tile, and V rows 4 quad + r, bytes 8n .. 8n+7.
+  // The reads are written as asm with their wait inside, because the
+  // compiler would otherwise wait for every LDS-direct load in flight (it
+  // cannot tell the slots apart) before each LDS read.
+  __device__ __forceinline__ void read_chunk(Buf& cb, uint32_t slot) const {
+    typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
+    typedef unsigned u32x2_v __attribute__((ext_vector_type(2)));
+    u32x4_v k[TILES][2];
+    uint32_t ka[TILES][2];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        ka[t][i] = slot + (uint32_t)(t * 2048 + (n * 8 + ((quad + 4 * i) ^ (n & 7))) * 16);
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1])
+        : "v"(ka[0][0]), "v"(ka[0][1]), "v"(ka[1][0]), "v"(ka[1][1])
+        : "memory");
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int i = 0; i < 2; ++i) cb.k[t][i] = __builtin_bit_cast(x8, k[t][i]);
+    u32x2_v v[TILES][4];
+    uint32_t va[TILES][4];
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * quad + r;
+        va[t][r] = slot + (uint32_t)((TILES + t) * 2048 + (row * 8 + ((n >> 1) ^ (row & 7))) * 16 +
+                                     (n & 1) * 8);
+      }
+    asm volatile(
+        "ds_read_b64 %0, %8\n\t"
+        "ds_read_b64 %1, %9\n\t"
+        "ds_read_b64 %2, %10\n\t"
+        "ds_read_b64 %3, %11\n\t"
+        "ds_read_b64 %4, %12\n\t"
+        "ds_read_b64 %5, %13\n\t"
+        "ds_read_b64 %6, %14\n\t"
+        "ds_read_b64 %7, %15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
+          "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+        : "v"(va[0][0]), "v"(va[0][1]), "v"(va[0][2]), "v"(va[0][3]),
+          "v"(va[1][0]), "v"(va[1][1]), "v"(va[1][2]), "v"(va[1][3])
+        : "memory");
+#pragma unroll
+    for (int t = 0; t < TILES; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) cb.v[t][r] = make_uint2(v[t][r].x, v[t][r].y);
+  }
+
   // s[cg * TILES + t]: scores of tile t against column group cg.
   __device__ __forceinline__ void qk(const Buf& cb, f32x4_t* s) const {
 #pragma unroll
@@ -602,6 +697,33 @@ struct Stream {
       if (16 * cg + n < gw) flush_cols(c, whole, cg, lt[cg]);
   }
 
+  // Per-pair kernel with LDS staging: the partial (unnormalised output of
+  // the gw heads, then their (max, sum)) into LDS at byte address `base`,
+  // laid out [head][D] floats then [head][2], for the workgroup's merge.
+  __device__ __forceinline__ void flush_lds(uint32_t base) {
+    static_assert(NC == 1 && VD % 4 == 0, "LDS partials: one column group");
+    typedef __attribute__((address_space(3))) float lds_float;
+    const float lt = sum_x32(sum_x16(l[0]));
+    if (n >= gw) return;
+    lds_float* of = (lds_float*)(uintptr_t)base + n * D + kQuadDims * quad;
+    const f32x4_t* a = acc[0];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int h = 0; h < VD / 4; ++h) {
+        lds_float* d = of + kRowDims * r + kHalfDims * (h / 2) + 4 * (h % 2);
+        d[0] = a[4 * h][r];
+        d[1] = a[4 * h + 1][r];
+        d[2] = a[4 * h + 2][r];
+        d[3] = a[4 * h + 3][r];
+      }
+    if (quad == 0) {
+      lds_float* ml = (lds_float*)(uintptr_t)base + gw * D + 2 * n;
+      ml[0] = m[0];
+      ml[1] = lt;
+    }
+  }
+
   // Column group cg's share of flush: head 16*cg + n of this (virtual) KV head.
   __device__ __forceinline__ void flush_cols(const Cursor& c, bool whole, int cg, float lt) {
     const int G = p.group;   // partial slot stride
@@ -693,6 +815,9 @@ struct StreamF32 {
   static constexpr int NB = D / 16;   // output blocks (h, e)
   using OutElem = float;
   static constexpr bool kPairs = true;
+  static constexpr bool kLdsStream = false;
+  static constexpr uint32_t kSlotBytes = 0;
+  __device__ __forceinline__ void flush_lds(uint32_t) {}
   static constexpr int kDim = D;
   struct Buf {
     float4 k[KQ / 4];
@@ -943,6 +1068,69 @@ __device__ __forceinline__ void stream_chunks(const DecodeParams& p, int lane, i
   st.flush(cur, whole_start && cur.j == cur.nb - 1);
 }
 
+// Wait until at most N vector-memory operations of this wavefront are in
+// flight (gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14, expcnt and lgkmcnt
+// left at their maxima, so they are not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// One wavefront of the per-pair kernel over chunks cur.j .. cur.j + rem - 1
+// of one sequence, its K and V staged through two LDS slots at `slot0` and
+// slot0 + kSlotBytes: while the wavefront computes chunk i from registers,
+// chunks i + 1 and i + 2 are in flight or waiting in LDS.  A chunk's copy
+// is 8 LDS-direct loads (K and V, two tiles, two 1 KiB rows of lanes each),
+// and vector-memory operations complete in issue order, so chunk i is in
+// LDS once at most the 8 loads of chunk i + 1 are still in flight.  The
+// block-table entries of a chunk are fetched one chunk ahead of its copy.
+template <typename S>
+__device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane, int g, int64_t unit,
+                                                Cursor cur, int rem, uint32_t slot0) {
+  S st(p, lane, g, unit);
+  st.reset();
+  st.load_q(cur);
+  typename S::Buf cb;
+  constexpr uint32_t SB = S::kSlotBytes;
+  int ph[S::kPh], ph1[S::kPh], ph_nx[S::kPh];
+  const bool whole = cur.j == 0 && rem == cur.nb;
+  // the table entries of the first three chunks are loaded together
+  Cursor c1 = cur, c = cur;   // c: the chunk whose table entries are in ph_nx
+  c1.j = cur.j + 1;
+  c.j = cur.j + 2;
+  st.fetch_phys(cur, ph);
+#pragma unroll
+  for (int t = 0; t < S::kPh; ++t) ph1[t] = ph_nx[t] = ph[t];
+  if (rem > 1) st.fetch_phys(c1, ph1);
+  if (rem > 2) st.fetch_phys(c, ph_nx);
+  st.dma_chunk(cur, ph, slot0);
+  if (rem > 1) st.dma_chunk(c1, ph1, slot0 + SB);
+  f32x4_t s[S::kTiles];
+  for (int i = 0; i < rem; ++i) {
+    if (i + 1 < rem)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    const uint32_t slot = slot0 + (uint32_t)(i & 1) * SB;
+    st.read_chunk(cb, slot);
+    if (i + 2 < rem) {   // chunk i + 2 into the slot just read
+      st.dma_chunk(c, ph_nx, slot);
+      if (i + 3 < rem) {
+        c.j = cur.j + 3;
+        st.fetch_phys(c, ph_nx);
+      }
+    }
+    st.qk(cb, s);
+    st.attend_chunk(s, cb, cur);
+    if (i + 1 < rem) ++cur.j;
+  }
+  if (whole)
+    st.flush(cur, true);
+  else   // the partial goes to this wavefront's own (now free) slots
+    st.flush_lds(slot0);
+}
+
 // One persistent kernel for every stream type S (16-bit or fp32 elements).
 template <typename S>
 __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
@@ -1014,6 +1202,13 @@ constexpr int kPairWaves = 8;
 // through one CU, which streams only ~27 GB/s however many wavefronts it
 // runs (16 wavefronts per pair were slower than 8 at the same length).
 constexpr int64_t kPairBytesPerWave = 32 << 10;
+// The LDS-staged stream (head_dim 64, 16-bit, blocks of a multiple of 16
+// tokens) keeps two chunks in flight per wavefront without registers and
+// merges through LDS.  Measured against the chunk split (bf16, 2 to 8 KV
+// heads, batches of 4 to 64): faster or even up to 64 KB per wavefront
+// (2048-token tables: churned pool 14.7 -> 13.1 us, 16 sequences x 8 KV
+// heads 15.5 -> 13.4 us), slower at 128 KB (4096 tokens: ~20 vs ~17 us).
+constexpr int64_t kPairBytesPerWaveLds = 64 << 10;
 
 template <typename S>
 __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodeParams p) {
@@ -1036,8 +1231,17 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
   if (w < A) {
     cur.j = w * n / A;
     // unit 7b + w makes partial_slot() give slot (8b + w) * vheads + g
-    stream_chunks<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, nullptr, lens, poss, cur,
-                     (w + 1) * n / A - cur.j);
+    if constexpr (S::kLdsStream) {
+      extern __shared__ __attribute__((aligned(16))) unsigned char pair_lds[];
+      const uint32_t slot0 =
+          (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)pair_lds +
+          (uint32_t)w * 2 * S::kSlotBytes;
+      stream_pair_lds<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, cur,
+                         (w + 1) * n / A - cur.j, slot0);
+    } else {
+      stream_chunks<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, nullptr, lens, poss, cur,
+                       (w + 1) * n / A - cur.j);
+    }
   }
 
   const VHead vh = vhead_rows(g, p.qsplit, p.kv_group);
@@ -1055,13 +1259,25 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
 #pragma unroll
       for (int u = 0; u < kPairWaves; ++u) {
         const int k = min(u, A - 1);   // copies past A are not folded
-        const int64_t e = (((int64_t)kPairWaves * b + k) * H + g) * G + hn;
-        mv[u] = p.ws_ml[2 * e];
-        lv[u] = p.ws_ml[2 * e + 1];
+        if constexpr (S::kLdsStream) {   // wavefront k's partial, in its LDS slots
+          extern __shared__ __attribute__((aligned(16))) unsigned char pair_lds[];
+          const float* part = reinterpret_cast<const float*>(pair_lds + (size_t)k * 2 * S::kSlotBytes);
+          mv[u] = part[vh.count * D + 2 * hn];
+          lv[u] = part[vh.count * D + 2 * hn + 1];
 #pragma unroll
-        for (int i = 0; i < DPL; ++i) {
-          const int d = lane + 64 * i;
-          ov[u][i] = d < D ? p.ws_o[e * D + d] : 0.f;
+          for (int i = 0; i < DPL; ++i) {
+            const int d = lane + 64 * i;
+            ov[u][i] = d < D ? part[hn * D + d] : 0.f;
+          }
+        } else {
+          const int64_t e = (((int64_t)kPairWaves * b + k) * H + g) * G + hn;
+          mv[u] = p.ws_ml[2 * e];
+          lv[u] = p.ws_ml[2 * e + 1];
+#pragma unroll
+          for (int i = 0; i < DPL; ++i) {
+            const int d = lane + 64 * i;
+            ov[u][i] = d < D ? p.ws_o[e * D + d] : 0.f;
+          }
         }
       }
       float M = -INFINITY, L = 0.f, a[DPL];
@@ -1140,19 +1356,21 @@ bool launch_pairs(const DecodeParams& p, int64_t pairs, hipStream_t s) {
     hipFuncAttributes a;
     return hipFuncGetAttributes(&a, fn) == hipSuccess && a.localSizeBytes == 0;
   }();
+  const size_t lds = S::kLdsStream ? (size_t)kPairWaves * 2 * S::kSlotBytes : 0;
   int resident = 0;
   if (!spill_free || (kPairWaves - 1) * pairs > kMaxWaves ||
-      resident_workgroups(fn, 64 * kPairWaves, 0, &resident) != hipSuccess || pairs > resident)
+      resident_workgroups(fn, 64 * kPairWaves, lds, &resident) != hipSuccess || pairs > resident)
     return false;
-  hipLaunchKernelGGL((decode_pair_kernel<S>), dim3((unsigned)pairs), dim3(64 * kPairWaves), 0, s,
+  hipLaunchKernelGGL((decode_pair_kernel<S>), dim3((unsigned)pairs), dim3(64 * kPairWaves), lds, s,
                      p);
   return true;
 }
 
 // Pass 1 for stream type S.  When p.pair_mode asks for it, the per-pair
 // kernel runs if the longest sequence the block tables allow holds at most
-// kPairBytesPerWave of K and V per wavefront; otherwise p.pair_mode is
-// cleared and the persistent kernel runs on wgs workgroups.
+// kPairBytesPerWave (kPairBytesPerWaveLds for the LDS-staged stream) of K
+// and V per wavefront; otherwise p.pair_mode is cleared and the persistent
+// kernel runs on wgs workgroups.
 template <typename S>
 void launch_one(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
   if constexpr (S::kPairs) {
@@ -1160,7 +1378,8 @@ void launch_one(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
       const int64_t pairs = (int64_t)p.batch * p.vheads;
       const int64_t bytes = 2 * (int64_t)p.max_blocks_per_seq * p.pool.block_size *
                             p.pool.head_dim * (p.dtype == PAGEDKV_F32 ? 4 : 2);
-      if (bytes <= kPairWaves * kPairBytesPerWave && launch_pairs<S>(p, pairs, s)) return;
+      const int64_t per_wave = S::kLdsStream ? kPairBytesPerWaveLds : kPairBytesPerWave;
+      if (bytes <= kPairWaves * per_wave && launch_pairs<S>(p, pairs, s)) return;
     }
   }
   p.pair_mode = 0;

@@ -67,13 +67,22 @@ def reference(w):
                                          w.context_lens, w.q, w.scale)
 
 
-PAIR_KV_BYTES = 256 << 10   # per (sequence, KV head): 8 wavefronts x 32 KiB
+PAIR_KV_BYTES = 256 << 10       # per (sequence, KV head): 8 wavefronts x 32 KiB
+PAIR_KV_BYTES_LDS = 512 << 10   # the LDS-staged stream: 8 wavefronts x 64 KiB
+
+
+def pair_kv_bytes(dtype, D, BS):
+    """K/V bytes per (sequence, KV head) up to which the per-pair kernel runs:
+    more for the LDS-staged stream (head_dim 64, 16-bit, blocks of a multiple
+    of 16 tokens)."""
+    lds = dtype != "f32" and D == 64 and BS % 16 == 0
+    return PAIR_KV_BYTES_LDS if lds else PAIR_KV_BYTES
 
 
 def longest_pair_tokens(dtype, D, BS):
     """The longest table span (a whole number of blocks) the per-pair kernel takes."""
     e = 4 if dtype == "f32" else 2
-    return PAIR_KV_BYTES // (2 * D * e) // BS * BS
+    return pair_kv_bytes(dtype, D, BS) // (2 * D * e) // BS * BS
 
 
 def pair_lens(dtype, D, BS):
@@ -127,8 +136,10 @@ def test_pair_split_matches_oracle_and_chunk_split(dtype, Hq, Hkv, D, BS):
 
 
 @pytest.mark.parametrize("dtype,D,BS,extra,expect_pairs", [
-    ("bf16", 64, 16, 0, True),     # 1024 tokens: the limit
+    ("bf16", 64, 16, 0, True),     # 2048 tokens: the limit (LDS-staged stream)
     ("bf16", 64, 16, 16, False),   # one block more
+    ("f16", 64, 16, 0, True),
+    ("f16", 64, 16, 16, False),
     ("bf16", 64, 8, 0, True),      # 8-token blocks
     ("bf16", 64, 8, 8, False),
     ("bf16", 128, 16, 0, True),    # 512 tokens
@@ -163,9 +174,10 @@ def test_pair_split_not_taken_for_many_pairs():
 
 
 def test_pair_split_named_small_workloads():
-    """By default the tiny fp32 batch takes the per-pair split; the
-    churned-pool batch, whose tables span 2048 tokens, keeps the chunk split."""
-    for idx, expect_pairs in ((0, True), (1, False)):
+    """By default the tiny fp32 batch and the churned-pool batch (tables of
+    2048 tokens at head_dim 64, bf16: the LDS-staged stream) take the
+    per-pair split."""
+    for idx, expect_pairs in ((0, True), (1, True)):
         say(f"pair split named workload {idx}")
         w = make_workload(idx)
         dw = DeviceWorkload(w)
