@@ -45,28 +45,52 @@ MALL_BYTES = 256 << 20
 ROOT = os.path.dirname(os.path.abspath(__file__))
 PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_mfma.hip")
 
-# HBM bytes per decode pass-1 launch, from two rocprofv3 PMC passes
-# (FETCH_SIZE x 2.000 + WRITE_SIZE x 1.000; the factors make a 1 GiB device
-# copy read and write 1 GiB), averaged over the dispatches of the profiled
-# run (the input replicas share the context lengths, so they move the same
-# bytes).  Only valid for the pass-1 kernel source whose SHA-256 is recorded;
+# HBM bytes per decode pass-1 launch (the per-pair kernel where the step
+# runs it), from two rocprofv3 PMC passes (FETCH_SIZE x 2.000 + WRITE_SIZE
+# x 1.000; the factors make a 1 GiB device copy read and write 1 GiB),
+# averaged over the dispatches of the profiled run (the input replicas share
+# the context lengths, so they move the same bytes).  Only valid for the pass-1 kernel source whose SHA-256 is recorded;
 # otherwise the JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
-        "bytes": 542149257,
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 542164173,
     },
     "long_context_bf16": {
-        "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
-        "bytes": 2210997390,
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 2211046093,
     },
     "churned_pool_bf16_gqa7": {
-        "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
-        "bytes": 21581971,
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 19326566,
     },
     "high_concurrency_bf16": {
-        "kernel_sha256": "57688c5d3de5a480caf4f41e978bb86684ba7544d319a202748939e5ff6b5fa1",
-        "bytes": 3819908795,
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 3819974963,
+    },
+    "tiny_fp32_mha": {
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 630374,
+    },
+    "llama8b_decode_f32": {
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 1146568806,
+    },
+    "llama8b_decode_f16": {
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 582661325,
+    },
+    "gemma_like_d256_bf16": {
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 1134509978,
+    },
+    "mqa32_decode_bf16": {
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 85687296,
+    },
+    "mqa32_high_concurrency_bf16": {
+        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "bytes": 483666637,
     },
 }
 
@@ -486,8 +510,11 @@ def measure_step(torch, pk, name: str, steps: int, warmup: int, split: str, rota
             "parallelism": "single GPU",
         },
         "roofline": {
-            "kernel": "paged_attention_decode_append (one call: decode pass 1 reading the new "
-                      "rows, the merge of split sequences and the row store)",
+            "kernel": ("paged_attention_decode_append (one call: decode pass 1 reading the new "
+                       "rows, the merge of split sequences and the row store)"
+                       if split_used == "chunks" else
+                       "paged_attention_decode_append (one call: the per-pair kernel, which "
+                       "streams, merges in its workgroup and stores the new rows)"),
             "bound": "hbm",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBS,

@@ -1187,10 +1187,11 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
 // its pieces stay inside one workgroup and no merge launch follows.  Of the
 // pair's n chunks, wavefront w < A = min(n, kPairWaves) streams
 // [w*n/A, (w+1)*n/A) and leaves a partial (running max, sum, unnormalised
-// output) in slot (kPairWaves*b + w)*vheads + g of the workspace.  After a
-// barrier the wavefronts combine the A partials of each query head with the
-// same log-sum-exp update as the merge pass and write the output rows.  A
-// pair one wavefront sees whole (n == 1) is written directly; an empty one
+// output) in slot (kPairWaves*b + w)*vheads + g of the workspace, or, with
+// the LDS-staged stream, in its own LDS slots.  After a barrier the
+// wavefronts combine the A partials of each query head with the same
+// log-sum-exp update as the merge pass and write the output rows.  A pair
+// one wavefront sees whole (n == 1) is written directly; an empty one
 // (T_b = 0) gets zero rows.  With a fused append the workgroup of the pool
 // head's first virtual head also stores the new K/V rows into the pool: this
 // call reads them from k_new / v_new only, so the store may come at any time.
@@ -1228,6 +1229,24 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
   cur.nb = chunks_of(cur.T, S::kChunk);
   const int n = cur.nb;
   const int A = min(n, kPairWaves);   // wavefronts with chunks (uniform over the workgroup)
+  // Fused append: the last wavefront stores the new K/V rows of the pool
+  // head (one 16-byte unit per lane) once the workgroup is done; its loads
+  // are issued here so that they are in hand by then.
+  constexpr int D = S::kDim;
+  const int row_units = D * (int)sizeof(Out) / 16;   // 16-byte units per row
+  const bool app_row = S::kAppend && w == kPairWaves - 1 && cur.pos >= 0 &&
+                       (p.qsplit == 1 || g % p.qsplit == 0);
+  uint4 row_unit = make_uint4(0, 0, 0, 0);
+  int row_phys = 0;
+  if (app_row) {
+    const int gp = vhead_pool_head(g, p.qsplit);
+    const int kv = lane >= row_units;
+    if (lane < 2 * row_units)
+      row_unit = reinterpret_cast<const uint4*>(
+          static_cast<const Out*>(kv ? p.v_new : p.k_new) +
+          ((int64_t)b * p.pool.kv_heads + gp) * D)[lane - kv * row_units];
+    row_phys = p.block_tables[(int64_t)b * p.max_blocks_per_seq + cur.pos / p.pool.block_size];
+  }
   if (w < A) {
     cur.j = w * n / A;
     // unit 7b + w makes partial_slot() give slot (8b + w) * vheads + g
@@ -1245,7 +1264,6 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
   }
 
   const VHead vh = vhead_rows(g, p.qsplit, p.kv_group);
-  constexpr int D = S::kDim;
   constexpr int DPL = (D + 63) / 64;   // dims per lane in the merge
   Out* out = static_cast<Out*>(p.out) + ((int64_t)b * p.num_q_heads + vh.first) * D;
   if (A == 0) {
@@ -1305,19 +1323,14 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
   }
 
   if constexpr (S::kAppend) {
-    const int units = D * (int)sizeof(Out) / 16;   // 16-byte units per row
-    if (w == kPairWaves - 1 && cur.pos >= 0 && (p.qsplit == 1 || g % p.qsplit == 0) &&
-        lane < 2 * units) {
-      const int kv = lane >= units;
-      const int u = lane - kv * units;
+    if (app_row && lane < 2 * row_units) {
+      const int kv = lane >= row_units;
       const int gp = vhead_pool_head(g, p.qsplit);
-      const uint4 v = reinterpret_cast<const uint4*>(
-          static_cast<const Out*>(kv ? p.v_new : p.k_new) + ((int64_t)b * p.pool.kv_heads + gp) * D)[u];
-      const int phys = p.block_tables[(int64_t)b * p.max_blocks_per_seq + cur.pos / p.pool.block_size];
-      const int64_t row = (int64_t)phys * p.pool.block_stride + (int64_t)p.layer * p.pool.layer_stride +
-                          (int64_t)gp * p.pool.head_stride +
+      const int64_t row = (int64_t)row_phys * p.pool.block_stride +
+                          (int64_t)p.layer * p.pool.layer_stride + (int64_t)gp * p.pool.head_stride +
                           (int64_t)(cur.pos % p.pool.block_size) * D + kv * p.pool.kv_stride;
-      reinterpret_cast<uint4*>(reinterpret_cast<Out*>(const_cast<char*>(p.pool.base)) + row)[u] = v;
+      reinterpret_cast<uint4*>(reinterpret_cast<Out*>(const_cast<char*>(p.pool.base)) + row)[lane - kv * row_units] =
+          row_unit;
     }
   }
 }
