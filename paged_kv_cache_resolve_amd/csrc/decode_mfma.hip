@@ -293,6 +293,10 @@ struct Stream {
   x8 qop[NC][NK];
   f32x4_t acc[NC][VD];
   float m[NC], l[NC];
+  // LDS-staged stream only: the normaliser of column n summed over every
+  // token by one MFMA per chunk (A operand all ones), in each of the four
+  // rows a lane holds, so it needs no cross-lane sum at the end.
+  f32x4_t lacc[NC];
 
   __device__ Stream(const DecodeParams& p_, int lane_, int g_, int64_t unit_)
       : p(p_), lane(lane_), n(lane_ & 15), quad(lane_ >> 4), g(g_),
@@ -307,6 +311,7 @@ struct Stream {
     for (int cg = 0; cg < NC; ++cg) {
 #pragma unroll
       for (int c = 0; c < VD; ++c) acc[cg][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      lacc[cg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       m[cg] = -INFINITY;
       l[cg] = 0.f;
     }
@@ -471,13 +476,31 @@ struct Stream {
   static constexpr bool kLdsStream = !DENSE && !SMALL && D == 64 && NC == 1 && TILES == 2;
   static constexpr uint32_t kSlotBytes = 2 * TILES * 16 * D * 2;   // K then V of one chunk
 
+  // Block-table entries of chunk c's tiles for the LDS-staged stream: the
+  // block of each tile's first token, clamped to the sequence's last token
+  // (a tile past T is masked, so any block of the sequence will do).  Unlike
+  // fetch_phys, no entry is chosen by another loaded value, so the scalar
+  // loads are waited for only where the entries are used.
+  __device__ __forceinline__ void fetch_phys_clamped(const Cursor& c, int* ph) const {
+    const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
+    const unsigned bs = (unsigned)p.pool.block_size;
+#pragma unroll
+    for (int t = 0; t < TILES; ++t) {
+      const int tok = min(c.j * kChunk + 16 * t, c.T - 1);
+      ph[t] = uni(trow[(unsigned)tok / bs]);
+    }
+  }
+
   // Copy chunk c into the slot at LDS byte address `slot`.  Tile t's K rows
   // go to slot + t * 2 KiB, its V rows to slot + (TILES + t) * 2 KiB: 16
   // rows of 128 bytes, row r's 16-byte column q stored at column q ^ (r & 7)
   // (so that the reads below hit distinct banks).  Unit u = 64 h + lane of
   // instruction h is LDS column u & 7 of row u >> 3.  The appended token's
-  // row comes from k_new / v_new, as in issue_k / issue_v.
-  __device__ __forceinline__ void dma_chunk(const Cursor& c, const int* ph, uint32_t slot) const {
+  // row comes from k_new / v_new, as in issue_k / issue_v; whether the chunk
+  // holds it is wave-uniform, so other chunks take the form without the
+  // per-lane choice.
+  template <bool OVR>
+  __device__ __forceinline__ void dma_tiles(const Cursor& c, const int* ph, uint32_t slot) const {
     typedef __attribute__((address_space(3))) void* lds_ptr;
 #pragma unroll
     for (int kv = 0; kv < 2; ++kv)
@@ -490,67 +513,77 @@ struct Stream {
           const int col = (u & 7) ^ (r & 7);
           const char* src =
               tile_base(c, ph, t) + (kv ? 2 * p.pool.kv_stride : 0) + (uint32_t)(2 * r * D + 16 * col);
-          if constexpr (APPEND) {
+          if constexpr (OVR) {
             if (c.j * kChunk + 16 * t + r == c.pos) src = new_row(c, kv) + 16 * col;
           }
           __builtin_amdgcn_global_load_lds(
               src, (lds_ptr)(uintptr_t)(slot + (uint32_t)((kv * TILES + t) * 2048 + h * 1024)), 16, 0, 0);
         }
   }
+  __device__ __forceinline__ void dma_chunk(const Cursor& c, const int* ph, uint32_t slot) const {
+    if (APPEND && (unsigned)(c.pos - c.j * kChunk) < (unsigned)kChunk)
+      dma_tiles<APPEND>(c, ph, slot);
+    else
+      dma_tiles<false>(c, ph, slot);
+  }
 
-  // Read the chunk in the slot at `slot` into the Buf registers, in the
-  // layouts issue_k and issue_v load: lane (n, quad) takes K row n, columns
-  // quad and quad + 4 of each tile, and V rows 4 quad + r, bytes 8n .. 8n+7.
-  // The reads are written as asm with their wait inside, because the
-  // compiler would otherwise wait for every LDS-direct load in flight (it
-  // cannot tell the slots apart) before each LDS read.
-  __device__ __forceinline__ void read_chunk(Buf& cb, uint32_t slot) const {
+  // A lane's LDS read addresses in slot 0 of its wavefront; the other slot
+  // and the tiles are immediate offsets.  Lane (n, quad) takes K row n,
+  // columns quad and quad + 4 of each tile, and V rows 4 quad + r, bytes
+  // 8n .. 8n+7: the layouts issue_k and issue_v load.
+  struct LdsLane {
+    uint32_t k[2], v[4];
+  };
+  __device__ __forceinline__ LdsLane lds_lane(uint32_t slot0) const {
+    LdsLane a;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) a.k[i] = slot0 + (uint32_t)((n * 8 + ((quad + 4 * i) ^ (n & 7))) * 16);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int row = 4 * quad + r;
+      a.v[r] = slot0 + (uint32_t)(TILES * 2048 + (row * 8 + ((n >> 1) ^ (row & 7))) * 16 + (n & 1) * 8);
+    }
+    return a;
+  }
+
+  // Read the chunk in slot SLOT into the Buf registers.  The reads are
+  // written as asm with their wait inside, because the compiler would
+  // otherwise wait for every LDS-direct load in flight (it cannot tell the
+  // slots apart) before each LDS read.
+  template <int SLOT>
+  __device__ __forceinline__ void read_chunk(Buf& cb, const LdsLane& a) const {
+    static_assert(TILES == 2, "two tiles per chunk");
+    constexpr int O = SLOT * (int)kSlotBytes;
     typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
     typedef unsigned u32x2_v __attribute__((ext_vector_type(2)));
     u32x4_v k[TILES][2];
-    uint32_t ka[TILES][2];
-#pragma unroll
-    for (int t = 0; t < TILES; ++t)
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        ka[t][i] = slot + (uint32_t)(t * 2048 + (n * 8 + ((quad + 4 * i) ^ (n & 7))) * 16);
     asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
+        "ds_read_b128 %0, %4 offset:%6\n\t"
+        "ds_read_b128 %1, %5 offset:%6\n\t"
+        "ds_read_b128 %2, %4 offset:%7\n\t"
+        "ds_read_b128 %3, %5 offset:%7\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1])
-        : "v"(ka[0][0]), "v"(ka[0][1]), "v"(ka[1][0]), "v"(ka[1][1])
+        : "v"(a.k[0]), "v"(a.k[1]), "i"(O), "i"(O + 2048)
         : "memory");
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
 #pragma unroll
       for (int i = 0; i < 2; ++i) cb.k[t][i] = __builtin_bit_cast(x8, k[t][i]);
     u32x2_v v[TILES][4];
-    uint32_t va[TILES][4];
-#pragma unroll
-    for (int t = 0; t < TILES; ++t)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * quad + r;
-        va[t][r] = slot + (uint32_t)((TILES + t) * 2048 + (row * 8 + ((n >> 1) ^ (row & 7))) * 16 +
-                                     (n & 1) * 8);
-      }
     asm volatile(
-        "ds_read_b64 %0, %8\n\t"
-        "ds_read_b64 %1, %9\n\t"
-        "ds_read_b64 %2, %10\n\t"
-        "ds_read_b64 %3, %11\n\t"
-        "ds_read_b64 %4, %12\n\t"
-        "ds_read_b64 %5, %13\n\t"
-        "ds_read_b64 %6, %14\n\t"
-        "ds_read_b64 %7, %15\n\t"
+        "ds_read_b64 %0, %8 offset:%12\n\t"
+        "ds_read_b64 %1, %9 offset:%12\n\t"
+        "ds_read_b64 %2, %10 offset:%12\n\t"
+        "ds_read_b64 %3, %11 offset:%12\n\t"
+        "ds_read_b64 %4, %8 offset:%13\n\t"
+        "ds_read_b64 %5, %9 offset:%13\n\t"
+        "ds_read_b64 %6, %10 offset:%13\n\t"
+        "ds_read_b64 %7, %11 offset:%13\n\t"
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
           "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
-        : "v"(va[0][0]), "v"(va[0][1]), "v"(va[0][2]), "v"(va[0][3]),
-          "v"(va[1][0]), "v"(va[1][1]), "v"(va[1][2]), "v"(va[1][3])
+        : "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]), "i"(O), "i"(O + 2048)
         : "memory");
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
@@ -574,7 +607,16 @@ struct Stream {
   // Online softmax of column group cg over one chunk: rescales its m, l and
   // acc and returns the probabilities rounded to the pool type, packed in
   // pairs (the B-operand layout of the PV product).
-  template <bool TAIL>
+  // LAZY (the LDS-staged stream): the normaliser is summed by the MFMA unit
+  // (lacc, in attend), and m, acc and lacc are rescaled only when some
+  // column's chunk maximum exceeds its running max by more than kLazyLog2.
+  // Until then the older max stays the common reference of acc, lacc and the
+  // probabilities, which stay below 2^kLazyLog2 (times 2^kPScaleLog2), so
+  // the result is the same up to rounding; fp16 takes 0 (its probabilities
+  // already use the range up to 2^15), which still skips every chunk that
+  // raises no column's max.
+  static constexpr float kLazyLog2 = E::kPScaleLog2 == 0.f ? 8.f : 0.f;
+  template <bool TAIL, bool LAZY = false>
   __device__ __forceinline__ void softmax_cols(const f32x4_t* s, const Buf& cb, const Cursor& c,
                                                int cg, uint32_t (&pw)[TILES][2]) {
     float sv[TILES][4];
@@ -595,7 +637,18 @@ struct Stream {
     // running max is still -inf, exponents are taken against 0 instead
     // (acc and l are zero then, and the weights of masked tokens are 0).
     float mref;
-    {
+    if constexpr (LAZY) {
+      static_assert(!DENSE, "every chunk of a paged sequence holds a token");
+      if (__builtin_amdgcn_ballot_w64(bmax > m[cg] + kLazyLog2) != 0) {
+        const float mn = fmaxf(m[cg], bmax);
+        const float alpha = __builtin_amdgcn_exp2f(m[cg] - mn);
+#pragma unroll
+        for (int i = 0; i < VD; ++i) acc[cg][i] *= alpha;
+        lacc[cg] *= alpha;
+        m[cg] = mn;
+      }
+      mref = m[cg];
+    } else {
       // branch-free rescale (alpha = 1 when no running max grows)
       const float mn = fmaxf(m[cg], bmax);
       mref = DENSE && mn == -INFINITY ? 0.f : mn;
@@ -610,7 +663,8 @@ struct Stream {
     for (int t = 0; t < TILES; ++t) {
       pw[t][0] = E::pack2(__builtin_amdgcn_exp2f(sv[t][0] - mp), __builtin_amdgcn_exp2f(sv[t][1] - mp));
       pw[t][1] = E::pack2(__builtin_amdgcn_exp2f(sv[t][2] - mp), __builtin_amdgcn_exp2f(sv[t][3] - mp));
-      l[cg] += (E::lo(pw[t][0]) + E::hi(pw[t][0])) + (E::lo(pw[t][1]) + E::hi(pw[t][1]));
+      if constexpr (!LAZY)
+        l[cg] += (E::lo(pw[t][0]) + E::hi(pw[t][0])) + (E::lo(pw[t][1]) + E::hi(pw[t][1]));
     }
   }
 
@@ -618,11 +672,12 @@ struct Stream {
   // product), then the weighted V sum; updates m, l, acc.  TAIL masks tokens
   // at or past T; masked V rows are zeroed, not weighted by zero, so unused
   // pool slots never reach the sum.
-  template <bool TAIL>
+  template <bool TAIL, bool LAZY = false>
   __device__ __forceinline__ void attend(const f32x4_t* s, Buf& cb, const Cursor& c) {
+    static_assert(!LAZY || TILES == 2, "the lazy form sums the normaliser with the 16x16x32 MFMA");
     uint32_t pw[NC][TILES][2];
 #pragma unroll
-    for (int cg = 0; cg < NC; ++cg) softmax_cols<TAIL>(s + cg * TILES, cb, c, cg, pw[cg]);
+    for (int cg = 0; cg < NC; ++cg) softmax_cols<TAIL, LAZY>(s + cg * TILES, cb, c, cg, pw[cg]);
     if (TAIL && !DENSE) {   // dense rows past the end repeat a real row; their weight is 0
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
@@ -655,6 +710,12 @@ struct Stream {
       for (int cg = 0; cg < NC; ++cg)
         pop[cg] = __builtin_bit_cast(
             x8, make_uint4(pw[cg][0][0], pw[cg][0][1], pw[cg][1][0], pw[cg][1][1]));
+      if constexpr (LAZY) {   // column sums of the rounded probabilities
+        const uint32_t one2 = E::pack2(1.f, 1.f);
+        const x8 ones = __builtin_bit_cast(x8, make_uint4(one2, one2, one2, one2));
+#pragma unroll
+        for (int cg = 0; cg < NC; ++cg) lacc[cg] = E::mma32(ones, pop[cg], lacc[cg]);
+      }
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         uint32_t ev[4], od[4];
@@ -678,12 +739,13 @@ struct Stream {
     }
   }
 
+  template <bool LAZY = false>
   __device__ __forceinline__ void attend_chunk(const f32x4_t* s, Buf& cb,
                                                const Cursor& c) {
     if (DENSE || (c.j == c.nb - 1 && (c.T % (16 * TILES)) != 0))
-      attend<true>(s, cb, c);
+      attend<true, LAZY>(s, cb, c);
     else
-      attend<false>(s, cb, c);
+      attend<false, LAZY>(s, cb, c);
   }
 
   // End of this wavefront's part of sequence c.b: normalised output if it
@@ -703,7 +765,7 @@ struct Stream {
   __device__ __forceinline__ void flush_lds(uint32_t base) {
     static_assert(NC == 1 && VD % 4 == 0, "LDS partials: one column group");
     typedef __attribute__((address_space(3))) float lds_float;
-    const float lt = sum_x32(sum_x16(l[0]));
+    const float lt = lacc[0][0];
     if (n >= gw) return;
     lds_float* of = (lds_float*)(uintptr_t)base + n * D + kQuadDims * quad;
     const f32x4_t* a = acc[0];
@@ -1077,58 +1139,70 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// One wavefront of the per-pair kernel over chunks cur.j .. cur.j + rem - 1
-// of one sequence, its K and V staged through two LDS slots at `slot0` and
-// slot0 + kSlotBytes: while the wavefront computes chunk i from registers,
-// chunks i + 1 and i + 2 are in flight or waiting in LDS.  A chunk's copy
-// is 8 LDS-direct loads (K and V, two tiles, two 1 KiB rows of lanes each),
-// and vector-memory operations complete in issue order, so chunk i is in
-// LDS once at most the 8 loads of chunk i + 1 are still in flight.  The
-// block-table entries of a chunk are fetched one chunk ahead of its copy.
+// One wavefront of the per-pair kernel over chunks cur.j, cur.j + stride,
+// ... (rem of them) of one sequence, its K and V staged through two LDS
+// slots at `slot0` and slot0 + kSlotBytes: while the wavefront computes
+// chunk i from registers, chunks i + 1 and i + 2 are in flight or waiting in
+// LDS.  A chunk's copy is 8 LDS-direct loads (K and V, two tiles, two 1 KiB
+// rows of lanes each), and vector-memory operations complete in issue order,
+// so chunk i is in LDS once at most the 8 loads of chunk i + 1 are still in
+// flight.  ph0, ph1 and ph2 are the block-table entries of the first three
+// chunks (loaded by the caller with the sequence's length); later entries
+// are fetched one chunk ahead of their copy.  The loop runs two chunks per
+// pass so that each read has its slot as an immediate offset.
+template <int P> struct SlotTag { static constexpr int value = P; };
+
 template <typename S>
 __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane, int g, int64_t unit,
-                                                Cursor cur, int rem, uint32_t slot0) {
+                                                Cursor cur, int stride, int rem, const int* ph0,
+                                                const int* ph1, const int* ph2, uint32_t slot0) {
   S st(p, lane, g, unit);
   st.reset();
   st.load_q(cur);
+  const typename S::LdsLane la = st.lds_lane(slot0);
   typename S::Buf cb;
   constexpr uint32_t SB = S::kSlotBytes;
-  int ph[S::kPh], ph1[S::kPh], ph_nx[S::kPh];
-  const bool whole = cur.j == 0 && rem == cur.nb;
-  // the table entries of the first three chunks are loaded together
-  Cursor c1 = cur, c = cur;   // c: the chunk whose table entries are in ph_nx
-  c1.j = cur.j + 1;
-  c.j = cur.j + 2;
-  st.fetch_phys(cur, ph);
+  const bool whole = cur.nb == 1;
+  const int j0 = cur.j;
+  int ph_nx[S::kPh];   // entries of the next chunk to copy (i + 2 at step i)
 #pragma unroll
-  for (int t = 0; t < S::kPh; ++t) ph1[t] = ph_nx[t] = ph[t];
-  if (rem > 1) st.fetch_phys(c1, ph1);
-  if (rem > 2) st.fetch_phys(c, ph_nx);
-  st.dma_chunk(cur, ph, slot0);
-  if (rem > 1) st.dma_chunk(c1, ph1, slot0 + SB);
+  for (int t = 0; t < S::kPh; ++t) ph_nx[t] = ph2[t];
+  st.dma_chunk(cur, ph0, slot0);
+  if (rem > 1) {
+    Cursor c1 = cur;
+    c1.j = j0 + stride;
+    st.dma_chunk(c1, ph1, slot0 + SB);
+  }
   f32x4_t s[S::kTiles];
-  for (int i = 0; i < rem; ++i) {
+  auto step = [&](auto tag, int i) {
+    constexpr int P = decltype(tag)::value;
     if (i + 1 < rem)
       wait_vmcnt<8>();
     else
       wait_vmcnt<0>();
-    const uint32_t slot = slot0 + (uint32_t)(i & 1) * SB;
-    st.read_chunk(cb, slot);
+    st.template read_chunk<P>(cb, la);
     if (i + 2 < rem) {   // chunk i + 2 into the slot just read
-      st.dma_chunk(c, ph_nx, slot);
+      Cursor c = cur;
+      c.j = j0 + (i + 2) * stride;
+      st.dma_chunk(c, ph_nx, slot0 + P * SB);
       if (i + 3 < rem) {
-        c.j = cur.j + 3;
-        st.fetch_phys(c, ph_nx);
+        c.j += stride;
+        st.fetch_phys_clamped(c, ph_nx);
       }
     }
+    cur.j = j0 + i * stride;
     st.qk(cb, s);
-    st.attend_chunk(s, cb, cur);
-    if (i + 1 < rem) ++cur.j;
+    st.template attend_chunk<true>(s, cb, cur);
+  };
+  for (int i = 0; i < rem; i += 2) {
+    step(SlotTag<0>{}, i);
+    if (i + 1 < rem) step(SlotTag<1>{}, i + 1);
   }
-  if (whole)
-    st.flush(cur, true);
-  else   // the partial goes to this wavefront's own (now free) slots
+  if (whole) {
+    if (st.n < st.gw) st.flush_cols(cur, true, 0, st.lacc[0][0]);
+  } else {   // the partial goes to this wavefront's own (now free) slots
     st.flush_lds(slot0);
+  }
 }
 
 // One persistent kernel for every stream type S (16-bit or fp32 elements).
@@ -1224,6 +1298,21 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
   Cursor cur;
   cur.dense_T = 0;
   cur.b = b;
+  // LDS-staged stream: wavefront w < min(n, 8) takes chunks w, w + 8, ...
+  // (so its first chunks are known before the length is), and the table
+  // entries of chunks w, w + 8 and w + 16 are loaded together with the
+  // length.  Indices are clamped into the table row; an entry of a chunk
+  // that does not exist is never used.
+  int pre[3][S::kPh];
+  if constexpr (S::kLdsStream) {
+    const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
+    const unsigned bs = (unsigned)p.pool.block_size, last = (unsigned)p.max_blocks_per_seq - 1;
+#pragma unroll
+    for (int k = 0; k < 3; ++k)
+#pragma unroll
+      for (int t = 0; t < S::kPh; ++t)
+        pre[k][t] = uni(trow[min((unsigned)((w + kPairWaves * k) * S::kChunk + 16 * t) / bs, last)]);
+  }
   cur.T = uni(lens[b]);
   cur.pos = poss ? uni(poss[b]) : -1;
   cur.nb = chunks_of(cur.T, S::kChunk);
@@ -1248,16 +1337,24 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
     row_phys = p.block_tables[(int64_t)b * p.max_blocks_per_seq + cur.pos / p.pool.block_size];
   }
   if (w < A) {
-    cur.j = w * n / A;
     // unit 7b + w makes partial_slot() give slot (8b + w) * vheads + g
     if constexpr (S::kLdsStream) {
       extern __shared__ __attribute__((aligned(16))) unsigned char pair_lds[];
       const uint32_t slot0 =
           (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)pair_lds +
           (uint32_t)w * 2 * S::kSlotBytes;
-      stream_pair_lds<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, cur,
-                         (w + 1) * n / A - cur.j, slot0);
+      // a tile that starts at or past T takes its chunk's first block (it is
+      // masked); chunks w + 8 and w + 16 are used only when A == 8
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int t = 1; t < S::kPh; ++t)
+          if ((w + kPairWaves * k) * S::kChunk + 16 * t >= cur.T) pre[k][t] = pre[k][0];
+      cur.j = w;
+      stream_pair_lds<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, cur, A, (n - 1 - w) / A + 1,
+                         pre[0], pre[1], pre[2], slot0);
     } else {
+      cur.j = w * n / A;
       stream_chunks<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, nullptr, lens, poss, cur,
                        (w + 1) * n / A - cur.j);
     }
