@@ -1139,23 +1139,49 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Wait until at most `newer` chunk copies (8 LDS-direct loads each) issued
+// after the oldest one are still in flight, for newer in [0, K].
+template <int K>
+__device__ __forceinline__ void wait_newer_chunks(int newer) {
+  if constexpr (K == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (newer >= K)
+      wait_vmcnt<8 * K>();
+    else
+      wait_newer_chunks<K - 1>(newer);
+  }
+}
+
 // One wavefront of the per-pair kernel over chunks cur.j, cur.j + stride,
-// ... (rem of them) of one sequence, its K and V staged through two LDS
-// slots at `slot0` and slot0 + kSlotBytes: while the wavefront computes
-// chunk i from registers, chunks i + 1 and i + 2 are in flight or waiting in
-// LDS.  A chunk's copy is 8 LDS-direct loads (K and V, two tiles, two 1 KiB
-// rows of lanes each), and vector-memory operations complete in issue order,
-// so chunk i is in LDS once at most the 8 loads of chunk i + 1 are still in
-// flight.  ph0, ph1 and ph2 are the block-table entries of the first three
-// chunks (loaded by the caller with the sequence's length); later entries
-// are fetched one chunk ahead of their copy.  The loop runs two chunks per
+// ... (rem of them) of one sequence, its K and V staged through NS LDS slots
+// of kSlotBytes from `slot0`: while the wavefront computes chunk i from
+// registers, chunks i + 1 .. i + NS are in flight or waiting in LDS.  A
+// chunk's copy is 8 LDS-direct loads (K and V, two tiles, two 1 KiB rows of
+// lanes each), and vector-memory operations complete in issue order, so
+// chunk i is in LDS once at most the loads of the chunks copied after it
+// are still in flight.  pre[k] holds the block-table entries of chunk k for
+// k <= NS (loaded by the caller with the sequence's length); later entries
+// are fetched one chunk ahead of their copy.  The loop runs NS chunks per
 // pass so that each read has its slot as an immediate offset.
 template <int P> struct SlotTag { static constexpr int value = P; };
 
-template <typename S>
+// Chunks of one wavefront of the per-pair LDS-staged stream: w, w + A,
+// w + 2A, ... for the A = min(n, 8) wavefronts with chunks.  Its first
+// three chunks, w, w + 8 and w + 16, do not depend on the pair's chunk
+// count n (with A < 8 each wavefront has at most one).  (Rounds that gave
+// wavefronts 0..3, the first of each SIMD, four chunks for every three of
+// the others were slower: churned pool 10.75 -> 11.5 us.)
+struct PairChunks {
+  int w, stride;
+  __device__ __forceinline__ int at(int i) const { return w + i * stride; }
+};
+
+template <typename S, int NS>
 __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane, int g, int64_t unit,
-                                                Cursor cur, int stride, int rem, const int* ph0,
-                                                const int* ph1, const int* ph2, uint32_t slot0) {
+                                                Cursor cur, PairChunks pc, int rem,
+                                                const int (*pre)[S::kPh], uint32_t slot0) {
+  static_assert(NS == 1 || NS == 2 || NS == 4, "slots per wavefront");
   S st(p, lane, g, unit);
   st.reset();
   st.load_q(cur);
@@ -1163,40 +1189,42 @@ __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane,
   typename S::Buf cb;
   constexpr uint32_t SB = S::kSlotBytes;
   const bool whole = cur.nb == 1;
-  const int j0 = cur.j;
-  int ph_nx[S::kPh];   // entries of the next chunk to copy (i + 2 at step i)
+  int ph_nx[S::kPh];   // entries of the next chunk to copy (i + NS at step i)
 #pragma unroll
-  for (int t = 0; t < S::kPh; ++t) ph_nx[t] = ph2[t];
-  st.dma_chunk(cur, ph0, slot0);
-  if (rem > 1) {
-    Cursor c1 = cur;
-    c1.j = j0 + stride;
-    st.dma_chunk(c1, ph1, slot0 + SB);
-  }
+  for (int t = 0; t < S::kPh; ++t) ph_nx[t] = pre[NS][t];
+#pragma unroll
+  for (int k = 0; k < NS; ++k)
+    if (k < rem) {
+      Cursor c = cur;
+      c.j = pc.at(k);
+      st.dma_chunk(c, pre[k], slot0 + k * SB);
+    }
   f32x4_t s[S::kTiles];
   auto step = [&](auto tag, int i) {
     constexpr int P = decltype(tag)::value;
-    if (i + 1 < rem)
-      wait_vmcnt<8>();
-    else
-      wait_vmcnt<0>();
+    wait_newer_chunks<NS - 1>(rem - 1 - i);
     st.template read_chunk<P>(cb, la);
-    if (i + 2 < rem) {   // chunk i + 2 into the slot just read
+    if (i + NS < rem) {   // chunk i + NS into the slot just read
       Cursor c = cur;
-      c.j = j0 + (i + 2) * stride;
+      c.j = pc.at(i + NS);
       st.dma_chunk(c, ph_nx, slot0 + P * SB);
-      if (i + 3 < rem) {
-        c.j += stride;
+      if (i + NS + 1 < rem) {
+        c.j = pc.at(i + NS + 1);
         st.fetch_phys_clamped(c, ph_nx);
       }
     }
-    cur.j = j0 + i * stride;
+    cur.j = pc.at(i);
     st.qk(cb, s);
     st.template attend_chunk<true>(s, cb, cur);
   };
-  for (int i = 0; i < rem; i += 2) {
+  for (int i = 0; i < rem; i += NS) {
     step(SlotTag<0>{}, i);
-    if (i + 1 < rem) step(SlotTag<1>{}, i + 1);
+    if constexpr (NS >= 2)
+      if (i + 1 < rem) step(SlotTag<1>{}, i + 1);
+    if constexpr (NS == 4) {
+      if (i + 2 < rem) step(SlotTag<2>{}, i + 2);
+      if (i + 3 < rem) step(SlotTag<3>{}, i + 3);
+    }
   }
   if (whole) {
     if (st.n < st.gw) st.flush_cols(cur, true, 0, st.lacc[0][0]);
@@ -1256,20 +1284,26 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
   stream_chunks<S>(p, lane, g, unit, prefix, lens, poss, cur, rem);
 }
 
-// Small batches: one workgroup of kPairWaves wavefronts per (sequence b,
-// virtual KV head g) pair, so that the split of a sequence and the merge of
-// its pieces stay inside one workgroup and no merge launch follows.  Of the
-// pair's n chunks, wavefront w < A = min(n, kPairWaves) streams
-// [w*n/A, (w+1)*n/A) and leaves a partial (running max, sum, unnormalised
-// output) in slot (kPairWaves*b + w)*vheads + g of the workspace, or, with
-// the LDS-staged stream, in its own LDS slots.  After a barrier the
-// wavefronts combine the A partials of each query head with the same
-// log-sum-exp update as the merge pass and write the output rows.  A pair
-// one wavefront sees whole (n == 1) is written directly; an empty one
-// (T_b = 0) gets zero rows.  With a fused append the workgroup of the pool
-// head's first virtual head also stores the new K/V rows into the pool: this
-// call reads them from k_new / v_new only, so the store may come at any time.
-constexpr int kPairWaves = 8;
+// Small batches: one workgroup of NW wavefronts per (sequence b, virtual KV
+// head g) pair, so that the split of a sequence and the merge of its pieces
+// stay inside one workgroup and no merge launch follows.  Of the pair's n
+// chunks, wavefront w < A = min(n, NW) streams [w*n/A, (w+1)*n/A) and
+// leaves a partial (running max, sum, unnormalised output) in slot
+// (kPairWaves*b + w)*vheads + g of the workspace; with the LDS-staged
+// stream it takes chunks w, w + A, w + 2A, ... and leaves its partial in
+// its own LDS slots.  After a barrier the wavefronts combine the A partials
+// of each query head with the same log-sum-exp update as the merge pass and
+// write the output rows.  A pair one wavefront sees whole (n == 1) is
+// written directly; an empty one (T_b = 0) gets zero rows.  With a fused
+// append the workgroup of the pool head's first virtual head also stores
+// the new K/V rows into the pool: this call reads them from k_new / v_new
+// only, so the store may come at any time.
+constexpr int kPairWaves = 8;   // NW of the register stream
+// NW of the LDS-staged stream, and its slots per wavefront
+constexpr int kLdsWaves = 8;
+constexpr int kLdsSlots = 2;
+template <typename S>
+constexpr int pair_waves() { return S::kLdsStream ? kLdsWaves : kPairWaves; }
 // K/V bytes per wavefront up to which the per-pair kernel is used.  Measured
 // (batches of 4 to 64 sequences, head_dim 64 and 128, bf16 and fp32): one
 // workgroup per pair is 15-25% faster than the chunk split and merge kernel
@@ -1277,17 +1311,15 @@ constexpr int kPairWaves = 8;
 // through one CU, which streams only ~27 GB/s however many wavefronts it
 // runs (16 wavefronts per pair were slower than 8 at the same length).
 constexpr int64_t kPairBytesPerWave = 32 << 10;
-// The LDS-staged stream (head_dim 64, 16-bit, blocks of a multiple of 16
-// tokens) keeps two chunks in flight per wavefront without registers and
-// merges through LDS.  Measured against the chunk split (bf16, 2 to 8 KV
-// heads, batches of 4 to 64): faster or even up to 64 KB per wavefront
-// (2048-token tables: churned pool 14.7 -> 13.1 us, 16 sequences x 8 KV
-// heads 15.5 -> 13.4 us), slower at 128 KB (4096 tokens: ~20 vs ~17 us).
-constexpr int64_t kPairBytesPerWaveLds = 64 << 10;
+// K/V bytes per pair up to which the LDS-staged stream (head_dim 64,
+// 16-bit, blocks of a multiple of 16 tokens) is used; it keeps several
+// chunks in flight per wavefront without registers and merges through LDS.
+constexpr int64_t kPairBytesLds = 512 << 10;
 
 template <typename S>
-__global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodeParams p) {
+__global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(DecodeParams p) {
   using Out = typename S::OutElem;
+  constexpr int NW = pair_waves<S>();
   const int H = p.vheads;
   const int b = blockIdx.x / H;
   const int g = blockIdx.x - b * H;
@@ -1298,32 +1330,32 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
   Cursor cur;
   cur.dense_T = 0;
   cur.b = b;
-  // LDS-staged stream: wavefront w < min(n, 8) takes chunks w, w + 8, ...
+  // LDS-staged stream: wavefront w < min(n, NW) takes chunks w, w + NW, ...
   // (so its first chunks are known before the length is), and the table
-  // entries of chunks w, w + 8 and w + 16 are loaded together with the
+  // entries of its first kLdsSlots + 1 chunks are loaded together with the
   // length.  Indices are clamped into the table row; an entry of a chunk
   // that does not exist is never used.
-  int pre[3][S::kPh];
+  int pre[kLdsSlots + 1][S::kPh];
   if constexpr (S::kLdsStream) {
     const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
     const unsigned bs = (unsigned)p.pool.block_size, last = (unsigned)p.max_blocks_per_seq - 1;
 #pragma unroll
-    for (int k = 0; k < 3; ++k)
+    for (int k = 0; k <= kLdsSlots; ++k)
 #pragma unroll
       for (int t = 0; t < S::kPh; ++t)
-        pre[k][t] = uni(trow[min((unsigned)((w + kPairWaves * k) * S::kChunk + 16 * t) / bs, last)]);
+        pre[k][t] = uni(trow[min((unsigned)((w + NW * k) * S::kChunk + 16 * t) / bs, last)]);
   }
   cur.T = uni(lens[b]);
   cur.pos = poss ? uni(poss[b]) : -1;
   cur.nb = chunks_of(cur.T, S::kChunk);
   const int n = cur.nb;
-  const int A = min(n, kPairWaves);   // wavefronts with chunks (uniform over the workgroup)
+  const int A = min(n, NW);   // wavefronts with chunks (uniform over the workgroup)
   // Fused append: the last wavefront stores the new K/V rows of the pool
   // head (one 16-byte unit per lane) once the workgroup is done; its loads
   // are issued here so that they are in hand by then.
   constexpr int D = S::kDim;
   const int row_units = D * (int)sizeof(Out) / 16;   // 16-byte units per row
-  const bool app_row = S::kAppend && w == kPairWaves - 1 && cur.pos >= 0 &&
+  const bool app_row = S::kAppend && w == NW - 1 && cur.pos >= 0 &&
                        (p.qsplit == 1 || g % p.qsplit == 0);
   uint4 row_unit = make_uint4(0, 0, 0, 0);
   int row_phys = 0;
@@ -1342,17 +1374,20 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
       extern __shared__ __attribute__((aligned(16))) unsigned char pair_lds[];
       const uint32_t slot0 =
           (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)pair_lds +
-          (uint32_t)w * 2 * S::kSlotBytes;
+          (uint32_t)w * kLdsSlots * S::kSlotBytes;
       // a tile that starts at or past T takes its chunk's first block (it is
-      // masked); chunks w + 8 and w + 16 are used only when A == 8
+      // masked); chunks past w are used only when A == NW
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
+      for (int k = 0; k <= kLdsSlots; ++k)
 #pragma unroll
         for (int t = 1; t < S::kPh; ++t)
-          if ((w + kPairWaves * k) * S::kChunk + 16 * t >= cur.T) pre[k][t] = pre[k][0];
+          if ((w + NW * k) * S::kChunk + 16 * t >= cur.T) pre[k][t] = pre[k][0];
+      PairChunks pc;
+      pc.w = w;
+      pc.stride = A;
       cur.j = w;
-      stream_pair_lds<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, cur, A, (n - 1 - w) / A + 1,
-                         pre[0], pre[1], pre[2], slot0);
+      stream_pair_lds<S, kLdsSlots>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, cur, pc,
+                                    (n - 1 - w) / A + 1, pre, slot0);
     } else {
       cur.j = w * n / A;
       stream_chunks<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, nullptr, lens, poss, cur,
@@ -1364,19 +1399,19 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
   constexpr int DPL = (D + 63) / 64;   // dims per lane in the merge
   Out* out = static_cast<Out*>(p.out) + ((int64_t)b * p.num_q_heads + vh.first) * D;
   if (A == 0) {
-    for (int hn = w; hn < vh.count; hn += kPairWaves)
+    for (int hn = w; hn < vh.count; hn += NW)
       for (int d = lane; d < D; d += 64) out[(int64_t)hn * D + d] = (Out)0.f;
   } else if (A > 1) {
     __syncthreads();   // the A partials are written (workgroup-scope release and acquire)
     const int G = p.group;   // partial slot stride
-    for (int hn = w; hn < vh.count; hn += kPairWaves) {
-      float mv[kPairWaves], lv[kPairWaves], ov[kPairWaves][DPL];
+    for (int hn = w; hn < vh.count; hn += NW) {
+      float mv[NW], lv[NW], ov[NW][DPL];
 #pragma unroll
-      for (int u = 0; u < kPairWaves; ++u) {
+      for (int u = 0; u < NW; ++u) {
         const int k = min(u, A - 1);   // copies past A are not folded
         if constexpr (S::kLdsStream) {   // wavefront k's partial, in its LDS slots
           extern __shared__ __attribute__((aligned(16))) unsigned char pair_lds[];
-          const float* part = reinterpret_cast<const float*>(pair_lds + (size_t)k * 2 * S::kSlotBytes);
+          const float* part = reinterpret_cast<const float*>(pair_lds + (size_t)k * kLdsSlots * S::kSlotBytes);
           mv[u] = part[vh.count * D + 2 * hn];
           lv[u] = part[vh.count * D + 2 * hn + 1];
 #pragma unroll
@@ -1399,7 +1434,7 @@ __global__ __launch_bounds__(64 * kPairWaves) void decode_pair_kernel(DecodePara
 #pragma unroll
       for (int i = 0; i < DPL; ++i) a[i] = 0.f;
 #pragma unroll
-      for (int u = 0; u < kPairWaves; ++u) {
+      for (int u = 0; u < NW; ++u) {
         if (u < A) {
           const float Mn = fmaxf(M, mv[u]);
           const float sc = __builtin_amdgcn_exp2f(M - Mn);
@@ -1466,20 +1501,20 @@ bool launch_pairs(const DecodeParams& p, int64_t pairs, hipStream_t s) {
     hipFuncAttributes a;
     return hipFuncGetAttributes(&a, fn) == hipSuccess && a.localSizeBytes == 0;
   }();
-  const size_t lds = S::kLdsStream ? (size_t)kPairWaves * 2 * S::kSlotBytes : 0;
+  constexpr int NW = pair_waves<S>();
+  const size_t lds = S::kLdsStream ? (size_t)NW * kLdsSlots * S::kSlotBytes : 0;
   int resident = 0;
   if (!spill_free || (kPairWaves - 1) * pairs > kMaxWaves ||
-      resident_workgroups(fn, 64 * kPairWaves, lds, &resident) != hipSuccess || pairs > resident)
+      resident_workgroups(fn, 64 * NW, lds, &resident) != hipSuccess || pairs > resident)
     return false;
-  hipLaunchKernelGGL((decode_pair_kernel<S>), dim3((unsigned)pairs), dim3(64 * kPairWaves), lds, s,
-                     p);
+  hipLaunchKernelGGL((decode_pair_kernel<S>), dim3((unsigned)pairs), dim3(64 * NW), lds, s, p);
   return true;
 }
 
 // Pass 1 for stream type S.  When p.pair_mode asks for it, the per-pair
 // kernel runs if the longest sequence the block tables allow holds at most
-// kPairBytesPerWave (kPairBytesPerWaveLds for the LDS-staged stream) of K
-// and V per wavefront; otherwise p.pair_mode is cleared and the persistent
+// kPairWaves * kPairBytesPerWave of K and V per pair (kPairBytesLds for the
+// LDS-staged stream); otherwise p.pair_mode is cleared and the persistent
 // kernel runs on wgs workgroups.
 template <typename S>
 void launch_one(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
@@ -1488,8 +1523,8 @@ void launch_one(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
       const int64_t pairs = (int64_t)p.batch * p.vheads;
       const int64_t bytes = 2 * (int64_t)p.max_blocks_per_seq * p.pool.block_size *
                             p.pool.head_dim * (p.dtype == PAGEDKV_F32 ? 4 : 2);
-      const int64_t per_wave = S::kLdsStream ? kPairBytesPerWaveLds : kPairBytesPerWave;
-      if (bytes <= kPairWaves * per_wave && launch_pairs<S>(p, pairs, s)) return;
+      const int64_t limit = S::kLdsStream ? kPairBytesLds : kPairWaves * kPairBytesPerWave;
+      if (bytes <= limit && launch_pairs<S>(p, pairs, s)) return;
     }
   }
   p.pair_mode = 0;

@@ -1,6 +1,7 @@
-"""The per-pair decode split (one workgroup of 8 wavefronts per (sequence,
-KV head) pair, which merges its own pieces) against the oracle, next to the
-persistent chunk split on the same inputs.
+"""The per-pair decode split (one workgroup per (sequence, KV head) pair,
+which merges its own pieces: 8 wavefronts, or 4 with the LDS-staged stream
+at head_dim 64) against the oracle, next to the persistent chunk split on
+the same inputs.
 
 Which split ran is read off the workspace: the chunk split's pass 1 writes
 the per-sequence chunk prefix at the start of the workspace, the per-pair
@@ -68,7 +69,7 @@ def reference(w):
 
 
 PAIR_KV_BYTES = 256 << 10       # per (sequence, KV head): 8 wavefronts x 32 KiB
-PAIR_KV_BYTES_LDS = 512 << 10   # the LDS-staged stream: 8 wavefronts x 64 KiB
+PAIR_KV_BYTES_LDS = 512 << 10   # the LDS-staged stream: 4 wavefronts x 128 KiB
 
 
 def pair_kv_bytes(dtype, D, BS):
@@ -87,12 +88,13 @@ def longest_pair_tokens(dtype, D, BS):
 
 def pair_lens(dtype, D, BS):
     """Lengths giving 0 chunks, 1 chunk (one wavefront sees the pair whole),
-    2..7 chunks (fewer pieces than wavefronts), 8 and more (uneven pieces)
-    and the longest pair the per-pair kernel takes."""
+    2..7 chunks (fewer pieces than wavefronts), 8 and more (uneven pieces,
+    and with the LDS-staged stream more chunks per wavefront than it has
+    slots) and the longest pair the per-pair kernel takes."""
     c = 16 if dtype == "f32" else 32   # tokens per chunk at head_dim <= 128
     top = longest_pair_tokens(dtype, D, BS)
     lens = [0, 1, c - 1, c, c + 1, 3 * c + 5, 7 * c, 8 * c, 8 * c + 1, 12 * c + 3, 16 * c,
-            16 * c + 1, top - 1, top]
+            16 * c + 1, 26 * c - 3, top - 1, top]
     assert top >= 8 * c + 1
     return sorted(set(t for t in lens if t <= top))
 
