@@ -53,44 +53,44 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # otherwise the JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 542164173,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 542161306,
     },
     "long_context_bf16": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 2211046093,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 2211059098,
     },
     "churned_pool_bf16_gqa7": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 19326566,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 19377357,
     },
     "high_concurrency_bf16": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 3819974963,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 3820024320,
     },
     "tiny_fp32_mha": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
         "bytes": 630374,
     },
     "llama8b_decode_f32": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 1146568806,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 1146534502,
     },
     "llama8b_decode_f16": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 582661325,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 582648832,
     },
     "gemma_like_d256_bf16": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 1134509978,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 1134173082,
     },
     "mqa32_decode_bf16": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 85687296,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 85686886,
     },
     "mqa32_high_concurrency_bf16": {
-        "kernel_sha256": "70d48a06fc7dd52c59085acc65b5799b276fa5644bdb456f54af465885a0aa6a",
-        "bytes": 483666637,
+        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
+        "bytes": 483646259,
     },
 }
 
