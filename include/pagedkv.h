@@ -272,10 +272,12 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * one kernel does the whole call.  That applies at head_dim 64, 96 or 128
  * with at most 16 query heads per wavefront, when every pair's workgroup is
  * resident at once and the longest sequence the block tables allow,
- * max_blocks_per_seq * block_size tokens, holds at most 256 KiB of K and V
- * per KV head (1024 tokens at head_dim 64 in bf16 or fp16, 512 at 128; 512
- * and 256 in fp32); flags = PAGEDKV_DECODE_CHUNKS keeps every call on the
- * chunk split (below).
+ * max_blocks_per_seq * block_size tokens, holds at most 512 KiB of K and V
+ * per KV head at head_dim 64 in bf16 or fp16 with block_size a multiple of
+ * 16 (2048 tokens; these pairs stage K and V through LDS), else 256 KiB
+ * (1024 tokens at head_dim 64 in bf16 or fp16 with 4- or 8-token blocks,
+ * 512 at 128; 512 and 256 in fp32); flags = PAGEDKV_DECODE_CHUNKS keeps
+ * every call on the chunk split (below).
  * Kernels: MFMA for head_dim 64 or 128 with block_size a multiple of 16
  * (bf16, fp16, fp32), and in bf16 and fp16 also for head_dim 96 and 256 and
  * for block_size 4 or 8; a VALU kernel for head_dim up to 256 in steps of 4
