@@ -187,3 +187,48 @@ def test_pair_split_named_small_workloads():
         assert wrote != expect_pairs, f"workload {idx}: unexpected split"
         assert_attention_close(out, reference(w), w.dtype, what=f"workload {idx}",
                                vmax=workload_vmax(w))
+
+
+def _score_pattern_workload(dtype):
+    """Four sequences on the LDS-staged per-pair stream (bf16/fp16, head_dim
+    64, 16-token blocks, 7 query heads per KV head) whose scores follow set
+    patterns: every query row is 1.0 in dim 0 and 0 elsewhere, and K's dim 0
+    is chosen so that scale * q.k_t = s(t) for every head.  The patterns make
+    the running max grow in every chunk (s = 0.01 t), never after the first
+    (s = -0.01 t), jump by 15 (21.6 in log2 units, past the lazy-rescale
+    threshold of 8) halfway, and grow by 4.5 in all (6.5 in log2 units, under
+    the threshold), so that probabilities above 1 meet the stale reference."""
+    from workloads import bf16_round_bits
+    lens = [2048, 2048, 2048, 1500]
+    w = workload(dtype, 14, 2, 64, 16, lens)
+    patterns = [lambda t: 0.01 * t, lambda t: -0.01 * t,
+                lambda t: np.where(t < 1024, 0.0, 15.0), lambda t: 0.003 * t]
+    store = (lambda x: bf16_round_bits(np.asarray(x, np.float32))) if dtype == "bf16" else \
+        (lambda x: np.asarray(x, np.float16))
+    q = np.zeros((w.S, w.Hq, w.D), np.float32)
+    q[:, :, 0] = 1.0
+    w.q = store(q)
+    for b, f in enumerate(patterns):
+        t = np.arange(int(w.context_lens[b]))
+        blks = w.block_tables[b, t // w.BS]
+        offs = t % w.BS
+        k0 = store(np.asarray(f(t), np.float32) / np.float32(w.scale))
+        w.pool[blks, 0, w.layer, :, offs, 0] = k0[:, None]
+    return w
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_lds_stream_running_max_patterns(dtype):
+    """The LDS-staged stream's rescale taken only when a column's max grows
+    past the threshold, and the normaliser summed by the MFMA unit, against
+    the oracle and the chunk split on score patterns that force each path."""
+    say(f"LDS stream running-max patterns {dtype}")
+    w = _score_pattern_workload(dtype)
+    dw = DeviceWorkload(w)
+    ref = reference(w)
+    out_p, wrote_p = decode_with(dw, pk.SPLIT_AUTO)
+    out_c, wrote_c = decode_with(dw, pk.SPLIT_CHUNKS)
+    assert not wrote_p and wrote_c
+    vmax = workload_vmax(w)
+    assert_attention_close(out_p, ref, dtype, what="per-pair, score patterns", vmax=vmax)
+    assert_attention_close(out_c, ref, dtype, what="chunk split, score patterns", vmax=vmax)
