@@ -232,3 +232,38 @@ def test_lds_stream_running_max_patterns(dtype):
     vmax = workload_vmax(w)
     assert_attention_close(out_p, ref, dtype, what="per-pair, score patterns", vmax=vmax)
     assert_attention_close(out_c, ref, dtype, what="chunk split, score patterns", vmax=vmax)
+
+
+def _random_pair_cases(n=24, seed=2024):
+    """Seeded shapes for the LDS-staged per-pair stream: 16-bit, head_dim 64,
+    block sizes that are multiples of 16 (48 and 80 among them, so a table
+    entry is found by a true division), 1 to 16 query heads per KV head,
+    lengths from 0 up to the 512 KiB per-pair limit."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        dtype = ["bf16", "f16"][i % 2]
+        BS = int(rng.choice([16, 32, 48, 64, 80]))
+        Hkv = int(rng.choice([1, 2, 4, 8]))
+        G = int(rng.integers(1, 17))
+        S = int(rng.integers(1, 24))
+        top = (512 << 10) // (2 * 64 * 2) // BS * BS
+        lens = rng.integers(0, top + 1, size=S)
+        lens[rng.integers(0, S)] = int(rng.integers(top // 2, top + 1))   # one long pair
+        cases.append((dtype, G * Hkv, Hkv, BS, [int(x) for x in lens]))
+    return cases
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_lds_stream_random_shapes(case):
+    dtype, Hq, Hkv, BS, lens = _random_pair_cases()[case]
+    say(f"LDS stream random case {case}: {dtype} Hq={Hq} Hkv={Hkv} BS={BS} S={len(lens)} "
+        f"max T={max(lens)}")
+    w = workload(dtype, Hq, Hkv, 64, BS, lens, L=2, layer=1)
+    dw = DeviceWorkload(w)
+    out, wrote = decode_with(dw, pk.SPLIT_AUTO)
+    assert not wrote, "expected the per-pair split"
+    assert_attention_close(out, reference(w), dtype, what=f"random case {case}",
+                           vmax=workload_vmax(w))
+    zero_rows = [i for i, t in enumerate(lens) if t == 0]
+    assert not dev_to_np(out)[zero_rows].any(), "empty sequences must give zero rows"
