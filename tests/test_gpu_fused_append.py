@@ -91,6 +91,8 @@ def test_fused_step_named_workloads(idx, S, split):
 SHAPES = [
     ("bf16", 8, 2, 128, 16),
     ("bf16", 14, 2, 64, 32),
+    ("f16", 14, 2, 64, 16),     # small batches here take the LDS-staged per-pair stream
+    ("bf16", 7, 1, 64, 48),     # the same with 48-token blocks
     ("bf16", 16, 1, 128, 16),
     ("bf16", 8, 2, 64, 8),
     ("f32", 8, 2, 64, 16),
