@@ -39,9 +39,10 @@ def decode_noalloc(dw, flags: int) -> torch.Tensor:
 @pytest.mark.parametrize("flags", [0, _lib.DECODE_CHUNKS])
 def test_noalloc_matches_workspace_decode_two_calls(flags):
     """First the full Llama-shaped batch (64 sequences, 18 MB of scratch),
-    then a 6-sequence batch of the same shape, then the tiny fp32 batch:
+    then a 6-sequence batch of the same shape, then the churned-pool batch
+    (the LDS-staged per-pair stream, by default) and the tiny fp32 batch:
     each noalloc call against the workspace call and the oracle."""
-    cases = [(2, {}), (2, {"S": 6, "seed_offset": 3}), (0, {})]
+    cases = [(2, {}), (2, {"S": 6, "seed_offset": 3}), (1, {}), (0, {})]
     for idx, over in cases:
         say(f"noalloc decode workload {idx} {over} flags={flags}")
         w = make_workload(idx, **over)
