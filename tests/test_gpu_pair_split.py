@@ -267,3 +267,18 @@ def test_lds_stream_random_shapes(case):
                            vmax=workload_vmax(w))
     zero_rows = [i for i, t in enumerate(lens) if t == 0]
     assert not dev_to_np(out)[zero_rows].any(), "empty sequences must give zero rows"
+
+
+@pytest.mark.parametrize("S,expect_pairs", [(128, True), (129, False)])
+def test_lds_stream_resident_limit(S, expect_pairs):
+    """The LDS-staged stream takes 128 KiB of LDS per workgroup, one per CU:
+    256 (sequence, KV head) pairs fit on the 256 CUs at once, 258 do not and
+    run on the chunk split; both against the oracle."""
+    say(f"LDS stream resident limit: {S} sequences x 2 KV heads")
+    rng = np.random.default_rng(S)
+    lens = rng.integers(0, 300, size=S)
+    w = workload("bf16", 14, 2, 64, 16, lens)
+    dw = DeviceWorkload(w)
+    out, wrote = decode_with(dw, pk.SPLIT_AUTO)
+    assert wrote != expect_pairs
+    assert_attention_close(out, reference(w), "bf16", what=f"{S} sequences")
