@@ -527,6 +527,29 @@ def measure_step(torch, pk, name: str, steps: int, warmup: int, split: str, rota
     return rec, reps
 
 
+def measure_layer_rotation(torch, pk, reps, split: str, rounds: int = 8) -> dict:
+    """The same fused step on replica 0's pool, attending each of its layers
+    in turn back to back.  The replicas of a small workload fit in the 256 MB
+    Infinity Cache together, so its step timings see K/V that stayed in the
+    cache since the previous step; cycling over every layer of the pool (a
+    model's other layers do the same between two uses of one layer) moves
+    that many distinct K/V bytes."""
+    r = reps[0]
+    w = r["w"]
+    plans = [pk.DecodePlan(r["out"], r["q"], r["pool"], layer, r["tables"], r["lens"], w.scale,
+                           r["k"], r["v"], r["pos"], split=split) for layer in range(w.L)]
+    n = rounds * w.L
+    ms = back_to_back_ms(torch, lambda i: plans[i % w.L].run(), n)
+    step_bytes = decode_bytes(w) + append_bytes(w)
+    return {
+        "what": f"the fused step attending layers 0..{w.L - 1} of one pool in turn, back to back",
+        "layers": w.L,
+        "distinct_kv_MB": round(w.L * (decode_bytes(w) + append_bytes(w)) / 1e6, 1),
+        "call_ms": round(ms, 5),
+        "GB_per_s": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+    }
+
+
 def measure_append_only(torch, pk, reps, n: int = 200) -> dict:
     """kv_append of one new token per sequence on its own (one launch).
     `ms_host_loop`: back to back from Python (each call goes through the
@@ -821,6 +844,7 @@ def main(argv=None) -> int:
                                      args.rotate, graph=False)
             if name == "churned_pool_bf16_gqa7":
                 rec["append_only"] = measure_append_only(torch, pk, reps)
+                rec["all_layers_rotated"] = measure_layer_rotation(torch, pk, reps, args.split)
             rec["decode_only_call_ms"] = measure_decode_only(torch, pk, reps, args.split)
             out["workloads"][name] = rec
             print(f"[bench] {name}: {rec['ms_per_step'] * 1e3:.1f} us/step, "
@@ -884,6 +908,7 @@ def main(argv=None) -> int:
         sub.pop("dtype", None)
         if name == "churned_pool_bf16_gqa7":
             sub["append_only"] = measure_append_only(torch, pk, sreps)
+            sub["all_layers_rotated"] = measure_layer_rotation(torch, pk, sreps, args.split)
             sub["decode_only_call_ms"] = measure_decode_only(torch, pk, sreps, args.split)
         subs[name] = sub
         del sreps
