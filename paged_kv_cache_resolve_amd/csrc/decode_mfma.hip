@@ -1598,7 +1598,12 @@ void launch_f32(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
 
 hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
   const size_t lds = mfma_lds_bytes(p.batch);
-  // instantiations of one head_dim have the same resources: size the grid by one
+  // The grid is kDecodeWgPerCu (1) workgroup per CU, capped by what one
+  // instantiation of this head_dim holds at once.  Every instantiation holds
+  // at least one workgroup per CU (its registers fit one wavefront per SIMD),
+  // so the grid is resident whichever one runs, although they differ in
+  // registers: the two-column-group streams hold one wavefront per SIMD
+  // where the others hold two to four.
   const void* fn =
       p.pool.head_dim == 256
           ? reinterpret_cast<const void*>(&decode_mfma_kernel<Stream<Bf16Ops, 256, kTilesD256, false>>)
