@@ -475,35 +475,31 @@ struct Stream {
   // the chunk is computed.
   static constexpr bool kLdsStream = !DENSE && !SMALL && D == 64 && NC == 1 && TILES == 2;
   static constexpr uint32_t kSlotBytes = 2 * TILES * 16 * D * 2;   // K then V of one chunk
-
-  // Block-table entries of chunk c's tiles for the LDS-staged stream: the
-  // block of each tile's first token, clamped to the sequence's last token
-  // (a tile past T is masked, so any block of the sequence will do).  Unlike
-  // fetch_phys, no entry is chosen by another loaded value, so the scalar
-  // loads are waited for only where the entries are used.
-  __device__ __forceinline__ void fetch_phys_clamped(const Cursor& c, int* ph) const {
-    const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
-    const unsigned bs = (unsigned)p.pool.block_size;
-#pragma unroll
-    for (int t = 0; t < TILES; ++t) {
-      const int tok = min(c.j * kChunk + 16 * t, c.T - 1);
-      ph[t] = uni(trow[(unsigned)tok / bs]);
-    }
-  }
+  // With VS (one of two workgroups of a pair, each with half of V's dims):
+  // K and that half of V
+  template <bool VS>
+  static constexpr uint32_t slot_bytes() { return VS ? kSlotBytes / 4 * 3 : kSlotBytes; }
+  // LDS-direct loads per chunk
+  template <bool VS>
+  static constexpr int chunk_loads() { return VS ? 6 : 8; }
 
   // Copy chunk c into the slot at LDS byte address `slot`.  Tile t's K rows
   // go to slot + t * 2 KiB, its V rows to slot + (TILES + t) * 2 KiB: 16
   // rows of 128 bytes, row r's 16-byte column q stored at column q ^ (r & 7)
   // (so that the reads below hit distinct banks).  Unit u = 64 h + lane of
-  // instruction h is LDS column u & 7 of row u >> 3.  The appended token's
-  // row comes from k_new / v_new, as in issue_k / issue_v; whether the chunk
-  // holds it is wave-uniform, so other chunks take the form without the
-  // per-lane choice.
-  template <bool OVR>
-  __device__ __forceinline__ void dma_tiles(const Cursor& c, const int* ph, uint32_t slot) const {
+  // instruction h is LDS column u & 7 of row u >> 3.  With VS only half
+  // `dhalf` of each V row is copied (dims 32 dhalf .. 32 dhalf + 31, 64 bytes),
+  // tile t to slot + TILES * 2 KiB + t * 1 KiB in one load: unit u = lane is
+  // LDS column u & 3 of row u >> 2 and holds the half's 16-byte column
+  // (u & 3) ^ (r & 3).  The appended token's row comes from k_new / v_new,
+  // as in issue_k / issue_v; whether the chunk holds it is wave-uniform, so
+  // other chunks take the form without the per-lane choice.
+  template <bool OVR, bool VS>
+  __device__ __forceinline__ void dma_tiles(const Cursor& c, const int* ph, uint32_t slot,
+                                            int dhalf) const {
     typedef __attribute__((address_space(3))) void* lds_ptr;
 #pragma unroll
-    for (int kv = 0; kv < 2; ++kv)
+    for (int kv = 0; kv < (VS ? 1 : 2); ++kv)
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
 #pragma unroll
@@ -519,29 +515,55 @@ struct Stream {
           __builtin_amdgcn_global_load_lds(
               src, (lds_ptr)(uintptr_t)(slot + (uint32_t)((kv * TILES + t) * 2048 + h * 1024)), 16, 0, 0);
         }
+    if constexpr (VS) {
+      const int r = lane >> 2;
+      const int q = (lane & 3) ^ (r & 3);
+#pragma unroll
+      for (int t = 0; t < TILES; ++t) {
+        const char* src = tile_base(c, ph, t) + 2 * p.pool.kv_stride +
+                          (uint32_t)(2 * r * D + 64 * dhalf + 16 * q);
+        if constexpr (OVR) {
+          if (c.j * kChunk + 16 * t + r == c.pos) src = new_row(c, 1) + 64 * dhalf + 16 * q;
+        }
+        __builtin_amdgcn_global_load_lds(
+            src, (lds_ptr)(uintptr_t)(slot + (uint32_t)(TILES * 2048 + t * 1024)), 16, 0, 0);
+      }
+    }
   }
-  __device__ __forceinline__ void dma_chunk(const Cursor& c, const int* ph, uint32_t slot) const {
+  template <bool VS = false>
+  __device__ __forceinline__ void dma_chunk(const Cursor& c, const int* ph, uint32_t slot,
+                                            int dhalf = 0) const {
     if (APPEND && (unsigned)(c.pos - c.j * kChunk) < (unsigned)kChunk)
-      dma_tiles<APPEND>(c, ph, slot);
+      dma_tiles<APPEND, VS>(c, ph, slot, dhalf);
     else
-      dma_tiles<false>(c, ph, slot);
+      dma_tiles<false, VS>(c, ph, slot, dhalf);
   }
 
   // A lane's LDS read addresses in slot 0 of its wavefront; the other slot
   // and the tiles are immediate offsets.  Lane (n, quad) takes K row n,
   // columns quad and quad + 4 of each tile, and V rows 4 quad + r, bytes
-  // 8n .. 8n+7: the layouts issue_k and issue_v load.
+  // 8n .. 8n+7: the layouts issue_k and issue_v load.  With VS, the lanes
+  // n in [8 dhalf, 8 dhalf + 8) hold the half of V that is staged; they feed
+  // the accumulators of dims 32 dhalf .. 32 dhalf + 31 (quads 2 dhalf and
+  // 2 dhalf + 1).  The other lanes read the same rows of that half, and the
+  // dims they feed are never written out.
   struct LdsLane {
     uint32_t k[2], v[4];
   };
-  __device__ __forceinline__ LdsLane lds_lane(uint32_t slot0) const {
+  template <bool VS = false>
+  __device__ __forceinline__ LdsLane lds_lane(uint32_t slot0, int dhalf = 0) const {
     LdsLane a;
 #pragma unroll
     for (int i = 0; i < 2; ++i) a.k[i] = slot0 + (uint32_t)((n * 8 + ((quad + 4 * i) ^ (n & 7))) * 16);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * quad + r;
-      a.v[r] = slot0 + (uint32_t)(TILES * 2048 + (row * 8 + ((n >> 1) ^ (row & 7))) * 16 + (n & 1) * 8);
+      if constexpr (VS) {
+        const int nh = (n - 8 * dhalf) & 7;
+        a.v[r] = slot0 + (uint32_t)(TILES * 2048 + row * 64 + ((nh >> 1) ^ (row & 3)) * 16 + (n & 1) * 8);
+      } else {
+        a.v[r] = slot0 + (uint32_t)(TILES * 2048 + (row * 8 + ((n >> 1) ^ (row & 7))) * 16 + (n & 1) * 8);
+      }
     }
     return a;
   }
@@ -550,10 +572,11 @@ struct Stream {
   // written as asm with their wait inside, because the compiler would
   // otherwise wait for every LDS-direct load in flight (it cannot tell the
   // slots apart) before each LDS read.
-  template <int SLOT>
+  template <int SLOT, bool VS = false>
   __device__ __forceinline__ void read_chunk(Buf& cb, const LdsLane& a) const {
     static_assert(TILES == 2, "two tiles per chunk");
-    constexpr int O = SLOT * (int)kSlotBytes;
+    constexpr int O = SLOT * (int)slot_bytes<VS>();
+    constexpr int OV1 = O + (VS ? 1024 : 2048);   // V tile 1
     typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
     typedef unsigned u32x2_v __attribute__((ext_vector_type(2)));
     u32x4_v k[TILES][2];
@@ -583,7 +606,7 @@ struct Stream {
         "s_waitcnt lgkmcnt(0)"
         : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
           "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
-        : "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]), "i"(O), "i"(O + 2048)
+        : "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]), "i"(O), "i"(OV1)
         : "memory");
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
@@ -787,12 +810,16 @@ struct Stream {
   }
 
   // Column group cg's share of flush: head 16*cg + n of this (virtual) KV head.
-  __device__ __forceinline__ void flush_cols(const Cursor& c, bool whole, int cg, float lt) {
+  // dhalf >= 0 (a workgroup with half of V's dims, whole sequences only):
+  // only the lanes of dims 32 dhalf .. 32 dhalf + 31 write.
+  __device__ __forceinline__ void flush_cols(const Cursor& c, bool whole, int cg, float lt,
+                                             int dhalf = -1) {
     const int G = p.group;   // partial slot stride
     const int hc = 16 * cg + n;
     const f32x4_t* a = acc[cg];
     // lane holds dims kQuadDims*quad + kRowDims*r + (i % 8) + kHalfDims*(i / 8)
     // of head hc as a[i][r]
+    if (dhalf >= 0 && (quad >> 1) != dhalf) return;
     if (whole) {
       const float inv = DENSE && lt == 0.f ? 0.f : 1.0f / lt;   // dense: all masked -> zeros
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
@@ -1139,17 +1166,17 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// Wait until at most `newer` chunk copies (8 LDS-direct loads each) issued
-// after the oldest one are still in flight, for newer in [0, K].
-template <int K>
+// Wait until at most `newer` chunk copies (LPC LDS-direct loads each)
+// issued after the oldest one are still in flight, for newer in [0, K].
+template <int K, int LPC>
 __device__ __forceinline__ void wait_newer_chunks(int newer) {
   if constexpr (K == 0) {
     wait_vmcnt<0>();
   } else {
     if (newer >= K)
-      wait_vmcnt<8 * K>();
+      wait_vmcnt<LPC * K>();
     else
-      wait_newer_chunks<K - 1>(newer);
+      wait_newer_chunks<K - 1, LPC>(newer);
   }
 }
 
@@ -1160,16 +1187,20 @@ __device__ __forceinline__ void wait_newer_chunks(int newer) {
 // chunk's copy is 8 LDS-direct loads (K and V, two tiles, two 1 KiB rows of
 // lanes each), and vector-memory operations complete in issue order, so
 // chunk i is in LDS once at most the loads of the chunks copied after it
-// are still in flight.  pre[k] holds the block-table entries of chunk k for
-// k <= NS (loaded by the caller with the sequence's length); later entries
-// are fetched one chunk ahead of their copy.  The loop runs NS chunks per
-// pass so that each read has its slot as an immediate offset.
+// are still in flight.  Lane 2k + t of `ent` holds the block-table entry of
+// tile t of the wavefront's k-th chunk (loaded by the caller with the
+// sequence's length), so the loop makes no table loads: a scalar load
+// issued in one step would be waited for by the next step's LDS reads
+// (s_waitcnt lgkmcnt counts both), which put its latency on every chunk.
+// The loop runs NS chunks per pass so that each read has its slot as an
+// immediate offset.
 template <int P> struct SlotTag { static constexpr int value = P; };
 
 // Chunks of one wavefront of the per-pair LDS-staged stream: w, w + A,
-// w + 2A, ... for the A = min(n, 8) wavefronts with chunks.  Its first
-// three chunks, w, w + 8 and w + 16, do not depend on the pair's chunk
-// count n (with A < 8 each wavefront has at most one).  (Rounds that gave
+// w + 2A, ... for the A = min(n, NW) of the workgroup's NW wavefronts that
+// have chunks.  They are w, w + NW, w + 2 NW, ... whatever the pair's chunk
+// count n (with A < NW each wavefront has at most one), so their table
+// entries can be loaded before n is known.  (Rounds that gave
 // wavefronts 0..3, the first of each SIMD, four chunks for every three of
 // the others were slower: churned pool 10.75 -> 11.5 us.)
 struct PairChunks {
@@ -1177,41 +1208,53 @@ struct PairChunks {
   __device__ __forceinline__ int at(int i) const { return w + i * stride; }
 };
 
-template <typename S, int NS>
+// With VS the workgroup stages half `dhalf` of V's dims (the other half is
+// its partner workgroup's) and writes only those dims of the output.
+template <typename S, int NS, bool VS>
 __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane, int g, int64_t unit,
-                                                Cursor cur, PairChunks pc, int rem,
-                                                const int (*pre)[S::kPh], uint32_t slot0) {
+                                                Cursor cur, PairChunks pc, int rem, int ent,
+                                                uint32_t slot0, int dhalf) {
   static_assert(NS == 1 || NS == 2 || NS == 4, "slots per wavefront");
   S st(p, lane, g, unit);
   st.reset();
   st.load_q(cur);
-  const typename S::LdsLane la = st.lds_lane(slot0);
+  const typename S::LdsLane la = st.template lds_lane<VS>(slot0, dhalf);
   typename S::Buf cb;
-  constexpr uint32_t SB = S::kSlotBytes;
+  constexpr uint32_t SB = S::template slot_bytes<VS>();
+  constexpr int LPC = S::template chunk_loads<VS>();
   const bool whole = cur.nb == 1;
-  int ph_nx[S::kPh];   // entries of the next chunk to copy (i + NS at step i)
-#pragma unroll
-  for (int t = 0; t < S::kPh; ++t) ph_nx[t] = pre[NS][t];
+  static_assert(S::kPh == 2, "two tiles per chunk");
+  // entries of the wavefront's k-th chunk; a tile that starts at or past T
+  // takes the chunk's first block (it is masked)
+  // the entries arrive before the first copy is issued: waiting for them
+  // here, on every path, keeps the compiler from waiting for all vector
+  // memory (copies included) at a later use
+  asm volatile("" ::"v"(ent));
+  auto chunk_blocks = [&](int k, int* ph) {
+    const int e = (2 * k) & 63;
+    ph[0] = __builtin_amdgcn_readlane(ent, e);
+    ph[1] = pc.at(k) * S::kChunk + 16 < cur.T ? __builtin_amdgcn_readlane(ent, e + 1) : ph[0];
+  };
 #pragma unroll
   for (int k = 0; k < NS; ++k)
     if (k < rem) {
       Cursor c = cur;
       c.j = pc.at(k);
-      st.dma_chunk(c, pre[k], slot0 + k * SB);
+      int ph[2];
+      chunk_blocks(k, ph);
+      st.template dma_chunk<VS>(c, ph, slot0 + k * SB, dhalf);
     }
   f32x4_t s[S::kTiles];
   auto step = [&](auto tag, int i) {
     constexpr int P = decltype(tag)::value;
-    wait_newer_chunks<NS - 1>(rem - 1 - i);
-    st.template read_chunk<P>(cb, la);
+    wait_newer_chunks<NS - 1, LPC>(rem - 1 - i);
+    st.template read_chunk<P, VS>(cb, la);
     if (i + NS < rem) {   // chunk i + NS into the slot just read
       Cursor c = cur;
       c.j = pc.at(i + NS);
-      st.dma_chunk(c, ph_nx, slot0 + P * SB);
-      if (i + NS + 1 < rem) {
-        c.j = pc.at(i + NS + 1);
-        st.fetch_phys_clamped(c, ph_nx);
-      }
+      int ph[2];
+      chunk_blocks(i + NS, ph);
+      st.template dma_chunk<VS>(c, ph, slot0 + P * SB, dhalf);
     }
     cur.j = pc.at(i);
     st.qk(cb, s);
@@ -1227,7 +1270,7 @@ __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane,
     }
   }
   if (whole) {
-    if (st.n < st.gw) st.flush_cols(cur, true, 0, st.lacc[0][0]);
+    if (st.n < st.gw) st.flush_cols(cur, true, 0, st.lacc[0][0], VS ? dhalf : -1);
   } else {   // the partial goes to this wavefront's own (now free) slots
     st.flush_lds(slot0);
   }
@@ -1315,14 +1358,34 @@ constexpr int64_t kPairBytesPerWave = 32 << 10;
 // 16-bit, blocks of a multiple of 16 tokens) is used; it keeps several
 // chunks in flight per wavefront without registers and merges through LDS.
 constexpr int64_t kPairBytesLds = 512 << 10;
+// Chunks (32 tokens of head_dim 64 in 16 bits: 8 KiB) per wavefront at most
+// on the LDS-staged stream with NW wavefronts: kPairBytesLds of K and V over
+// NW, rounded up.
+template <int NW>
+constexpr int lds_chunks_per_wave() {
+  return (int)((kPairBytesLds / (8 << 10) + NW - 1) / NW);
+}
+static_assert(2 * lds_chunks_per_wave<kLdsWaves>() <= 64, "one table entry per lane");
 
-template <typename S>
+// VS (LDS-staged stream only): two workgroups per pair, each staging K and
+// half of V's dims and writing those dims of the output rows; the halves of
+// pair pr are workgroups 16 (pr / 8) + pr % 8 and that + 8, which share an
+// XCD (workgroups go to the 8 XCDs round-robin), so their K reads meet in
+// one L2.  The grid is twice the pair count rounded up to a multiple of 8.
+template <typename S, bool VS = false>
 __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(DecodeParams p) {
   using Out = typename S::OutElem;
   constexpr int NW = pair_waves<S>();
+  static_assert(!VS || S::kLdsStream, "split V only with the LDS-staged stream");
   const int H = p.vheads;
-  const int b = blockIdx.x / H;
-  const int g = blockIdx.x - b * H;
+  int pr = blockIdx.x, dhalf = 0;
+  if constexpr (VS) {
+    pr = (int)(blockIdx.x >> 4) * 8 + (int)(blockIdx.x & 7);
+    dhalf = (int)(blockIdx.x >> 3) & 1;
+    if (pr >= p.batch * H) return;
+  }
+  const int b = pr / H;
+  const int g = pr - b * H;
   const int lane = threadIdx.x & 63;
   const int w = uni(threadIdx.x >> 6);
   const const_i32_ptr lens = (const_i32_ptr)p.context_lens;
@@ -1331,19 +1394,17 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
   cur.dense_T = 0;
   cur.b = b;
   // LDS-staged stream: wavefront w < min(n, NW) takes chunks w, w + NW, ...
-  // (so its first chunks are known before the length is), and the table
-  // entries of its first kLdsSlots + 1 chunks are loaded together with the
-  // length.  Indices are clamped into the table row; an entry of a chunk
-  // that does not exist is never used.
-  int pre[kLdsSlots + 1][S::kPh];
+  // (so its chunks are known before the length is), and one vector load
+  // issued together with the length brings the table entries of all of
+  // them: lane 2k + t takes tile t of chunk w + NW k, for the at most
+  // lds_chunks_per_wave<NW>() chunks a wavefront gets.  Indices are clamped into the
+  // table row; an entry of a chunk that does not exist is never used.
+  int ent = 0;
   if constexpr (S::kLdsStream) {
-    const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)b * p.max_blocks_per_seq);
+    const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
     const unsigned bs = (unsigned)p.pool.block_size, last = (unsigned)p.max_blocks_per_seq - 1;
-#pragma unroll
-    for (int k = 0; k <= kLdsSlots; ++k)
-#pragma unroll
-      for (int t = 0; t < S::kPh; ++t)
-        pre[k][t] = uni(trow[min((unsigned)((w + NW * k) * S::kChunk + 16 * t) / bs, last)]);
+    if (lane < 2 * lds_chunks_per_wave<NW>())
+      ent = trow[min((unsigned)((w + NW * (lane >> 1)) * S::kChunk + 16 * (lane & 1)) / bs, last)];
   }
   cur.T = uni(lens[b]);
   cur.pos = poss ? uni(poss[b]) : -1;
@@ -1355,7 +1416,7 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
   // are issued here so that they are in hand by then.
   constexpr int D = S::kDim;
   const int row_units = D * (int)sizeof(Out) / 16;   // 16-byte units per row
-  const bool app_row = S::kAppend && w == NW - 1 && cur.pos >= 0 &&
+  const bool app_row = S::kAppend && w == NW - 1 && cur.pos >= 0 && dhalf == 0 &&
                        (p.qsplit == 1 || g % p.qsplit == 0);
   uint4 row_unit = make_uint4(0, 0, 0, 0);
   int row_phys = 0;
@@ -1374,20 +1435,13 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
       extern __shared__ __attribute__((aligned(16))) unsigned char pair_lds[];
       const uint32_t slot0 =
           (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)pair_lds +
-          (uint32_t)w * kLdsSlots * S::kSlotBytes;
-      // a tile that starts at or past T takes its chunk's first block (it is
-      // masked); chunks past w are used only when A == NW
-#pragma unroll
-      for (int k = 0; k <= kLdsSlots; ++k)
-#pragma unroll
-        for (int t = 1; t < S::kPh; ++t)
-          if ((w + NW * k) * S::kChunk + 16 * t >= cur.T) pre[k][t] = pre[k][0];
+          (uint32_t)w * kLdsSlots * S::template slot_bytes<VS>();
       PairChunks pc;
       pc.w = w;
       pc.stride = A;
       cur.j = w;
-      stream_pair_lds<S, kLdsSlots>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, cur, pc,
-                                    (n - 1 - w) / A + 1, pre, slot0);
+      stream_pair_lds<S, kLdsSlots, VS>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, cur, pc,
+                                        (n - 1 - w) / A + 1, ent, slot0, dhalf);
     } else {
       cur.j = w * n / A;
       stream_chunks<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, nullptr, lens, poss, cur,
@@ -1400,7 +1454,8 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
   Out* out = static_cast<Out*>(p.out) + ((int64_t)b * p.num_q_heads + vh.first) * D;
   if (A == 0) {
     for (int hn = w; hn < vh.count; hn += NW)
-      for (int d = lane; d < D; d += 64) out[(int64_t)hn * D + d] = (Out)0.f;
+      for (int d = lane; d < D; d += 64)
+        if (!VS || d / 32 == dhalf) out[(int64_t)hn * D + d] = (Out)0.f;
   } else if (A > 1) {
     __syncthreads();   // the A partials are written (workgroup-scope release and acquire)
     const int G = p.group;   // partial slot stride
@@ -1411,7 +1466,8 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
         const int k = min(u, A - 1);   // copies past A are not folded
         if constexpr (S::kLdsStream) {   // wavefront k's partial, in its LDS slots
           extern __shared__ __attribute__((aligned(16))) unsigned char pair_lds[];
-          const float* part = reinterpret_cast<const float*>(pair_lds + (size_t)k * kLdsSlots * S::kSlotBytes);
+          const float* part = reinterpret_cast<const float*>(
+              pair_lds + (size_t)k * kLdsSlots * S::template slot_bytes<VS>());
           mv[u] = part[vh.count * D + 2 * hn];
           lv[u] = part[vh.count * D + 2 * hn + 1];
 #pragma unroll
@@ -1449,7 +1505,7 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
 #pragma unroll
       for (int i = 0; i < DPL; ++i) {
         const int d = lane + 64 * i;
-        if (d < D) out[(int64_t)hn * D + d] = (Out)(a[i] * inv);
+        if (d < D && (!VS || d / 32 == dhalf)) out[(int64_t)hn * D + d] = (Out)(a[i] * inv);
       }
     }
   }
@@ -1496,6 +1552,25 @@ namespace {
 // workgroup is resident at once.
 template <typename S>
 bool launch_pairs(const DecodeParams& p, int64_t pairs, hipStream_t s) {
+  if constexpr (S::kLdsStream) {
+    // two workgroups per pair (each with half of V's dims) while they all
+    // fit on the device at once
+    const void* fv = reinterpret_cast<const void*>(&decode_pair_kernel<S, true>);
+    static const bool spill_free_v = [fv] {
+      hipFuncAttributes a;
+      return hipFuncGetAttributes(&a, fv) == hipSuccess && a.localSizeBytes == 0;
+    }();
+    constexpr int NWV = pair_waves<S>();
+    const size_t ldsv = (size_t)NWV * kLdsSlots * S::template slot_bytes<true>();
+    const int64_t grid = 2 * ((pairs + 7) / 8 * 8);
+    int resident = 0;
+    if (spill_free_v && resident_workgroups(fv, 64 * NWV, ldsv, &resident) == hipSuccess &&
+        grid <= resident) {
+      hipLaunchKernelGGL((decode_pair_kernel<S, true>), dim3((unsigned)grid), dim3(64 * NWV), ldsv,
+                         s, p);
+      return true;
+    }
+  }
   const void* fn = reinterpret_cast<const void*>(&decode_pair_kernel<S>);
   static const bool spill_free = [fn] {
     hipFuncAttributes a;

@@ -1,7 +1,8 @@
-"""The per-pair decode split (one workgroup per (sequence, KV head) pair,
-which merges its own pieces: 8 wavefronts, or 4 with the LDS-staged stream
-at head_dim 64) against the oracle, next to the persistent chunk split on
-the same inputs.
+"""The per-pair decode split (one workgroup of 8 wavefronts per (sequence,
+KV head) pair, which merges its own pieces; at head_dim 64 in 16 bits the
+LDS-staged stream, whose pairs get two workgroups, each with half of V's
+dims, while those fit on the device at once) against the oracle, next to
+the persistent chunk split on the same inputs.
 
 Which split ran is read off the workspace: the chunk split's pass 1 writes
 the per-sequence chunk prefix at the start of the workspace, the per-pair
@@ -267,6 +268,39 @@ def test_lds_stream_random_shapes(case):
                            vmax=workload_vmax(w))
     zero_rows = [i for i, t in enumerate(lens) if t == 0]
     assert not dev_to_np(out)[zero_rows].any(), "empty sequences must give zero rows"
+
+
+@pytest.mark.parametrize("S", [64, 65])
+def test_lds_stream_split_v_limit(S):
+    """Two workgroups per pair (half of V's dims each) while twice the pair
+    count, rounded up to a multiple of 8, fits on the 256 CUs: 64 sequences x
+    2 KV heads (grid 256) take that form, 65 (grid 264) one workgroup per
+    pair.  Both against the oracle."""
+    say(f"LDS stream split-V limit: {S} sequences x 2 KV heads")
+    rng = np.random.default_rng(1000 + S)
+    lens = rng.integers(0, 700, size=S)
+    lens[0] = 640
+    w = workload("bf16", 14, 2, 64, 16, lens)
+    dw = DeviceWorkload(w)
+    out, wrote = decode_with(dw, pk.SPLIT_AUTO)
+    assert not wrote, "expected the per-pair split"
+    assert_attention_close(out, reference(w), "bf16", what=f"{S} sequences")
+
+
+@pytest.mark.parametrize("S,Hkv", [(1, 1), (3, 1), (5, 3), (9, 1)])
+def test_lds_stream_split_v_partial_grid(S, Hkv):
+    """Pair counts that are not a multiple of 8: the split-V grid is rounded
+    up, and the workgroups past the last pair exit at once.  Every output
+    row (both halves of every head) against the oracle."""
+    say(f"LDS stream split-V partial grid: S={S} Hkv={Hkv}")
+    rng = np.random.default_rng(77 + 10 * S + Hkv)
+    lens = rng.integers(1, 1200, size=S)
+    w = workload("f16", 4 * Hkv, Hkv, 64, 32, lens, L=3, layer=2)
+    dw = DeviceWorkload(w)
+    out, wrote = decode_with(dw, pk.SPLIT_AUTO)
+    assert not wrote, "expected the per-pair split"
+    assert_attention_close(out, reference(w), "f16", what=f"S={S} Hkv={Hkv}",
+                           vmax=workload_vmax(w))
 
 
 @pytest.mark.parametrize("S,expect_pairs", [(128, True), (129, False)])
