@@ -488,10 +488,11 @@ struct Stream {
   // rows of 128 bytes, row r's 16-byte column q stored at column q ^ (r & 7)
   // (so that the reads below hit distinct banks).  Unit u = 64 h + lane of
   // instruction h is LDS column u & 7 of row u >> 3.  With VS only half
-  // `dhalf` of each V row is copied (dims 32 dhalf .. 32 dhalf + 31, 64 bytes),
-  // tile t to slot + TILES * 2 KiB + t * 1 KiB in one load: unit u = lane is
-  // LDS column u & 3 of row u >> 2 and holds the half's 16-byte column
-  // (u & 3) ^ (r & 3).  The appended token's row comes from k_new / v_new,
+  // `dhalf` of each V row is copied (dims 32 dhalf .. 32 dhalf + 31, 64
+  // bytes, four 16-byte columns), tile t to slot + TILES * 2 KiB + t * 1 KiB
+  // in one load: unit u = lane holds column u & 3 of row 4 ((u >> 2) & 3) +
+  // (u >> 4), so that the rows a read instruction takes (4 quad + r for the
+  // four quads) sit in different banks.  The appended token's row comes from k_new / v_new,
   // as in issue_k / issue_v; whether the chunk holds it is wave-uniform, so
   // other chunks take the form without the per-lane choice.
   template <bool OVR, bool VS>
@@ -516,8 +517,8 @@ struct Stream {
               src, (lds_ptr)(uintptr_t)(slot + (uint32_t)((kv * TILES + t) * 2048 + h * 1024)), 16, 0, 0);
         }
     if constexpr (VS) {
-      const int r = lane >> 2;
-      const int q = (lane & 3) ^ (r & 3);
+      const int r = 4 * ((lane >> 2) & 3) + (lane >> 4);
+      const int q = lane & 3;
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
         const char* src = tile_base(c, ph, t) + 2 * p.pool.kv_stride +
@@ -542,11 +543,9 @@ struct Stream {
   // A lane's LDS read addresses in slot 0 of its wavefront; the other slot
   // and the tiles are immediate offsets.  Lane (n, quad) takes K row n,
   // columns quad and quad + 4 of each tile, and V rows 4 quad + r, bytes
-  // 8n .. 8n+7: the layouts issue_k and issue_v load.  With VS, the lanes
-  // n in [8 dhalf, 8 dhalf + 8) hold the half of V that is staged; they feed
-  // the accumulators of dims 32 dhalf .. 32 dhalf + 31 (quads 2 dhalf and
-  // 2 dhalf + 1).  The other lanes read the same rows of that half, and the
-  // dims they feed are never written out.
+  // 8n .. 8n+7: the layouts issue_k and issue_v load.  With VS, lane
+  // (n, quad) takes dims 32 dhalf + 2n and + 1 of V rows 4 quad + r (4 bytes
+  // of the staged half row), for the two-column PV product of attend.
   struct LdsLane {
     uint32_t k[2], v[4];
   };
@@ -559,8 +558,7 @@ struct Stream {
     for (int r = 0; r < 4; ++r) {
       const int row = 4 * quad + r;
       if constexpr (VS) {
-        const int nh = (n - 8 * dhalf) & 7;
-        a.v[r] = slot0 + (uint32_t)(TILES * 2048 + row * 64 + ((nh >> 1) ^ (row & 3)) * 16 + (n & 1) * 8);
+        a.v[r] = slot0 + (uint32_t)(TILES * 2048 + (16 * r + 4 * quad + (n >> 2)) * 16 + (n & 3) * 4);
       } else {
         a.v[r] = slot0 + (uint32_t)(TILES * 2048 + (row * 8 + ((n >> 1) ^ (row & 7))) * 16 + (n & 1) * 8);
       }
@@ -593,6 +591,28 @@ struct Stream {
     for (int t = 0; t < TILES; ++t)
 #pragma unroll
       for (int i = 0; i < 2; ++i) cb.k[t][i] = __builtin_bit_cast(x8, k[t][i]);
+    if constexpr (VS) {
+      uint32_t v[TILES][4];
+      asm volatile(
+          "ds_read_b32 %0, %8 offset:%12\n\t"
+          "ds_read_b32 %1, %9 offset:%12\n\t"
+          "ds_read_b32 %2, %10 offset:%12\n\t"
+          "ds_read_b32 %3, %11 offset:%12\n\t"
+          "ds_read_b32 %4, %8 offset:%13\n\t"
+          "ds_read_b32 %5, %9 offset:%13\n\t"
+          "ds_read_b32 %6, %10 offset:%13\n\t"
+          "ds_read_b32 %7, %11 offset:%13\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
+            "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+          : "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]), "i"(O), "i"(OV1)
+          : "memory");
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cb.v[t][r] = make_uint2(v[t][r], 0u);
+      return;
+    }
     u32x2_v v[TILES][4];
     asm volatile(
         "ds_read_b64 %0, %8 offset:%12\n\t"
@@ -639,7 +659,8 @@ struct Stream {
   // already use the range up to 2^15), which still skips every chunk that
   // raises no column's max.
   static constexpr float kLazyLog2 = E::kPScaleLog2 == 0.f ? 8.f : 0.f;
-  template <bool TAIL, bool LAZY = false>
+  // VS (half of V's dims, two dims per lane): acc[cg][0..1] only
+  template <bool TAIL, bool LAZY = false, bool VS = false>
   __device__ __forceinline__ void softmax_cols(const f32x4_t* s, const Buf& cb, const Cursor& c,
                                                int cg, uint32_t (&pw)[TILES][2]) {
     float sv[TILES][4];
@@ -666,7 +687,7 @@ struct Stream {
         const float mn = fmaxf(m[cg], bmax);
         const float alpha = __builtin_amdgcn_exp2f(m[cg] - mn);
 #pragma unroll
-        for (int i = 0; i < VD; ++i) acc[cg][i] *= alpha;
+        for (int i = 0; i < (VS ? 2 : VD); ++i) acc[cg][i] *= alpha;
         lacc[cg] *= alpha;
         m[cg] = mn;
       }
@@ -695,12 +716,17 @@ struct Stream {
   // product), then the weighted V sum; updates m, l, acc.  TAIL masks tokens
   // at or past T; masked V rows are zeroed, not weighted by zero, so unused
   // pool slots never reach the sum.
-  template <bool TAIL, bool LAZY = false>
+  // VS (LDS-staged stream, half `dhalf` of V's dims per workgroup): the
+  // lane's V words hold dims 2n and 2n + 1 of its half for its eight tokens,
+  // so one 16x16x32 product per dim parity e takes row n as dim
+  // 32 dhalf + 2n + e, and acc[cg][e][r] is dim 32 dhalf + 8 quad + 2r + e.
+  template <bool TAIL, bool LAZY = false, bool VS = false>
   __device__ __forceinline__ void attend(const f32x4_t* s, Buf& cb, const Cursor& c) {
     static_assert(!LAZY || TILES == 2, "the lazy form sums the normaliser with the 16x16x32 MFMA");
+    static_assert(!VS || (LAZY && NC == 1), "VS: LDS-staged stream only");
     uint32_t pw[NC][TILES][2];
 #pragma unroll
-    for (int cg = 0; cg < NC; ++cg) softmax_cols<TAIL, LAZY>(s + cg * TILES, cb, c, cg, pw[cg]);
+    for (int cg = 0; cg < NC; ++cg) softmax_cols<TAIL, LAZY, VS>(s + cg * TILES, cb, c, cg, pw[cg]);
     if (TAIL && !DENSE) {   // dense rows past the end repeat a real row; their weight is 0
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
@@ -739,6 +765,21 @@ struct Stream {
 #pragma unroll
         for (int cg = 0; cg < NC; ++cg) lacc[cg] = E::mma32(ones, pop[cg], lacc[cg]);
       }
+      if constexpr (VS) {
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const uint32_t sel = e ? 0x07060302u : 0x05040100u;
+          uint32_t a[4];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            a[2 * t] = __builtin_amdgcn_perm(cb.v[t][1].x, cb.v[t][0].x, sel);
+            a[2 * t + 1] = __builtin_amdgcn_perm(cb.v[t][3].x, cb.v[t][2].x, sel);
+          }
+          acc[0][e] = E::mma32(__builtin_bit_cast(x8, make_uint4(a[0], a[1], a[2], a[3])), pop[0],
+                               acc[0][e]);
+        }
+        return;
+      }
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
         uint32_t ev[4], od[4];
@@ -762,13 +803,13 @@ struct Stream {
     }
   }
 
-  template <bool LAZY = false>
+  template <bool LAZY = false, bool VS = false>
   __device__ __forceinline__ void attend_chunk(const f32x4_t* s, Buf& cb,
                                                const Cursor& c) {
     if (DENSE || (c.j == c.nb - 1 && (c.T % (16 * TILES)) != 0))
-      attend<true, LAZY>(s, cb, c);
+      attend<true, LAZY, VS>(s, cb, c);
     else
-      attend<false, LAZY>(s, cb, c);
+      attend<false, LAZY, VS>(s, cb, c);
   }
 
   // End of this wavefront's part of sequence c.b: normalised output if it
@@ -809,17 +850,46 @@ struct Stream {
     }
   }
 
+  // VS: the partial of this workgroup's half of V's dims, in flush_lds's
+  // layout (the other half's dims are left as they are: the fold does not
+  // read them).  Lane (n, quad) holds dims 32 dhalf + 8 quad .. + 7.
+  __device__ __forceinline__ void flush_lds_vs(uint32_t base, int dhalf) {
+    typedef __attribute__((address_space(3))) float lds_float;
+    const float lt = lacc[0][0];
+    if (n >= gw) return;
+    lds_float* of = (lds_float*)(uintptr_t)base + n * D + 32 * dhalf + 8 * quad;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      of[2 * r] = acc[0][0][r];
+      of[2 * r + 1] = acc[0][1][r];
+    }
+    if (quad == 0) {
+      lds_float* ml = (lds_float*)(uintptr_t)base + gw * D + 2 * n;
+      ml[0] = m[0];
+      ml[1] = lt;
+    }
+  }
+
+  // VS, a sequence this wavefront saw whole: its half of head n's output
+  // row, 8 dims per lane in one 16-byte store.
+  __device__ __forceinline__ void flush_whole_vs(const Cursor& c, float lt, int dhalf) {
+    if (n >= gw) return;
+    const float inv = 1.0f / lt;
+    uint16_t* dst = static_cast<uint16_t*>(p.out) +
+                    ((int64_t)c.b * p.num_q_heads + qh0 + n) * D + 32 * dhalf + 8 * quad;
+    const f32x4_t* a = acc[0];
+    *reinterpret_cast<uint4*>(dst) =
+        make_uint4(E::pack2(a[0][0] * inv, a[1][0] * inv), E::pack2(a[0][1] * inv, a[1][1] * inv),
+                   E::pack2(a[0][2] * inv, a[1][2] * inv), E::pack2(a[0][3] * inv, a[1][3] * inv));
+  }
+
   // Column group cg's share of flush: head 16*cg + n of this (virtual) KV head.
-  // dhalf >= 0 (a workgroup with half of V's dims, whole sequences only):
-  // only the lanes of dims 32 dhalf .. 32 dhalf + 31 write.
-  __device__ __forceinline__ void flush_cols(const Cursor& c, bool whole, int cg, float lt,
-                                             int dhalf = -1) {
+  __device__ __forceinline__ void flush_cols(const Cursor& c, bool whole, int cg, float lt) {
     const int G = p.group;   // partial slot stride
     const int hc = 16 * cg + n;
     const f32x4_t* a = acc[cg];
     // lane holds dims kQuadDims*quad + kRowDims*r + (i % 8) + kHalfDims*(i / 8)
     // of head hc as a[i][r]
-    if (dhalf >= 0 && (quad >> 1) != dhalf) return;
     if (whole) {
       const float inv = DENSE && lt == 0.f ? 0.f : 1.0f / lt;   // dense: all masked -> zeros
       uint16_t* dst = static_cast<uint16_t*>(p.out) +
@@ -1224,12 +1294,12 @@ __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane,
   constexpr int LPC = S::template chunk_loads<VS>();
   const bool whole = cur.nb == 1;
   static_assert(S::kPh == 2, "two tiles per chunk");
-  // entries of the wavefront's k-th chunk; a tile that starts at or past T
-  // takes the chunk's first block (it is masked)
   // the entries arrive before the first copy is issued: waiting for them
   // here, on every path, keeps the compiler from waiting for all vector
   // memory (copies included) at a later use
   asm volatile("" ::"v"(ent));
+  // entries of the wavefront's k-th chunk; a tile that starts at or past T
+  // takes the chunk's first block (it is masked)
   auto chunk_blocks = [&](int k, int* ph) {
     const int e = (2 * k) & 63;
     ph[0] = __builtin_amdgcn_readlane(ent, e);
@@ -1258,7 +1328,7 @@ __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane,
     }
     cur.j = pc.at(i);
     st.qk(cb, s);
-    st.template attend_chunk<true>(s, cb, cur);
+    st.template attend_chunk<true, VS>(s, cb, cur);
   };
   for (int i = 0; i < rem; i += NS) {
     step(SlotTag<0>{}, i);
@@ -1270,9 +1340,15 @@ __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane,
     }
   }
   if (whole) {
-    if (st.n < st.gw) st.flush_cols(cur, true, 0, st.lacc[0][0], VS ? dhalf : -1);
+    if constexpr (VS)
+      st.flush_whole_vs(cur, st.lacc[0][0], dhalf);
+    else if (st.n < st.gw)
+      st.flush_cols(cur, true, 0, st.lacc[0][0]);
   } else {   // the partial goes to this wavefront's own (now free) slots
-    st.flush_lds(slot0);
+    if constexpr (VS)
+      st.flush_lds_vs(slot0, dhalf);
+    else
+      st.flush_lds(slot0);
   }
 }
 
