@@ -1453,6 +1453,11 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
   using Out = typename S::OutElem;
   constexpr int NW = pair_waves<S>();
   static_assert(!VS || S::kLdsStream, "split V only with the LDS-staged stream");
+  // The kernel-argument fields the prologue reads, requested before its
+  // first branch: their loads then go out in one batch, not in a second
+  // one after the early exit, which would wait a round trip of its own.
+  asm volatile("" ::"s"(p.block_tables), "s"(p.context_lens), "s"(p.positions),
+               "s"(p.max_blocks_per_seq), "s"(p.pool.block_size), "s"(p.batch), "s"(p.vheads));
   const int H = p.vheads;
   int pr = blockIdx.x, dhalf = 0;
   if constexpr (VS) {
