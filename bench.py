@@ -53,44 +53,44 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # otherwise the JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 542161306,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 542151270,
     },
     "long_context_bf16": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 2211059098,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 2211011686,
     },
     "churned_pool_bf16_gqa7": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 19377357,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 19341722,
     },
     "high_concurrency_bf16": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 3820024320,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 3819848704,
     },
     "tiny_fp32_mha": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 630374,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 621158,
     },
     "llama8b_decode_f32": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 1146534502,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 1146507674,
     },
     "llama8b_decode_f16": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 582648832,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 582640640,
     },
     "gemma_like_d256_bf16": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 1134173082,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 1134142976,
     },
     "mqa32_decode_bf16": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 85686886,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 85686579,
     },
     "mqa32_high_concurrency_bf16": {
-        "kernel_sha256": "84cb67b5010c7b5e4a25aa14437af8c4c9bb2ad8bc2801d61871247c6fcf7650",
-        "bytes": 483646259,
+        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "bytes": 483643699,
     },
 }
 
