@@ -358,21 +358,21 @@ struct Stream {
     }
     const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
     const int tok0 = c.j * (16 * TILES);
-    ph[0] = uni(trow[tok0 / p.pool.block_size]);
+    ph[0] = uni(trow[fdiv(tok0, p.bs_div)]);
 #pragma unroll
     for (int t = 1; t < TILES; ++t) {
       const int tok = tok0 + 16 * t;
-      ph[t] = tok < c.T ? uni(trow[tok / p.pool.block_size]) : ph[0];
+      ph[t] = tok < c.T ? uni(trow[fdiv(tok, p.bs_div)]) : ph[0];
     }
   }
 
   // Byte address of the K rows of tile t of chunk c.
   __device__ __forceinline__ const char* tile_base(const Cursor& c, const int* ph, int t) const {
     const int tok = c.j * (16 * TILES) + 16 * t;
+    const int off = tok - (int)fdiv(tok, p.bs_div) * p.pool.block_size;   // tok % block_size
     return p.pool.base + 2 * ((int64_t)p.layer * p.pool.layer_stride +
                               (int64_t)gp * p.pool.head_stride +
-                              (int64_t)ph[t] * p.pool.block_stride +
-                              (int64_t)(tok % p.pool.block_size) * D);
+                              (int64_t)ph[t] * p.pool.block_stride + (int64_t)off * D);
   }
 
   // SMALL blocks: byte address of token tok's K (kv = 0) or V (kv = 1) row
@@ -1026,15 +1026,15 @@ struct StreamF32 {
 
   __device__ __forceinline__ void fetch_phys(const Cursor& c, int* ph) const {
     const const_i32_ptr trow = (const_i32_ptr)(p.block_tables + (int64_t)c.b * p.max_blocks_per_seq);
-    ph[0] = uni(trow[(c.j * 16) / p.pool.block_size]);
+    ph[0] = uni(trow[fdiv(c.j * 16, p.bs_div)]);
   }
 
   __device__ __forceinline__ const char* tile_base(const Cursor& c, const int* ph) const {
     const int tok = c.j * 16;
+    const int off = tok - (int)fdiv(tok, p.bs_div) * p.pool.block_size;   // tok % block_size
     return p.pool.base + 4 * ((int64_t)p.layer * p.pool.layer_stride +
                               (int64_t)gp * p.pool.head_stride +
-                              (int64_t)ph[0] * p.pool.block_stride +
-                              (int64_t)(tok % p.pool.block_size) * D);
+                              (int64_t)ph[0] * p.pool.block_stride + (int64_t)off * D);
   }
 
   __device__ __forceinline__ const char* new_row(const Cursor& c, int kv) const {
@@ -1384,7 +1384,7 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     g = k * kWaves + w;
   } else {
     const int64_t wave = (int64_t)blockIdx.x * kWaves + w;
-    unit = wave / H;
+    unit = fdiv((uint32_t)wave, p.vh_div);
     g = (int)(wave - unit * H);
   }
   const int64_t C = uni(prefix[p.batch]);
@@ -1465,7 +1465,7 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
     dhalf = (int)(blockIdx.x >> 3) & 1;
     if (pr >= p.batch * H) return;
   }
-  const int b = pr / H;
+  const int b = (int)fdiv((uint32_t)pr, p.vh_div);
   const int g = pr - b * H;
   const int lane = threadIdx.x & 63;
   const int w = uni(threadIdx.x >> 6);
@@ -1483,9 +1483,10 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
   int ent = 0;
   if constexpr (S::kLdsStream) {
     const int32_t* trow = p.block_tables + (int64_t)b * p.max_blocks_per_seq;
-    const unsigned bs = (unsigned)p.pool.block_size, last = (unsigned)p.max_blocks_per_seq - 1;
+    const unsigned last = (unsigned)p.max_blocks_per_seq - 1;
     if (lane < 2 * lds_chunks_per_wave<NW>())
-      ent = trow[min((unsigned)((w + NW * (lane >> 1)) * S::kChunk + 16 * (lane & 1)) / bs, last)];
+      ent = trow[min(fdiv((uint32_t)((w + NW * (lane >> 1)) * S::kChunk + 16 * (lane & 1)), p.bs_div),
+                     last)];
   }
   cur.T = uni(lens[b]);
   cur.pos = poss ? uni(poss[b]) : -1;
@@ -1508,7 +1509,7 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
       row_unit = reinterpret_cast<const uint4*>(
           static_cast<const Out*>(kv ? p.v_new : p.k_new) +
           ((int64_t)b * p.pool.kv_heads + gp) * D)[lane - kv * row_units];
-    row_phys = p.block_tables[(int64_t)b * p.max_blocks_per_seq + cur.pos / p.pool.block_size];
+    row_phys = p.block_tables[(int64_t)b * p.max_blocks_per_seq + fdiv(cur.pos, p.bs_div)];
   }
   if (w < A) {
     // unit 7b + w makes partial_slot() give slot (8b + w) * vheads + g
@@ -1522,7 +1523,7 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
       pc.stride = A;
       cur.j = w;
       stream_pair_lds<S, kLdsSlots, VS>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, cur, pc,
-                                        (n - 1 - w) / A + 1, ent, slot0, dhalf);
+                                        A == NW ? (n - 1 - w) / NW + 1 : 1, ent, slot0, dhalf);
     } else {
       cur.j = w * n / A;
       stream_chunks<S>(p, lane, g, (int64_t)(kPairWaves - 1) * b + w, nullptr, lens, poss, cur,
@@ -1597,7 +1598,8 @@ __global__ __launch_bounds__(64 * pair_waves<S>()) void decode_pair_kernel(Decod
       const int gp = vhead_pool_head(g, p.qsplit);
       const int64_t row = (int64_t)row_phys * p.pool.block_stride +
                           (int64_t)p.layer * p.pool.layer_stride + (int64_t)gp * p.pool.head_stride +
-                          (int64_t)(cur.pos % p.pool.block_size) * D + kv * p.pool.kv_stride;
+                          (int64_t)(cur.pos - (int)fdiv(cur.pos, p.bs_div) * p.pool.block_size) * D +
+                          kv * p.pool.kv_stride;
       reinterpret_cast<uint4*>(reinterpret_cast<Out*>(const_cast<char*>(p.pool.base)) + row)[lane - kv * row_units] =
           row_unit;
     }
@@ -1753,6 +1755,8 @@ void launch_f32(DecodeParams& p, int wgs, size_t lds, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_mfma(DecodeParams& p, hipStream_t s) {
+  p.bs_div = make_fast_div((uint32_t)p.pool.block_size);
+  p.vh_div = make_fast_div((uint32_t)p.vheads);
   const size_t lds = mfma_lds_bytes(p.batch);
   // The grid is kDecodeWgPerCu (1) workgroup per CU, capped by what one
   // instantiation of this head_dim holds at once.  Every instantiation holds

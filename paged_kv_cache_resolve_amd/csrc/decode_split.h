@@ -4,7 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.h"
+
 namespace pagedkv {
+
+// n / d for 0 <= n < 2^31, with f = make_fast_div(d).
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, FastDiv f) {
+  return (__umulhi(n, f.m) + n) >> f.s;
+}
 
 __device__ __forceinline__ int chunks_of(int T, int ct) {
   return T > 0 ? (T + ct - 1) / ct : 0;

@@ -73,6 +73,24 @@ inline int elem_size(pagedkv_dtype_t t) { return t == PAGEDKV_F32 ? 4 : 2; }
 // (b + u) * kv_heads + g, and the merge kernel combines the partials of
 // every pair that was split between units.
 // ---------------------------------------------------------------------------
+// Unsigned division by a divisor d >= 1 fixed for a launch, as a
+// multiply-high, an add and a shift (the round-up method:
+// s = ceil(log2 d), m = floor(2^32 (2^s - d) / d) + 1, n / d =
+// (mulhi(n, m) + n) >> s), exact for every 0 <= n < 2^31.  The kernels use
+// it for the block size and the virtual KV head count, where the
+// compiler's expansion of a division by a run-time value costs some twenty
+// scalar instructions, which the wavefronts of a CU issue one at a time.
+struct FastDiv {
+  uint32_t m;
+  uint32_t s;
+};
+inline FastDiv make_fast_div(uint32_t d) {
+  uint32_t s = 0;
+  while (((uint64_t)1 << s) < d) ++s;
+  const uint64_t m = (((uint64_t)1 << 32) * (((uint64_t)1 << s) - d)) / d + 1;
+  return FastDiv{(uint32_t)m, s};
+}
+
 struct DecodeParams {
   PoolGeom pool;
   const void* q;
@@ -118,6 +136,9 @@ struct DecodeParams {
   // virtual KV head) pair, which merges its own pieces.  Out (set by the
   // pass-1 launcher): non-zero if that kernel ran, so no merge pass follows.
   int pair_mode;
+  // Set by the pass-1 launcher: division by pool.block_size and by vheads.
+  FastDiv bs_div;
+  FastDiv vh_div;
 };
 
 constexpr int kMaxWaves = 8192;          // upper bound on wavefronts (256 CUs x 32)
