@@ -53,44 +53,44 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # otherwise the JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 542151270,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 542127718,
     },
     "long_context_bf16": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 2211011686,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 2211000422,
     },
     "churned_pool_bf16_gqa7": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 19341722,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 19327386,
     },
     "high_concurrency_bf16": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
         "bytes": 3819848704,
     },
     "tiny_fp32_mha": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 621158,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 620134,
     },
     "llama8b_decode_f32": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 1146507674,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 1146325811,
     },
     "llama8b_decode_f16": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 582640640,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 582620774,
     },
     "gemma_like_d256_bf16": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 1134142976,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 1134481510,
     },
     "mqa32_decode_bf16": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 85686579,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 85659750,
     },
     "mqa32_high_concurrency_bf16": {
-        "kernel_sha256": "906d837ee771d24d984dd283c12274918409d3a788c3e5823988e141e52b1115",
-        "bytes": 483643699,
+        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
+        "bytes": 483614208,
     },
 }
 
