@@ -274,7 +274,9 @@ size_t paged_attention_workspace_bytes(const kv_pool_t* pool, int batch,
  * resident at once and the longest sequence the block tables allow,
  * max_blocks_per_seq * block_size tokens, holds at most 512 KiB of K and V
  * per KV head at head_dim 64 in bf16 or fp16 with block_size a multiple of
- * 16 (2048 tokens; these pairs stage K and V through LDS), else 256 KiB
+ * 16 (2048 tokens; these pairs stage K and V through LDS, and while at
+ * most 128 such pairs are launched each runs as two workgroups that take
+ * one half of V's dims each), else 256 KiB
  * (1024 tokens at head_dim 64 in bf16 or fp16 with 4- or 8-token blocks,
  * 512 at 128; 512 and 256 in fp32); flags = PAGEDKV_DECODE_CHUNKS keeps
  * every call on the chunk split (below).
