@@ -492,9 +492,10 @@ struct Stream {
   // bytes, four 16-byte columns), tile t to slot + TILES * 2 KiB + t * 1 KiB
   // in one load: unit u = lane holds column u & 3 of row 4 ((u >> 2) & 3) +
   // (u >> 4), so that the rows a read instruction takes (4 quad + r for the
-  // four quads) sit in different banks.  The appended token's row comes from k_new / v_new,
-  // as in issue_k / issue_v; whether the chunk holds it is wave-uniform, so
-  // other chunks take the form without the per-lane choice.
+  // four quads) sit in different banks.  The appended token's row comes
+  // from k_new / v_new, as in issue_k / issue_v; whether the chunk holds it
+  // is wave-uniform, so other chunks take the form without the per-lane
+  // choice.
   template <bool OVR, bool VS>
   __device__ __forceinline__ void dma_tiles(const Cursor& c, const int* ph, uint32_t slot,
                                             int dhalf) const {
@@ -1252,18 +1253,18 @@ __device__ __forceinline__ void wait_newer_chunks(int newer) {
 
 // One wavefront of the per-pair kernel over chunks cur.j, cur.j + stride,
 // ... (rem of them) of one sequence, its K and V staged through NS LDS slots
-// of kSlotBytes from `slot0`: while the wavefront computes chunk i from
-// registers, chunks i + 1 .. i + NS are in flight or waiting in LDS.  A
-// chunk's copy is 8 LDS-direct loads (K and V, two tiles, two 1 KiB rows of
-// lanes each), and vector-memory operations complete in issue order, so
-// chunk i is in LDS once at most the loads of the chunks copied after it
-// are still in flight.  Lane 2k + t of `ent` holds the block-table entry of
-// tile t of the wavefront's k-th chunk (loaded by the caller with the
-// sequence's length), so the loop makes no table loads: a scalar load
-// issued in one step would be waited for by the next step's LDS reads
-// (s_waitcnt lgkmcnt counts both), which put its latency on every chunk.
-// The loop runs NS chunks per pass so that each read has its slot as an
-// immediate offset.
+// of slot_bytes<VS>() from `slot0`: while the wavefront computes chunk i
+// from registers, chunks i + 1 .. i + NS are in flight or waiting in LDS.  A
+// chunk's copy is chunk_loads<VS>() LDS-direct loads (K and V, or K and half
+// of V, two tiles, 1 KiB of lanes each), and vector-memory operations
+// complete in issue order, so chunk i is in LDS once at most the loads of
+// the chunks copied after it are still in flight.  Lane 2k + t of `ent`
+// holds the block-table entry of tile t of the wavefront's k-th chunk
+// (loaded by the caller with the sequence's length), so the loop makes no
+// table loads: a scalar load issued in one step would be waited for by the
+// next step's LDS reads (s_waitcnt lgkmcnt counts both), which put its
+// latency on every chunk.  The loop runs NS chunks per pass so that each
+// read has its slot as an immediate offset.
 template <int P> struct SlotTag { static constexpr int value = P; };
 
 // Chunks of one wavefront of the per-pair LDS-staged stream: w, w + A,
