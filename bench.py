@@ -53,44 +53,44 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # otherwise the JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 542127718,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 542139597,
     },
     "long_context_bf16": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 2211000422,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 2211005645,
     },
     "churned_pool_bf16_gqa7": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 19327386,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 19326362,
     },
     "high_concurrency_bf16": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 3819848704,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 3819849216,
     },
     "tiny_fp32_mha": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 620134,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 620339,
     },
     "llama8b_decode_f32": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 1146325811,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 1146319462,
     },
     "llama8b_decode_f16": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 582620774,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 582624666,
     },
     "gemma_like_d256_bf16": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 1134481510,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 1134782054,
     },
     "mqa32_decode_bf16": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 85659750,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 87812096,
     },
     "mqa32_high_concurrency_bf16": {
-        "kernel_sha256": "72293b1d8887070b93e68dc71b882bc58ffcf3d39a725b6b89a8aa03dd367e9e",
-        "bytes": 483614208,
+        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
+        "bytes": 486554931,
     },
 }
 

@@ -1384,7 +1384,13 @@ __global__ __launch_bounds__(kThreads) void decode_mfma_kernel(DecodeParams p) {
     unit = blockIdx.x - k * stride;
     g = k * kWaves + w;
   } else {
-    const int64_t wave = (int64_t)blockIdx.x * kWaves + w;
+    // With one (virtual) KV head a unit is one wavefront, and the units that
+    // get work (fewer than launched when chunks are few) go round-robin over
+    // the workgroups rather than filling the first ones, so that they spread
+    // over every CU: one KV head for 32 query heads at batch 64 went from
+    // 34.6 to 30.4 us per call.
+    const int64_t wave = H == 1 ? (int64_t)w * gridDim.x + blockIdx.x
+                                : (int64_t)blockIdx.x * kWaves + w;
     unit = fdiv((uint32_t)wave, p.vh_div);
     g = (int)(wave - unit * H);
   }
