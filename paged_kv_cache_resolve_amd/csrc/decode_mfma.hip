@@ -368,11 +368,14 @@ struct Stream {
 
   // Byte address of the K rows of tile t of chunk c.
   __device__ __forceinline__ const char* tile_base(const Cursor& c, const int* ph, int t) const {
-    const int tok = c.j * (16 * TILES) + 16 * t;
+    return tile_addr(ph[t], c.j * (16 * TILES) + 16 * t);
+  }
+  // Byte address of the K row of token tok, which lies in block phys.
+  __device__ __forceinline__ const char* tile_addr(int phys, int tok) const {
     const int off = tok - (int)fdiv(tok, p.bs_div) * p.pool.block_size;   // tok % block_size
     return p.pool.base + 2 * ((int64_t)p.layer * p.pool.layer_stride +
                               (int64_t)gp * p.pool.head_stride +
-                              (int64_t)ph[t] * p.pool.block_stride + (int64_t)off * D);
+                              (int64_t)phys * p.pool.block_stride + (int64_t)off * D);
   }
 
   // SMALL blocks: byte address of token tok's K (kv = 0) or V (kv = 1) row
@@ -497,7 +500,7 @@ struct Stream {
   // is wave-uniform, so other chunks take the form without the per-lane
   // choice.
   template <bool OVR, bool VS>
-  __device__ __forceinline__ void dma_tiles(const Cursor& c, const int* ph, uint32_t slot,
+  __device__ __forceinline__ void dma_tiles(const Cursor& c, const char* const* tb, uint32_t slot,
                                             int dhalf) const {
     typedef __attribute__((address_space(3))) void* lds_ptr;
 #pragma unroll
@@ -510,7 +513,7 @@ struct Stream {
           const int r = u >> 3;
           const int col = (u & 7) ^ (r & 7);
           const char* src =
-              tile_base(c, ph, t) + (kv ? 2 * p.pool.kv_stride : 0) + (uint32_t)(2 * r * D + 16 * col);
+              tb[t] + (kv ? 2 * p.pool.kv_stride : 0) + (uint32_t)(2 * r * D + 16 * col);
           if constexpr (OVR) {
             if (c.j * kChunk + 16 * t + r == c.pos) src = new_row(c, kv) + 16 * col;
           }
@@ -522,7 +525,7 @@ struct Stream {
       const int q = lane & 3;
 #pragma unroll
       for (int t = 0; t < TILES; ++t) {
-        const char* src = tile_base(c, ph, t) + 2 * p.pool.kv_stride +
+        const char* src = tb[t] + 2 * p.pool.kv_stride +
                           (uint32_t)(2 * r * D + 64 * dhalf + 16 * q);
         if constexpr (OVR) {
           if (c.j * kChunk + 16 * t + r == c.pos) src = new_row(c, 1) + 64 * dhalf + 16 * q;
@@ -533,12 +536,12 @@ struct Stream {
     }
   }
   template <bool VS = false>
-  __device__ __forceinline__ void dma_chunk(const Cursor& c, const int* ph, uint32_t slot,
+  __device__ __forceinline__ void dma_chunk(const Cursor& c, const char* const* tb, uint32_t slot,
                                             int dhalf = 0) const {
     if (APPEND && (unsigned)(c.pos - c.j * kChunk) < (unsigned)kChunk)
-      dma_tiles<APPEND, VS>(c, ph, slot, dhalf);
+      dma_tiles<APPEND, VS>(c, tb, slot, dhalf);
     else
-      dma_tiles<false, VS>(c, ph, slot, dhalf);
+      dma_tiles<false, VS>(c, tb, slot, dhalf);
   }
 
   // A lane's LDS read addresses in slot 0 of its wavefront; the other slot
@@ -570,7 +573,8 @@ struct Stream {
   // Read the chunk in slot SLOT into the Buf registers.  The reads are
   // written as asm with their wait inside, because the compiler would
   // otherwise wait for every LDS-direct load in flight (it cannot tell the
-  // slots apart) before each LDS read.
+  // slots apart) before each LDS read.  K and V go out together under one
+  // wait: a wait between them cost the churned-pool call 0.2 us.
   template <int SLOT, bool VS = false>
   __device__ __forceinline__ void read_chunk(Buf& cb, const LdsLane& a) const {
     static_assert(TILES == 2, "two tiles per chunk");
@@ -579,60 +583,63 @@ struct Stream {
     typedef unsigned u32x4_v __attribute__((ext_vector_type(4)));
     typedef unsigned u32x2_v __attribute__((ext_vector_type(2)));
     u32x4_v k[TILES][2];
-    asm volatile(
-        "ds_read_b128 %0, %4 offset:%6\n\t"
-        "ds_read_b128 %1, %5 offset:%6\n\t"
-        "ds_read_b128 %2, %4 offset:%7\n\t"
-        "ds_read_b128 %3, %5 offset:%7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1])
-        : "v"(a.k[0]), "v"(a.k[1]), "i"(O), "i"(O + 2048)
-        : "memory");
-#pragma unroll
-    for (int t = 0; t < TILES; ++t)
-#pragma unroll
-      for (int i = 0; i < 2; ++i) cb.k[t][i] = __builtin_bit_cast(x8, k[t][i]);
     if constexpr (VS) {
       uint32_t v[TILES][4];
       asm volatile(
-          "ds_read_b32 %0, %8 offset:%12\n\t"
-          "ds_read_b32 %1, %9 offset:%12\n\t"
-          "ds_read_b32 %2, %10 offset:%12\n\t"
-          "ds_read_b32 %3, %11 offset:%12\n\t"
-          "ds_read_b32 %4, %8 offset:%13\n\t"
-          "ds_read_b32 %5, %9 offset:%13\n\t"
-          "ds_read_b32 %6, %10 offset:%13\n\t"
-          "ds_read_b32 %7, %11 offset:%13\n\t"
+          "ds_read_b128 %0, %12 offset:%18\n\t"
+          "ds_read_b128 %1, %13 offset:%18\n\t"
+          "ds_read_b128 %2, %12 offset:%19\n\t"
+          "ds_read_b128 %3, %13 offset:%19\n\t"
+          "ds_read_b32 %4, %14 offset:%18\n\t"
+          "ds_read_b32 %5, %15 offset:%18\n\t"
+          "ds_read_b32 %6, %16 offset:%18\n\t"
+          "ds_read_b32 %7, %17 offset:%18\n\t"
+          "ds_read_b32 %8, %14 offset:%20\n\t"
+          "ds_read_b32 %9, %15 offset:%20\n\t"
+          "ds_read_b32 %10, %16 offset:%20\n\t"
+          "ds_read_b32 %11, %17 offset:%20\n\t"
           "s_waitcnt lgkmcnt(0)"
-          : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
+          : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1]),
+            "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
             "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
-          : "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]), "i"(O), "i"(OV1)
+          : "v"(a.k[0]), "v"(a.k[1]), "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]),
+            "i"(O), "i"(O + 2048), "i"(OV1)
           : "memory");
 #pragma unroll
       for (int t = 0; t < TILES; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) cb.v[t][r] = make_uint2(v[t][r], 0u);
-      return;
+    } else {
+      u32x2_v v[TILES][4];
+      asm volatile(
+          "ds_read_b128 %0, %12 offset:%18\n\t"
+          "ds_read_b128 %1, %13 offset:%18\n\t"
+          "ds_read_b128 %2, %12 offset:%19\n\t"
+          "ds_read_b128 %3, %13 offset:%19\n\t"
+          "ds_read_b64 %4, %14 offset:%18\n\t"
+          "ds_read_b64 %5, %15 offset:%18\n\t"
+          "ds_read_b64 %6, %16 offset:%18\n\t"
+          "ds_read_b64 %7, %17 offset:%18\n\t"
+          "ds_read_b64 %8, %14 offset:%20\n\t"
+          "ds_read_b64 %9, %15 offset:%20\n\t"
+          "ds_read_b64 %10, %16 offset:%20\n\t"
+          "ds_read_b64 %11, %17 offset:%20\n\t"
+          "s_waitcnt lgkmcnt(0)"
+          : "=&v"(k[0][0]), "=&v"(k[0][1]), "=&v"(k[1][0]), "=&v"(k[1][1]),
+            "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
+            "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
+          : "v"(a.k[0]), "v"(a.k[1]), "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]),
+            "i"(O), "i"(O + 2048), "i"(OV1)
+          : "memory");
+#pragma unroll
+      for (int t = 0; t < TILES; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) cb.v[t][r] = make_uint2(v[t][r].x, v[t][r].y);
     }
-    u32x2_v v[TILES][4];
-    asm volatile(
-        "ds_read_b64 %0, %8 offset:%12\n\t"
-        "ds_read_b64 %1, %9 offset:%12\n\t"
-        "ds_read_b64 %2, %10 offset:%12\n\t"
-        "ds_read_b64 %3, %11 offset:%12\n\t"
-        "ds_read_b64 %4, %8 offset:%13\n\t"
-        "ds_read_b64 %5, %9 offset:%13\n\t"
-        "ds_read_b64 %6, %10 offset:%13\n\t"
-        "ds_read_b64 %7, %11 offset:%13\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(v[0][0]), "=&v"(v[0][1]), "=&v"(v[0][2]), "=&v"(v[0][3]),
-          "=&v"(v[1][0]), "=&v"(v[1][1]), "=&v"(v[1][2]), "=&v"(v[1][3])
-        : "v"(a.v[0]), "v"(a.v[1]), "v"(a.v[2]), "v"(a.v[3]), "i"(O), "i"(OV1)
-        : "memory");
 #pragma unroll
     for (int t = 0; t < TILES; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) cb.v[t][r] = make_uint2(v[t][r].x, v[t][r].y);
+      for (int i = 0; i < 2; ++i) cb.k[t][i] = __builtin_bit_cast(x8, k[t][i]);
   }
 
   // s[cg * TILES + t]: scores of tile t against column group cg.
@@ -1299,36 +1306,45 @@ __device__ __forceinline__ void stream_pair_lds(const DecodeParams& p, int lane,
   // here, on every path, keeps the compiler from waiting for all vector
   // memory (copies included) at a later use
   asm volatile("" ::"v"(ent));
-  // entries of the wavefront's k-th chunk; a tile that starts at or past T
-  // takes the chunk's first block (it is masked)
-  auto chunk_blocks = [&](int k, int* ph) {
+  // lane 2k + t: address of tile t of the wavefront's k-th chunk, worked
+  // out once for all chunks, so that a chunk's copies take four lane reads
+  // instead of ~30 scalar operations (0.17 us on the churned-pool call); a
+  // tile that starts at or past T takes the block of the chunk's first tile
+  // (its rows are masked)
+  const int tokl = pc.at(lane >> 1) * S::kChunk + 16 * (lane & 1);
+  const int ent0 = __builtin_amdgcn_update_dpp(0, ent, 0xA0, 0xf, 0xf, false);   // lane & ~1
+  const uint64_t tla = (uint64_t)(uintptr_t)st.tile_addr(tokl < cur.T ? ent : ent0, tokl);
+  const uint32_t tlo = (uint32_t)tla, thi = (uint32_t)(tla >> 32);
+  auto chunk_blocks = [&](int k, const char** tb) {
     const int e = (2 * k) & 63;
-    ph[0] = __builtin_amdgcn_readlane(ent, e);
-    ph[1] = pc.at(k) * S::kChunk + 16 < cur.T ? __builtin_amdgcn_readlane(ent, e + 1) : ph[0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      tb[t] = (const char*)(uintptr_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane(thi, e + t) << 32) |
+                                       (uint32_t)__builtin_amdgcn_readlane(tlo, e + t));
   };
 #pragma unroll
   for (int k = 0; k < NS; ++k)
     if (k < rem) {
       Cursor c = cur;
       c.j = pc.at(k);
-      int ph[2];
-      chunk_blocks(k, ph);
-      st.template dma_chunk<VS>(c, ph, slot0 + k * SB, dhalf);
+      const char* tb[2];
+      chunk_blocks(k, tb);
+      st.template dma_chunk<VS>(c, tb, slot0 + k * SB, dhalf);
     }
   f32x4_t s[S::kTiles];
   auto step = [&](auto tag, int i) {
     constexpr int P = decltype(tag)::value;
     wait_newer_chunks<NS - 1, LPC>(rem - 1 - i);
     st.template read_chunk<P, VS>(cb, la);
+    st.qk(cb, s);
     if (i + NS < rem) {   // chunk i + NS into the slot just read
       Cursor c = cur;
       c.j = pc.at(i + NS);
-      int ph[2];
-      chunk_blocks(i + NS, ph);
-      st.template dma_chunk<VS>(c, ph, slot0 + P * SB, dhalf);
+      const char* tb[2];
+      chunk_blocks(i + NS, tb);
+      st.template dma_chunk<VS>(c, tb, slot0 + P * SB, dhalf);
     }
     cur.j = pc.at(i);
-    st.qk(cb, s);
     st.template attend_chunk<true, VS>(s, cb, cur);
   };
   for (int i = 0; i < rem; i += NS) {
