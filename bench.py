@@ -53,44 +53,44 @@ PASS1_SOURCE = os.path.join(ROOT, "paged_kv_cache_resolve_amd", "csrc", "decode_
 # otherwise the JSON reports null.
 MEASURED_TRAFFIC = {
     "llama8b_decode_bf16": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 542139597,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 542140621,
     },
     "long_context_bf16": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 2211005645,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 2211046605,
     },
     "churned_pool_bf16_gqa7": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 19326362,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 19310797,
     },
     "high_concurrency_bf16": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 3819849216,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 3819921408,
     },
     "tiny_fp32_mha": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 620339,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 620134,
     },
     "llama8b_decode_f32": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 1146319462,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 1146355098,
     },
     "llama8b_decode_f16": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 582624666,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 582644326,
     },
     "gemma_like_d256_bf16": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 1134782054,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 1134821683,
     },
     "mqa32_decode_bf16": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 87812096,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 87819162,
     },
     "mqa32_high_concurrency_bf16": {
-        "kernel_sha256": "b7743c3cca19e02cad54702035af532a79b8fea394f3543e761b7ac6baf28370",
-        "bytes": 486554931,
+        "kernel_sha256": "37b226c30e9e3ea4fc5d01075410df2a24e33e0dc619b2b2c6503a624b334a34",
+        "bytes": 486555341,
     },
 }
 
